@@ -1,0 +1,201 @@
+"""Seeded synthetic inputs shared by the HIP path's tests/bench and by the oracle.
+
+This module only *makes inputs*: random fp32 data, its quantisation to FP8 e4m3
+bytes plus fp32 scale factors, expert ids and masked row counts.  It holds none
+of the GEMM's arithmetic (no decode, no products, no accumulation, no output
+rounding), so the oracle and the GPU path can both consume its bytes without
+sharing any of the method's code.
+
+Quantisation follows the fine-grained scaling the DeepGEMM pages describe
+(DeepSeek DeepGEMM 中文讲解, "使用示例": activations carry one fp32 scale per
+row and 128-wide K block, shape [M, K/128]; weights one per 128x128 block,
+shape [ceil(N/128), K/128]; "注意事项": FP8 needs dynamic scale factors from
+amax).  Per group: amax = max |x|, s = amax / 448 (448 = largest finite e4m3
+value), q = e4m3(clamp(x / s, +-448)) with round-to-nearest-even; an all-zero
+group gets s = 1.  The e4m3 encoding is torch's CPU cast to float8_e4m3fn
+(OCP E4M3FN), a library routine; the clamp is needed because that cast does not
+saturate (470 becomes NaN).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+SEED_BASE = 20250226
+E4M3_MAX = 448.0
+BLOCK_K = 128
+
+
+def _rng(seed: int, stream: int) -> np.random.Generator:
+    """Child stream `stream` of SeedSequence(seed) (PCG64)."""
+    ss = np.random.SeedSequence(seed)
+    return np.random.Generator(np.random.PCG64(ss.spawn(stream + 1)[stream]))
+
+
+def _encode_e4m3(y: np.ndarray) -> np.ndarray:
+    """fp32 values already in [-448, 448] -> e4m3fn bytes (RNE), via torch's CPU cast."""
+    t = torch.from_numpy(np.ascontiguousarray(y, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def quantize_1x128(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """x fp32 [R, K] (K % 128 == 0) -> (q uint8 [R, K], s fp32 [R, K/128]).
+
+    One scale per row and 128-wide K group, as the activation operand of the
+    pages' usage example ([M, K] with [M, K//128] scales).
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    r, k = x.shape
+    assert k % BLOCK_K == 0, "K must be a multiple of 128"
+    g = x.reshape(r, k // BLOCK_K, BLOCK_K)
+    amax = np.abs(g).max(axis=2)
+    s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    s[amax == 0] = np.float32(1.0)
+    y = np.clip(g / s[:, :, None], -E4M3_MAX, E4M3_MAX).astype(np.float32)
+    return _encode_e4m3(y.reshape(r, k)), s
+
+
+def quantize_128x128(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """x fp32 [N, K] -> (q uint8 [N, K], s fp32 [ceil(N/128), K/128]).
+
+    One scale per 128x128 block, the last row block clipped to the rows that
+    exist (the pages' example pairs N = 2112 with a [17, 56] scale tensor).
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    n, k = x.shape
+    assert k % BLOCK_K == 0, "K must be a multiple of 128"
+    nb = (n + BLOCK_K - 1) // BLOCK_K
+    kb = k // BLOCK_K
+    s = np.empty((nb, kb), dtype=np.float32)
+    q = np.empty((n, k), dtype=np.uint8)
+    for i in range(nb):
+        blk = x[i * BLOCK_K:(i + 1) * BLOCK_K].reshape(-1, kb, BLOCK_K)
+        amax = np.abs(blk).max(axis=(0, 2))
+        si = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+        si[amax == 0] = np.float32(1.0)
+        s[i] = si
+        y = np.clip(blk / si[None, :, None], -E4M3_MAX, E4M3_MAX).astype(np.float32)
+        q[i * BLOCK_K:(i + 1) * BLOCK_K] = _encode_e4m3(y.reshape(-1, k))
+    return q, s
+
+
+def _normal(rng: np.random.Generator, shape) -> np.ndarray:
+    return rng.standard_normal(size=shape, dtype=np.float32)
+
+
+@dataclass
+class Dense:
+    """Dense NT problem: A [M,K] + sa [M,K/128]; B [N,K] + sb [ceil(N/128),K/128]."""
+    m: int
+    n: int
+    k: int
+    a: np.ndarray
+    sa: np.ndarray
+    b: np.ndarray
+    sb: np.ndarray
+
+
+def make_dense(m: int, n: int, k: int, seed: int) -> Dense:
+    a, sa = quantize_1x128(_normal(_rng(seed, 0), (m, k)))
+    b, sb = quantize_128x128(_normal(_rng(seed, 1), (n, k)))
+    return Dense(m, n, k, a, sa, b, sb)
+
+
+def _grouped_rhs(g: int, n: int, k: int, seed: int) -> tuple[np.ndarray, np.ndarray]:
+    nb = (n + BLOCK_K - 1) // BLOCK_K
+    b = np.empty((g, n, k), dtype=np.uint8)
+    sb = np.empty((g, nb, k // BLOCK_K), dtype=np.float32)
+    rng = _rng(seed, 1)
+    for e in range(g):
+        b[e], sb[e] = quantize_128x128(_normal(rng, (n, k)))
+    return b, sb
+
+
+@dataclass
+class Contiguous:
+    """MoE contiguous layout: rows of all experts stacked, one expert id per row.
+
+    Each expert's segment is `rows_per_expert` rows (a multiple of 128): the
+    first `valid[e]` rows carry id e, the rest are padding rows with id -1 that
+    hold random A data (so wrongly computed padding is visible).
+    """
+    g: int
+    m_total: int
+    n: int
+    k: int
+    a: np.ndarray
+    sa: np.ndarray
+    b: np.ndarray
+    sb: np.ndarray
+    m_indices: np.ndarray
+    valid: np.ndarray = field(default_factory=lambda: np.zeros(0, np.int64))
+
+
+def make_contiguous(g: int, rows_per_expert: int, n: int, k: int, seed: int,
+                    pad: bool = True, max_pad: int = 127) -> Contiguous:
+    assert rows_per_expert % BLOCK_K == 0
+    m_total = g * rows_per_expert
+    a, sa = quantize_1x128(_normal(_rng(seed, 0), (m_total, k)))
+    b, sb = _grouped_rhs(g, n, k, seed)
+    rng = _rng(seed, 3)
+    pads = rng.integers(0, max_pad + 1, size=g) if pad else np.zeros(g, np.int64)
+    pads = np.minimum(pads, rows_per_expert)
+    ids = np.full(m_total, -1, dtype=np.int32)
+    for e in range(g):
+        v = rows_per_expert - int(pads[e])
+        ids[e * rows_per_expert:e * rows_per_expert + v] = e
+    return Contiguous(g, m_total, n, k, a, sa, b, sb, ids,
+                      (rows_per_expert - pads).astype(np.int64))
+
+
+@dataclass
+class Masked:
+    """MoE masked layout: A [G, M_max, K]; only rows < masked_m[g] are computed."""
+    g: int
+    m_max: int
+    n: int
+    k: int
+    a: np.ndarray
+    sa: np.ndarray
+    b: np.ndarray
+    sb: np.ndarray
+    masked_m: np.ndarray
+
+
+def make_masked(g: int, m_max: int, n: int, k: int, seed: int,
+                lo: int = 64, hi: int = 192, masked_m=None) -> Masked:
+    a, sa = quantize_1x128(_normal(_rng(seed, 0), (g * m_max, k)))
+    b, sb = _grouped_rhs(g, n, k, seed)
+    if masked_m is None:
+        masked_m = _rng(seed, 4).integers(lo, hi + 1, size=g)
+    masked_m = np.asarray(masked_m, dtype=np.int32)
+    return Masked(g, m_max, n, k, a.reshape(g, m_max, k), sa.reshape(g, m_max, k // BLOCK_K),
+                  b, sb, masked_m)
+
+
+@dataclass
+class Wgrad:
+    """Weight-gradient NT problem: both operands token-contiguous with 1x128 scales.
+
+    A [M, T] + sa [M, T/128], B [N, T] + sb [N, T/128], D0 fp32 [G?, M, N].
+    `ks` lists the token count of each group (one group for the dense case).
+    """
+    m: int
+    n: int
+    ks: list
+    a: np.ndarray
+    sa: np.ndarray
+    b: np.ndarray
+    sb: np.ndarray
+    d0: np.ndarray
+
+
+def make_wgrad(m: int, n: int, ks, seed: int) -> Wgrad:
+    ks = [int(x) for x in ks]
+    t = sum(ks)
+    a, sa = quantize_1x128(_normal(_rng(seed, 0), (m, t)))
+    b, sb = quantize_1x128(_normal(_rng(seed, 1), (n, t)))
+    d0 = _normal(_rng(seed, 2), (len(ks), m, n))
+    return Wgrad(m, n, ks, a, sa, b, sb, d0)
