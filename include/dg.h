@@ -1,0 +1,140 @@
+/*
+ * dg.h -- C ABI of the MI355X (gfx950) FP8 fine-grained-scaled NT GEMM library.
+ *
+ * The operation (DeepSeek DeepGEMM 中文讲解, "主要特点": FP8 GEMM with
+ * fine-grained scaling, two-level accumulation on the vector units;
+ * "使用示例": operands are (fp8 [M,K], fp32 [M,K/128]) and
+ * (fp8 [N,K], fp32 [ceil(N/128),K/128]), output bf16 [M,N] allocated by the
+ * caller; "适用条件": K must be a multiple of 128):
+ *
+ *     C[m,n] = bf16( sum_kb sa[m,kb] * sb[n/128,kb] * sum_{k in kb} A[m,k]*B[n,k] )
+ *
+ * with kb running over the 128-wide K blocks.  "NT" means both A and B are
+ * stored K-contiguous (row-major A [M,K], B [N,K]).
+ *
+ * Conventions shared by every entry point:
+ *   - every tensor pointer is a DEVICE pointer owned by the caller; the
+ *     library never allocates, frees or keeps user memory and holds no
+ *     workspace, so calls may be captured into a HIP graph;
+ *   - tensors are row-major with the last dimension contiguous;
+ *   - fp8 = OCP E4M3FN bytes (what torch calls float8_e4m3fn); scales fp32;
+ *   - K_b = K/128, NB = ceil(N/128);
+ *   - a and b must be 16-byte aligned, scales 4-byte aligned, c 2-byte
+ *     aligned (bf16) or d 4-byte aligned (fp32);
+ *   - work is enqueued on `stream` and the call returns without waiting;
+ *   - arguments are validated on the host BEFORE any HIP call; a bad argument
+ *     returns a status and enqueues nothing.  No call aborts or throws.
+ *   - device-resident control data (m_indices, masked_m) cannot be checked on
+ *     the host; out-of-range values mean "skip": a row whose expert id is not
+ *     in [0, G) is left untouched, masked_m[g] is clamped to [0, M_max].
+ */
+#ifndef DG_MI355X_H
+#define DG_MI355X_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DG_SUCCESS = 0,
+  DG_ERROR_INVALID_VALUE = 1, /* null pointer, a size <= 0, G <= 0           */
+  DG_ERROR_UNSUPPORTED = 2,   /* K % 128 != 0, misalignment, layout limits   */
+  DG_ERROR_LAUNCH = 3         /* the HIP runtime reported a launch failure   */
+} dg_status;
+
+/* Dense FP8 NT GEMM (DeepGEMM pages, "使用示例": the normal FP8 GEMM call).
+ *   a  [M,K] fp8,  sa [M,K_b] fp32  (one scale per row and 128-wide K block)
+ *   b  [N,K] fp8,  sb [NB,K_b] fp32 (one scale per 128x128 block)
+ *   c  [M,N] bf16, every element written.
+ * M, N >= 1; K >= 128 and K % 128 == 0. */
+dg_status dg_gemm_fp8_nt(const void* a, const float* sa, const void* b, const float* sb,
+                         void* c, int m, int n, int k, hipStream_t stream);
+
+/* MoE grouped GEMM, contiguous layout (DeepGEMM pages, "分组 GEMM": training
+ * forward and inference prefill; "使用示例": m_indices gives each LHS row its
+ * group).  The rows of all experts are stacked into one LHS:
+ *   a  [M_total,K] fp8, sa [M_total,K_b] fp32
+ *   b  [G,N,K] fp8,     sb [G,NB,K_b] fp32
+ *   m_indices [M_total] int32 (device): expert of each row, -1 = padding row
+ *   c  [M_total,N] bf16: rows with an id in [0,G) are written, others untouched.
+ * Layout limit: M_total % 128 == 0 and every aligned 128-row block holds rows
+ * of at most one expert (each expert's segment padded to a multiple of 128
+ * with -1 rows); rows of any other expert inside such a block are skipped. */
+dg_status dg_grouped_fp8_contiguous(const void* a, const float* sa, const void* b,
+                                    const float* sb, void* c, const int32_t* m_indices,
+                                    int m_total, int n, int k, int num_groups,
+                                    hipStream_t stream);
+
+/* MoE grouped GEMM, masked layout (DeepGEMM pages, "分组 GEMM": inference
+ * decode, the graph-captured case -- the valid row counts stay on the device
+ * and no host synchronisation happens).
+ *   a  [G,M_max,K] fp8, sa [G,M_max,K_b] fp32
+ *   b  [G,N,K] fp8,     sb [G,NB,K_b] fp32
+ *   masked_m [G] int32 (device): rows r < min(max(masked_m[g],0), M_max) of
+ *            group g are computed
+ *   c  [G,M_max,N] bf16: only those rows are written, others untouched. */
+dg_status dg_grouped_fp8_masked(const void* a, const float* sa, const void* b,
+                                const float* sb, void* c, const int32_t* masked_m,
+                                int num_groups, int m_max, int n, int k, hipStream_t stream);
+
+/* Weight-gradient FP8 GEMM with fp32 output accumulated into D (DeepGEMM
+ * pages, "反向传播中的梯度计算": dW from FP8 inputs, fp32 result without an
+ * explicit cast).  K is the token dimension; both operands are token-
+ * contiguous and scaled per row and per 128 tokens:
+ *   a [M,K] fp8, sa [M,K_b] fp32;  b [N,K] fp8, sb [N,K_b] fp32
+ *   d [M,N] fp32, updated in place: d += sum_kb sa[m,kb]*sb[n,kb]*block sum. */
+dg_status dg_wgrad_fp8_nt(const void* a, const float* sa, const void* b, const float* sb,
+                          float* d, int m, int n, int k, hipStream_t stream);
+
+/* K-grouped weight gradient (same passage: per-expert gradients in one call).
+ * The token ranges of the G groups are concatenated along K:
+ *   a [M,T] fp8, sa [M,T/128]; b [N,T] fp8, sb [N,T/128]; T = sum ks[g]
+ *   ks_host [G] int32 on the HOST: token count of each group, each a
+ *           multiple of 128 (0 allowed: that group's D is left as it is)
+ *   d [G,M,N] fp32, d[g] += the weight gradient over group g's tokens.
+ * Layout limit: G <= 256. */
+dg_status dg_k_grouped_wgrad_fp8_nt(const void* a, const float* sa, const void* b,
+                                    const float* sb, float* d, const int32_t* ks_host,
+                                    int num_groups, int m, int n, hipStream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* dg_status_string(dg_status s);
+
+/* ---- introspection (host only, no GPU needed) ---------------------------- */
+
+typedef enum {
+  DG_KIND_DENSE = 0,
+  DG_KIND_CONTIGUOUS = 1,
+  DG_KIND_MASKED = 2,
+  DG_KIND_WGRAD = 3,
+  DG_KIND_K_GROUPED_WGRAD = 4
+} dg_kind;
+
+/* Tile configuration the per-shape heuristic picks (DeepGEMM pages: block
+ * sizes and wave counts are chosen automatically per shape; non-power-of-two
+ * block sizes raise GPU utilisation).  `m` is the rows per group (M, M_total,
+ * M_max), `k` the K (or total tokens) and `num_cus` the compute-unit count the
+ * persistent grid is sized for. */
+typedef struct {
+  int block_m;      /* output rows per workgroup tile                        */
+  int block_n;      /* output columns per workgroup tile                     */
+  int waves_m;      /* waves along M (4 waves per workgroup in total)        */
+  int waves_n;      /* waves along N                                         */
+  int tiles;        /* tile count (an upper bound for the masked layout)     */
+  int grid;         /* persistent workgroups launched                        */
+} dg_tile_config;
+
+dg_status dg_select_config(int kind, int m, int n, int k, int num_groups, int num_cus,
+                           dg_tile_config* out);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int dg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DG_MI355X_H */

@@ -1,0 +1,215 @@
+"""Python binding of the MI355X FP8 fine-grained-scaled NT GEMM library.
+
+Argument marshalling only: every function below checks tensor dtypes, shapes
+and devices, then calls the C ABI (include/dg.h) of libdg_mi355x.so with raw
+device pointers and the current HIP stream.  All arithmetic runs in the HIP
+kernels; there is no CPU path.  If the library has not been built the import
+fails loudly (build it with `python -m moe_grouped_gemm_x128_amd.build`).
+
+The C-named functions mirror the C entry points one to one.  The
+`*_fp8_fp8_*` names follow the call style of the DeepGEMM pages' usage example
+(operands passed as (fp8 tensor, fp32 scale tensor) tuples, output tensor
+preallocated by the caller).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads torch's HIP runtime first, so the library binds to it
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdg_mi355x.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build the HIP library first "
+        "(python -m moe_grouped_gemm_x128_amd.build); there is no fallback path")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i32 = ctypes.c_void_p, ctypes.c_int
+_lib.dg_gemm_fp8_nt.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]
+_lib.dg_grouped_fp8_contiguous.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]
+_lib.dg_grouped_fp8_masked.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]
+_lib.dg_wgrad_fp8_nt.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]
+_lib.dg_k_grouped_wgrad_fp8_nt.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]
+for _f in ("dg_gemm_fp8_nt", "dg_grouped_fp8_contiguous", "dg_grouped_fp8_masked",
+           "dg_wgrad_fp8_nt", "dg_k_grouped_wgrad_fp8_nt"):
+    getattr(_lib, _f).restype = ctypes.c_int
+_lib.dg_status_string.argtypes = [ctypes.c_int]
+_lib.dg_status_string.restype = ctypes.c_char_p
+_lib.dg_version.restype = ctypes.c_int
+
+
+class TileConfig(ctypes.Structure):
+    _fields_ = [("block_m", ctypes.c_int), ("block_n", ctypes.c_int), ("waves_m", ctypes.c_int),
+                ("waves_n", ctypes.c_int), ("tiles", ctypes.c_int), ("grid", ctypes.c_int)]
+
+
+_lib.dg_select_config.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(TileConfig)]
+_lib.dg_select_config.restype = ctypes.c_int
+
+KIND_DENSE, KIND_CONTIGUOUS, KIND_MASKED, KIND_WGRAD, KIND_K_GROUPED_WGRAD = range(5)
+FP8 = torch.float8_e4m3fn
+
+
+class DGError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.dg_status_string(status).decode()
+        super().__init__(f"{where}: status {status} ({msg})")
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise DGError(status, where)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(*ts):
+    dev = ts[0].device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on the GPU")
+    for t in ts:
+        if t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _fp8(t, name):
+    if t.dtype not in (FP8, torch.uint8):
+        raise TypeError(f"{name} must be float8_e4m3fn (or its uint8 bytes), got {t.dtype}")
+
+
+def _f32(t, name):
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32, got {t.dtype}")
+
+
+def _shape(t, shape, name):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def version() -> int:
+    return _lib.dg_version()
+
+
+def select_config(kind: int, m: int, n: int, k: int, num_groups: int = 1, num_cus: int = 256) -> dict:
+    """Tile configuration the heuristic picks (host only, no GPU needed)."""
+    cfg = TileConfig()
+    _check(_lib.dg_select_config(kind, m, n, k, num_groups, num_cus, ctypes.byref(cfg)),
+           "dg_select_config")
+    return {f: getattr(cfg, f) for f, _ in TileConfig._fields_}
+
+
+# ---------------------------------------------------------------- C names ---
+
+def dg_gemm_fp8_nt(a, sa, b, sb, c):
+    """C[M,N] bf16 = fine-grained-scaled A[M,K] . B[N,K]^T (see include/dg.h)."""
+    _fp8(a, "a"); _fp8(b, "b"); _f32(sa, "sa"); _f32(sb, "sb")
+    m, k = a.shape
+    n = b.shape[0]
+    _shape(b, (n, k), "b"); _shape(sa, (m, k // 128), "sa"); _shape(sb, ((n + 127) // 128, k // 128), "sb")
+    _shape(c, (m, n), "c")
+    if c.dtype != torch.bfloat16:
+        raise TypeError("c must be bfloat16")
+    _dev(a, sa, b, sb, c)
+    _check(_lib.dg_gemm_fp8_nt(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(c), m, n, k, _stream(c)),
+           "dg_gemm_fp8_nt")
+    return c
+
+
+def dg_grouped_fp8_contiguous(a, sa, b, sb, c, m_indices):
+    _fp8(a, "a"); _fp8(b, "b"); _f32(sa, "sa"); _f32(sb, "sb")
+    m_total, k = a.shape
+    g, n, _ = b.shape
+    _shape(b, (g, n, k), "b"); _shape(sa, (m_total, k // 128), "sa")
+    _shape(sb, (g, (n + 127) // 128, k // 128), "sb"); _shape(c, (m_total, n), "c")
+    _shape(m_indices, (m_total,), "m_indices")
+    if m_indices.dtype != torch.int32:
+        raise TypeError("m_indices must be int32")
+    if c.dtype != torch.bfloat16:
+        raise TypeError("c must be bfloat16")
+    _dev(a, sa, b, sb, c, m_indices)
+    _check(_lib.dg_grouped_fp8_contiguous(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(c), _ptr(m_indices),
+                                          m_total, n, k, g, _stream(c)), "dg_grouped_fp8_contiguous")
+    return c
+
+
+def dg_grouped_fp8_masked(a, sa, b, sb, c, masked_m):
+    _fp8(a, "a"); _fp8(b, "b"); _f32(sa, "sa"); _f32(sb, "sb")
+    g, m_max, k = a.shape
+    n = b.shape[1]
+    _shape(b, (g, n, k), "b"); _shape(sa, (g, m_max, k // 128), "sa")
+    _shape(sb, (g, (n + 127) // 128, k // 128), "sb"); _shape(c, (g, m_max, n), "c")
+    _shape(masked_m, (g,), "masked_m")
+    if masked_m.dtype != torch.int32:
+        raise TypeError("masked_m must be int32")
+    if c.dtype != torch.bfloat16:
+        raise TypeError("c must be bfloat16")
+    _dev(a, sa, b, sb, c, masked_m)
+    _check(_lib.dg_grouped_fp8_masked(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(c), _ptr(masked_m),
+                                      g, m_max, n, k, _stream(c)), "dg_grouped_fp8_masked")
+    return c
+
+
+def dg_wgrad_fp8_nt(a, sa, b, sb, d):
+    _fp8(a, "a"); _fp8(b, "b"); _f32(sa, "sa"); _f32(sb, "sb")
+    m, k = a.shape
+    n = b.shape[0]
+    _shape(b, (n, k), "b"); _shape(sa, (m, k // 128), "sa"); _shape(sb, (n, k // 128), "sb")
+    _shape(d, (m, n), "d"); _f32(d, "d")
+    _dev(a, sa, b, sb, d)
+    _check(_lib.dg_wgrad_fp8_nt(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(d), m, n, k, _stream(d)),
+           "dg_wgrad_fp8_nt")
+    return d
+
+
+def dg_k_grouped_wgrad_fp8_nt(a, sa, b, sb, d, ks):
+    """ks: per-group token counts (host list/tuple of ints, multiples of 128)."""
+    _fp8(a, "a"); _fp8(b, "b"); _f32(sa, "sa"); _f32(sb, "sb")
+    ks = [int(x) for x in ks]
+    g = len(ks)
+    m, t = a.shape
+    n = b.shape[0]
+    if sum(ks) != t:
+        raise ValueError(f"sum(ks)={sum(ks)} does not match the token dimension {t}")
+    _shape(b, (n, t), "b"); _shape(sa, (m, t // 128), "sa"); _shape(sb, (n, t // 128), "sb")
+    _shape(d, (g, m, n), "d"); _f32(d, "d")
+    _dev(a, sa, b, sb, d)
+    ks_arr = (ctypes.c_int32 * g)(*ks)
+    _check(_lib.dg_k_grouped_wgrad_fp8_nt(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(d), ks_arr, g, m, n,
+                                          _stream(d)), "dg_k_grouped_wgrad_fp8_nt")
+    return d
+
+
+# ------------------------------------------------------ page-style names ---
+
+def gemm_fp8_fp8_bf16_nt(lhs, rhs, out):
+    return dg_gemm_fp8_nt(lhs[0], lhs[1], rhs[0], rhs[1], out)
+
+
+def m_grouped_gemm_fp8_fp8_bf16_nt_contiguous(lhs, rhs, out, m_indices):
+    return dg_grouped_fp8_contiguous(lhs[0], lhs[1], rhs[0], rhs[1], out, m_indices)
+
+
+def m_grouped_gemm_fp8_fp8_bf16_nt_masked(lhs, rhs, out, masked_m):
+    return dg_grouped_fp8_masked(lhs[0], lhs[1], rhs[0], rhs[1], out, masked_m)
+
+
+def wgrad_gemm_fp8_fp8_fp32_nt(lhs, rhs, out):
+    return dg_wgrad_fp8_nt(lhs[0], lhs[1], rhs[0], rhs[1], out)
+
+
+def k_grouped_wgrad_gemm_fp8_fp8_fp32_nt(lhs, rhs, out, ks):
+    return dg_k_grouped_wgrad_fp8_nt(lhs[0], lhs[1], rhs[0], rhs[1], out, ks)

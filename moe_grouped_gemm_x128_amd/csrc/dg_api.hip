@@ -1,0 +1,289 @@
+// dg_api.hip -- the C ABI (include/dg.h): host-side validation, the per-shape
+// tile heuristic and kernel dispatch.  Validation runs before any HIP call, so
+// every error path can be exercised on a machine without a GPU.
+#include <atomic>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/dg.h"
+#include "dg_kernel.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];  // 0 = not queried yet
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Compute units of the current device (cached per device).
+int device_cus(int* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (dev >= 0 && dev < kMaxDevices) {
+    int v = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (v > 0) {
+      *out = v;
+      return 0;
+    }
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return -1;
+  if (dev >= 0 && dev < kMaxDevices) g_cu_count[dev].store(cus, std::memory_order_relaxed);
+  *out = cus;
+  return 0;
+}
+
+// Workgroups per CU an instance can keep resident: LDS-limited (160 KB per CU).
+int occupancy(const dg::TileShape& s) {
+  const int lds = 2 * (s.bm + s.bn) * 128 + 2 * 4 * (s.bm + s.bn) + 4 * s.bm + 64;
+  int occ = (160 * 1024) / lds;
+  if (occ > 2) occ = 2;  // register file: two 4-wave workgroups per CU
+  return occ < 1 ? 1 : occ;
+}
+
+bool parse_forced(dg::TileShape* s) {
+  const char* e = std::getenv("DG_FORCE_TILE");
+  if (!e || !*e) return false;
+  int bm, bn, wm, wn;
+  if (std::sscanf(e, "%dx%dx%dx%d", &bm, &bn, &wm, &wn) != 4) return false;
+  *s = dg::TileShape{bm, bn, wm, wn};
+  return true;
+}
+
+// Per-shape tile choice (DeepGEMM pages: block sizes and wave counts are
+// selected per shape; small M underuses the matrix units).  `rows` is the
+// output rows per group, `groups` the number of groups whose tiles share the
+// launch (masked: an upper bound from M_max).
+dg::TileShape heuristic(int kind, int rows, int n, int k, int groups, int num_cus) {
+  (void)k;
+  const dg::TileShape big{128, 128, 2, 2};
+  const dg::TileShape mid{128, 64, 2, 2};
+  const dg::TileShape small_m{64, 128, 1, 4};
+  const dg::TileShape small_mn{64, 64, 1, 4};
+  const dg::TileShape tiny{64, 32, 2, 2};
+  if (kind == DG_KIND_MASKED || rows <= 64) {
+    // few rows: narrow column tiles so enough workgroups stream B
+    const int per_group_m = ceil_div(rows, 64);
+    const dg::TileShape cands[3] = {small_m, small_mn, tiny};
+    for (const auto& c : cands) {
+      const long tiles = (long)groups * per_group_m * ceil_div(n, c.bn);
+      if (tiles >= num_cus) return c;
+    }
+    return tiny;
+  }
+  const long tiles_big = (long)groups * ceil_div(rows, 128) * ceil_div(n, 128);
+  if (tiles_big >= num_cus) return big;
+  return mid;
+}
+
+struct Launch {
+  dg::TileShape shape;
+  int grid;
+};
+
+dg_status plan(int kind, int rows, int n, int k, int groups, int num_cus, dg::Params& p, Launch& l) {
+  dg::TileShape s;
+  if (!parse_forced(&s)) s = heuristic(kind, rows, n, k, groups, num_cus);
+  if (!dg::has_instance(kind, s)) return DG_ERROR_UNSUPPORTED;
+  if (kind == DG_KIND_CONTIGUOUS && 128 % s.bm != 0) return DG_ERROR_UNSUPPORTED;
+  p.tiles_m = ceil_div(rows, s.bm);
+  p.tiles_n = ceil_div(n, s.bn);
+  const long tiles = (long)groups * p.tiles_m * p.tiles_n;
+  if (tiles > 0x7fffffffL) return DG_ERROR_UNSUPPORTED;
+  p.tiles = (int)tiles;
+  const long slots = (long)num_cus * occupancy(s);
+  long grid = tiles < slots ? tiles : slots;
+  if (grid > 8) grid -= grid % 8;  // keep workgroup -> XCD round robin aligned
+  if (grid < 1) grid = 1;
+  l.shape = s;
+  l.grid = (int)grid;
+  if (std::getenv("DG_LOG"))
+    std::fprintf(stderr, "[dg] kind=%d rows=%d n=%d k=%d G=%d -> tile %dx%d waves %dx%d tiles=%ld grid=%ld\n",
+                 kind, rows, n, k, groups, s.bm, s.bn, s.wm, s.wn, tiles, grid);
+  return DG_SUCCESS;
+}
+
+dg_status run(int kind, dg::Params& p, int rows, int n, int k, int groups, hipStream_t stream) {
+  int cus = 0;
+  if (device_cus(&cus) != 0) return DG_ERROR_LAUNCH;
+  Launch l;
+  dg_status st = plan(kind, rows, n, k, groups, cus, p, l);
+  if (st != DG_SUCCESS) return st;
+  (void)hipGetLastError();  // clear a stale error from unrelated work
+  if (dg::launch(kind, l.shape, p, l.grid, stream) != hipSuccess) return DG_ERROR_LAUNCH;
+  return DG_SUCCESS;
+}
+
+dg::Params base_params() {
+  dg::Params p;
+  std::memset(&p, 0, sizeof(p));
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+dg_status dg_gemm_fp8_nt(const void* a, const float* sa, const void* b, const float* sb, void* c,
+                         int m, int n, int k, hipStream_t stream) {
+  if (!a || !sa || !b || !sb || !c) return DG_ERROR_INVALID_VALUE;
+  if (m <= 0 || n <= 0 || k <= 0) return DG_ERROR_INVALID_VALUE;
+  if (k % 128 != 0) return DG_ERROR_UNSUPPORTED;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(sa, 4) || !aligned(sb, 4) || !aligned(c, 2))
+    return DG_ERROR_UNSUPPORTED;
+  dg::Params p = base_params();
+  p.a = static_cast<const uint8_t*>(a);
+  p.sa = sa;
+  p.b = static_cast<const uint8_t*>(b);
+  p.sb = sb;
+  p.out = c;
+  p.m = m;
+  p.n = n;
+  p.lda = k;
+  p.kbs = k / 128;
+  p.groups = 1;
+  p.vec_out = (n % 4 == 0) && aligned(c, 8);
+  return run(dg::KIND_DENSE, p, m, n, k, 1, stream);
+}
+
+dg_status dg_grouped_fp8_contiguous(const void* a, const float* sa, const void* b, const float* sb,
+                                    void* c, const int32_t* m_indices, int m_total, int n, int k,
+                                    int num_groups, hipStream_t stream) {
+  if (!a || !sa || !b || !sb || !c || !m_indices) return DG_ERROR_INVALID_VALUE;
+  if (m_total <= 0 || n <= 0 || k <= 0 || num_groups <= 0) return DG_ERROR_INVALID_VALUE;
+  if (k % 128 != 0 || m_total % 128 != 0) return DG_ERROR_UNSUPPORTED;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(sa, 4) || !aligned(sb, 4) || !aligned(c, 2) ||
+      !aligned(m_indices, 4))
+    return DG_ERROR_UNSUPPORTED;
+  dg::Params p = base_params();
+  p.a = static_cast<const uint8_t*>(a);
+  p.sa = sa;
+  p.b = static_cast<const uint8_t*>(b);
+  p.sb = sb;
+  p.out = c;
+  p.ctrl = m_indices;
+  p.m = m_total;
+  p.n = n;
+  p.lda = k;
+  p.kbs = k / 128;
+  p.groups = num_groups;
+  p.vec_out = (n % 4 == 0) && aligned(c, 8);
+  return run(dg::KIND_CONTIGUOUS, p, m_total, n, k, 1, stream);
+}
+
+dg_status dg_grouped_fp8_masked(const void* a, const float* sa, const void* b, const float* sb,
+                                void* c, const int32_t* masked_m, int num_groups, int m_max, int n,
+                                int k, hipStream_t stream) {
+  if (!a || !sa || !b || !sb || !c || !masked_m) return DG_ERROR_INVALID_VALUE;
+  if (num_groups <= 0 || m_max <= 0 || n <= 0 || k <= 0) return DG_ERROR_INVALID_VALUE;
+  if (k % 128 != 0) return DG_ERROR_UNSUPPORTED;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(sa, 4) || !aligned(sb, 4) || !aligned(c, 2) ||
+      !aligned(masked_m, 4))
+    return DG_ERROR_UNSUPPORTED;
+  dg::Params p = base_params();
+  p.a = static_cast<const uint8_t*>(a);
+  p.sa = sa;
+  p.b = static_cast<const uint8_t*>(b);
+  p.sb = sb;
+  p.out = c;
+  p.ctrl = masked_m;
+  p.m = m_max;
+  p.n = n;
+  p.lda = k;
+  p.kbs = k / 128;
+  p.groups = num_groups;
+  p.vec_out = (n % 4 == 0) && aligned(c, 8);
+  return run(dg::KIND_MASKED, p, m_max, n, k, num_groups, stream);
+}
+
+dg_status dg_wgrad_fp8_nt(const void* a, const float* sa, const void* b, const float* sb, float* d,
+                          int m, int n, int k, hipStream_t stream) {
+  if (!a || !sa || !b || !sb || !d) return DG_ERROR_INVALID_VALUE;
+  if (m <= 0 || n <= 0 || k <= 0) return DG_ERROR_INVALID_VALUE;
+  if (k % 128 != 0) return DG_ERROR_UNSUPPORTED;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(sa, 4) || !aligned(sb, 4) || !aligned(d, 4))
+    return DG_ERROR_UNSUPPORTED;
+  dg::Params p = base_params();
+  p.a = static_cast<const uint8_t*>(a);
+  p.sa = sa;
+  p.b = static_cast<const uint8_t*>(b);
+  p.sb = sb;
+  p.out = d;
+  p.m = m;
+  p.n = n;
+  p.lda = k;
+  p.kbs = k / 128;
+  p.groups = 1;
+  p.vec_out = (n % 4 == 0) && aligned(d, 16);
+  return run(dg::KIND_WGRAD, p, m, n, k, 1, stream);
+}
+
+dg_status dg_k_grouped_wgrad_fp8_nt(const void* a, const float* sa, const void* b, const float* sb,
+                                    float* d, const int32_t* ks_host, int num_groups, int m, int n,
+                                    hipStream_t stream) {
+  if (!a || !sa || !b || !sb || !d || !ks_host) return DG_ERROR_INVALID_VALUE;
+  if (num_groups <= 0 || m <= 0 || n <= 0) return DG_ERROR_INVALID_VALUE;
+  if (num_groups > dg::kMaxKGroups) return DG_ERROR_UNSUPPORTED;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(sa, 4) || !aligned(sb, 4) || !aligned(d, 4))
+    return DG_ERROR_UNSUPPORTED;
+  dg::Params p = base_params();
+  long total = 0;
+  for (int g = 0; g < num_groups; ++g) {
+    if (ks_host[g] < 0) return DG_ERROR_INVALID_VALUE;
+    if (ks_host[g] % 128 != 0) return DG_ERROR_UNSUPPORTED;
+    p.kb_begin[g] = (int)(total / 128);
+    total += ks_host[g];
+  }
+  if (total > 0x7fffffffL) return DG_ERROR_UNSUPPORTED;
+  p.kb_begin[num_groups] = (int)(total / 128);
+  if (total == 0) return DG_SUCCESS;  // no tokens: every D[g] stays as it is
+  p.a = static_cast<const uint8_t*>(a);
+  p.sa = sa;
+  p.b = static_cast<const uint8_t*>(b);
+  p.sb = sb;
+  p.out = d;
+  p.m = m;
+  p.n = n;
+  p.lda = (int)total;
+  p.kbs = (int)(total / 128);
+  p.groups = num_groups;
+  p.vec_out = (n % 4 == 0) && aligned(d, 16);
+  return run(dg::KIND_KGROUPED, p, m, n, (int)total, num_groups, stream);
+}
+
+const char* dg_status_string(dg_status s) {
+  switch (s) {
+    case DG_SUCCESS: return "success";
+    case DG_ERROR_INVALID_VALUE: return "invalid value (null pointer or a size <= 0)";
+    case DG_ERROR_UNSUPPORTED: return "unsupported (K or row count not a multiple of 128, misaligned pointer, or layout limit)";
+    case DG_ERROR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+dg_status dg_select_config(int kind, int m, int n, int k, int num_groups, int num_cus,
+                           dg_tile_config* out) {
+  if (!out) return DG_ERROR_INVALID_VALUE;
+  if (kind < DG_KIND_DENSE || kind > DG_KIND_K_GROUPED_WGRAD) return DG_ERROR_INVALID_VALUE;
+  if (m <= 0 || n <= 0 || k <= 0 || num_groups <= 0 || num_cus <= 0) return DG_ERROR_INVALID_VALUE;
+  dg::Params p = base_params();
+  Launch l;
+  const int groups = (kind == DG_KIND_MASKED || kind == DG_KIND_K_GROUPED_WGRAD) ? num_groups : 1;
+  dg_status st = plan(kind, m, n, k, groups, num_cus, p, l);
+  if (st != DG_SUCCESS) return st;
+  out->block_m = l.shape.bm;
+  out->block_n = l.shape.bn;
+  out->waves_m = l.shape.wm;
+  out->waves_n = l.shape.wn;
+  out->tiles = p.tiles;
+  out->grid = l.grid;
+  return DG_SUCCESS;
+}
+
+int dg_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// dg_kernel.h -- kernel parameter block and launch interface shared by the
+// host dispatcher (dg_api.hip) and the gfx950 kernels (dg_kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dg {
+
+// Problem kinds; the kernel template is specialised on these.
+enum Kind : int {
+  KIND_DENSE = 0,       // C bf16 [M,N];      B scales per 128x128 block
+  KIND_CONTIGUOUS = 1,  // C bf16 [M_tot,N];  expert per row from m_indices
+  KIND_MASKED = 2,      // C bf16 [G,Mx,N];   rows < masked_m[g]
+  KIND_WGRAD = 3,       // D fp32 [M,N] +=;   B scales per row
+  KIND_KGROUPED = 4,    // D fp32 [G,M,N] +=; per-group K ranges
+};
+
+constexpr int kMaxKGroups = 256;
+
+struct Params {
+  const uint8_t* a;      // fp8 LHS (row stride lda bytes)
+  const float* sa;       // LHS scales, row stride kbs floats
+  const uint8_t* b;      // fp8 RHS, [G][N][lda]
+  const float* sb;       // RHS scales: [G][NB][kbs] (block) or [N][kbs] (row)
+  void* out;             // bf16 C or fp32 D
+  const int32_t* ctrl;   // m_indices (contiguous) or masked_m (masked)
+  int m;                 // rows per group: M, M_total or M_max
+  int n;                 // N
+  int lda;               // bytes per operand row: K, or total tokens T
+  int kbs;               // scale row stride in 128-blocks (lda / 128)
+  int groups;            // G (1 for dense and wgrad)
+  int tiles_m;           // ceil(m / BM)
+  int tiles_n;           // ceil(n / BN)
+  int tiles;             // tile count (upper bound for the masked layout)
+  int vec_out;           // 1 if 4 consecutive outputs may be stored as one vector
+  int kb_begin[kMaxKGroups + 1];  // K-grouped: first 128-block of each group
+};
+
+struct TileShape {
+  int bm, bn, wm, wn;
+};
+
+// Launches the kernel instance for (kind, shape) on `stream`.  Returns
+// hipErrorInvalidValue if no instance exists for that shape.
+hipError_t launch(int kind, const TileShape& shape, const Params& p, int grid,
+                  hipStream_t stream);
+
+// True if an instance exists for (kind, shape).
+bool has_instance(int kind, const TileShape& shape);
+
+}  // namespace dg

@@ -1,0 +1,177 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point that
+include/dg.h declares, rejects bad arguments before touching the GPU, and its
+tile heuristic obeys its invariants.  No compute call runs here."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dg.h")
+LIB = os.path.join(ROOT, "moe_grouped_gemm_x128_amd", "libdg_mi355x.so")
+
+INVALID, UNSUPPORTED, SUCCESS = 1, 2, 0
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from moe_grouped_gemm_x128_amd import build as b
+        b.build()
+    L = ctypes.CDLL(LIB)
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    L.dg_gemm_fp8_nt.argtypes = [vp, vp, vp, vp, vp, i, i, i, vp]
+    L.dg_grouped_fp8_contiguous.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, vp]
+    L.dg_grouped_fp8_masked.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, vp]
+    L.dg_wgrad_fp8_nt.argtypes = [vp, vp, vp, vp, vp, i, i, i, vp]
+    L.dg_k_grouped_wgrad_fp8_nt.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, vp]
+    L.dg_status_string.restype = ctypes.c_char_p
+    return L
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:dg_status|const char\*|int)\s+(dg_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for f in ("dg_gemm_fp8_nt", "dg_grouped_fp8_contiguous", "dg_grouped_fp8_masked",
+              "dg_wgrad_fp8_nt", "dg_k_grouped_wgrad_fp8_nt", "dg_status_string",
+              "dg_select_config", "dg_version"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_library_exports_nothing_but_c_symbols():
+    """Every exported dg_ symbol is declared in the header (extern "C", unmangled)."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = sorted({ln.split()[-1] for ln in out.splitlines() if " T dg_" in ln})
+    assert exported == declared_functions()
+
+
+def test_status_strings(lib):
+    for s in range(4):
+        assert len(lib.dg_status_string(s)) > 3
+    assert lib.dg_status_string(99) == b"unknown status"
+    assert lib.dg_version() >= 100
+
+
+# Fake device addresses: validation must reject before any dereference or HIP call.
+A16 = 0x10000
+MIS = 0x10001
+
+
+def test_dense_argument_errors(lib):
+    f = lib.dg_gemm_fp8_nt
+    assert f(None, A16, A16, A16, A16, 1, 1, 128, None) == INVALID
+    assert f(A16, A16, A16, A16, None, 1, 1, 128, None) == INVALID
+    assert f(A16, A16, A16, A16, A16, 0, 1, 128, None) == INVALID
+    assert f(A16, A16, A16, A16, A16, 1, -5, 128, None) == INVALID
+    assert f(A16, A16, A16, A16, A16, 1, 1, 0, None) == INVALID
+    assert f(A16, A16, A16, A16, A16, 1, 1, 100, None) == UNSUPPORTED   # K % 128
+    assert f(MIS, A16, A16, A16, A16, 1, 1, 128, None) == UNSUPPORTED   # a not 16B aligned
+    assert f(A16, A16, A16 + 8, A16, A16, 1, 1, 128, None) == UNSUPPORTED
+    assert f(A16, A16 + 2, A16, A16, A16, 1, 1, 128, None) == UNSUPPORTED  # scale alignment
+    assert f(A16, A16, A16, A16, MIS, 1, 1, 128, None) == UNSUPPORTED   # bf16 alignment
+
+
+def test_grouped_argument_errors(lib):
+    c = lib.dg_grouped_fp8_contiguous
+    assert c(A16, A16, A16, A16, A16, None, 128, 8, 128, 2, None) == INVALID
+    assert c(A16, A16, A16, A16, A16, A16, 128, 8, 128, 0, None) == INVALID
+    assert c(A16, A16, A16, A16, A16, A16, 100, 8, 128, 2, None) == UNSUPPORTED  # M_total % 128
+    assert c(A16, A16, A16, A16, A16, A16, 128, 8, 384 + 64, 2, None) == UNSUPPORTED
+    assert c(A16, A16, A16, A16, A16, A16 + 2, 128, 8, 128, 2, None) == UNSUPPORTED
+    m = lib.dg_grouped_fp8_masked
+    assert m(A16, A16, A16, A16, A16, None, 2, 256, 8, 128, None) == INVALID
+    assert m(A16, A16, A16, A16, A16, A16, 0, 256, 8, 128, None) == INVALID
+    assert m(A16, A16, A16, A16, A16, A16, 2, 0, 8, 128, None) == INVALID
+    assert m(A16, A16, A16, A16, A16, A16, 2, 256, 8, 200, None) == UNSUPPORTED
+
+
+def test_wgrad_argument_errors(lib):
+    w = lib.dg_wgrad_fp8_nt
+    assert w(A16, A16, A16, A16, None, 4, 4, 128, None) == INVALID
+    assert w(A16, A16, A16, A16, A16, 4, 4, 96, None) == UNSUPPORTED
+    assert w(A16, A16, A16, A16, A16 + 2, 4, 4, 128, None) == UNSUPPORTED
+    kg = lib.dg_k_grouped_wgrad_fp8_nt
+    ks = (ctypes.c_int32 * 3)(128, 256, 0)
+    assert kg(A16, A16, A16, A16, A16, None, 3, 4, 4, None) == INVALID
+    assert kg(A16, A16, A16, A16, A16, ks, 0, 4, 4, None) == INVALID
+    assert kg(A16, A16, A16, A16, A16, ks, 257, 4, 4, None) == UNSUPPORTED
+    bad = (ctypes.c_int32 * 2)(128, 100)
+    assert kg(A16, A16, A16, A16, A16, bad, 2, 4, 4, None) == UNSUPPORTED
+    neg = (ctypes.c_int32 * 2)(128, -128)
+    assert kg(A16, A16, A16, A16, A16, neg, 2, 4, 4, None) == INVALID
+    zero = (ctypes.c_int32 * 2)(0, 0)
+    assert kg(A16, A16, A16, A16, A16, zero, 2, 4, 4, None) == SUCCESS  # nothing to do, nothing enqueued
+
+
+# ------------------------------------------------------------- heuristic ---
+
+def _cfg(lib, kind, m, n, k, g=1, cus=256):
+    class Cfg(ctypes.Structure):
+        _fields_ = [(f, ctypes.c_int) for f in ("block_m", "block_n", "waves_m", "waves_n", "tiles", "grid")]
+    c = Cfg()
+    lib.dg_select_config.argtypes = [ctypes.c_int] * 6 + [ctypes.POINTER(Cfg)]
+    st = lib.dg_select_config(kind, m, n, k, g, cus, ctypes.byref(c))
+    assert st == SUCCESS
+    return {f: getattr(c, f) for f, _ in Cfg._fields_}
+
+
+SHAPES = [(0, m, n, k, 1) for m in (1, 64, 128, 4096)
+          for (n, k) in [(2112, 7168), (24576, 1536), (32768, 512), (7168, 16384), (4096, 7168), (7168, 2048)]]
+SHAPES += [(1, 32768, 4096, 7168, 4), (1, 65536, 7168, 2048, 8), (2, 256, 4096, 7168, 1),
+           (2, 256, 7168, 2048, 16), (3, 7168, 2048, 4096, 1), (4, 7168, 2048, 10240, 4)]
+
+
+@pytest.mark.parametrize("kind,m,n,k,g", SHAPES)
+def test_heuristic_invariants(lib, kind, m, n, k, g):
+    c = _cfg(lib, kind, m, n, k, g)
+    assert c["waves_m"] * c["waves_n"] == 4
+    assert c["block_m"] % (16 * c["waves_m"]) == 0 and c["block_n"] % (16 * c["waves_n"]) == 0
+    groups = g if kind in (2, 4) else 1
+    tiles = groups * -(-m // c["block_m"]) * -(-n // c["block_n"])
+    assert c["tiles"] == tiles
+    assert 1 <= c["grid"] <= tiles
+    if c["grid"] > 8:
+        assert c["grid"] % 8 == 0
+    assert c["grid"] <= 2 * 256
+    if kind == 1:
+        assert 128 % c["block_m"] == 0
+    assert _cfg(lib, kind, m, n, k, g) == c  # deterministic
+
+
+def test_heuristic_rejects_bad_queries(lib):
+    c = ctypes.c_int * 6
+    out = c()
+    lib.dg_select_config.argtypes = [ctypes.c_int] * 6 + [ctypes.c_void_p]
+    assert lib.dg_select_config(9, 1, 1, 128, 1, 256, ctypes.addressof(out)) == INVALID
+    assert lib.dg_select_config(0, 0, 1, 128, 1, 256, ctypes.addressof(out)) == INVALID
+    assert lib.dg_select_config(0, 1, 1, 128, 1, 256, None) == INVALID
+
+
+def test_python_binding_rejects_cpu_tensors_and_bad_shapes():
+    import torch
+    import moe_grouped_gemm_x128_amd as dg
+    a = torch.zeros(4, 128, dtype=torch.uint8)
+    sa = torch.ones(4, 1)
+    b = torch.zeros(8, 128, dtype=torch.uint8)
+    sb = torch.ones(1, 1)
+    c = torch.empty(4, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        dg.dg_gemm_fp8_nt(a, sa, b, sb, c)               # host tensors
+    with pytest.raises(ValueError):
+        dg.dg_gemm_fp8_nt(a, torch.ones(4, 2), b, sb, c)  # scale shape
+    with pytest.raises(TypeError):
+        dg.dg_gemm_fp8_nt(a, sa.double(), b, sb, c)
+    assert dg.select_config(dg.KIND_DENSE, 4096, 7168, 16384)["tiles"] > 0
