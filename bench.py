@@ -1,0 +1,279 @@
+"""Benchmark of the FP8 fine-grained-scaled NT GEMM library on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense]
+
+A step is one pass over the workload's GEMMs, each launched once through the
+C ABI on the current stream with inputs already resident in HBM.  The default
+workload is the dense sweep: M in {64,128,4096} x (N,K) in {(2112,7168),
+(24576,1536), (32768,512), (7168,16384), (4096,7168), (7168,2048)}, A scaled
+per 1x128, B per 128x128, bf16 out.  `value` is the step's algorithmic FLOPs
+(2*M*N*K per GEMM) over its measured time, in TFLOP/s.  Each GEMM is also
+bracketed by HIP events on the launch stream; the one with the largest time is
+the "dominant kernel" whose roofline fraction is reported.  The CPU oracle is
+timed on a bounded sample of the same workload's outputs (`cpu_baseline`).
+Other workloads (contiguous, masked, wgrad, k_grouped_wgrad, small) print a
+line of the same form.  Exactly one JSON line goes to stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP8 block-scaled GEMM TFLOPS (dense/grouped) and % of MI355X FP8 or HBM peak"
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+RIDGE = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Call:
+    """One GEMM launch of the step plus its algorithmic work."""
+
+    def __init__(self, name, flops, nbytes, fn, sample=None):
+        self.name, self.flops, self.bytes, self.fn, self.sample = name, flops, nbytes, fn, sample
+
+    @property
+    def bound(self):
+        return "mfma" if self.flops / self.bytes >= RIDGE else "hbm"
+
+
+def _dev(x):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
+
+
+def _sample_idx(rng, count, *highs):
+    return [rng.integers(0, h, count) for h in highs]
+
+
+# ------------------------------------------------------------- workloads ---
+
+def build_dense(small=False):
+    import torch
+    import moe_grouped_gemm_x128_amd as dg
+    from harness import inputs, workloads
+
+    shapes = [workloads.DENSE_SMALL] if small else workloads.dense_sweep()
+    seed = shapes[0]["seed"]
+    a_by_k, b_by_nk, calls = {}, {}, []
+    for s in shapes:
+        m, n, k = s["m"], s["n"], s["k"]
+        mmax = max(x["m"] for x in shapes if x["k"] == k)
+        if k not in a_by_k:
+            a, sa = inputs.quantize_1x128(inputs._normal(inputs._rng(seed + k, 0), (mmax, k)))
+            a_by_k[k] = (a, sa, _dev(a), _dev(sa))
+        if (n, k) not in b_by_nk:
+            b, sb = inputs.quantize_128x128(inputs._normal(inputs._rng(seed + n * 7 + k, 1), (n, k)))
+            b_by_nk[(n, k)] = (b, sb, _dev(b), _dev(sb))
+        a, sa, da, dsa = a_by_k[k]
+        b, sb, db, dsb = b_by_nk[(n, k)]
+        da_m, dsa_m = da[:m], dsa[:m]
+        out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        fn = (lambda da_m=da_m, dsa_m=dsa_m, db=db, dsb=dsb, out=out:
+              dg.dg_gemm_fp8_nt(da_m, dsa_m, db, dsb, out))
+        nbytes = m * k + m * (k // 128) * 4 + n * k + ((n + 127) // 128) * (k // 128) * 4 + m * n * 2
+
+        def sample(rng, count, a=a[:m], sa=sa[:m], b=b, sb=sb, m=m, n=n):
+            import oracle
+            r, c = _sample_idx(rng, count, m, n)
+            return oracle.gemm_fp8_nt_at(a, sa, b, sb, r, c)
+
+        calls.append(Call(s["name"], 2.0 * m * n * k, nbytes, fn, (sample, k)))
+    desc = ("dense FP8 NT GEMM sweep: M in {64,128,4096} x (N,K) in {(2112,7168),(24576,1536),"
+            "(32768,512),(7168,16384),(4096,7168),(7168,2048)}" if not small else "dense M=128 N=256 K=512")
+    return calls, {"workload": "dense_sweep" if not small else "dense_small", "description": desc,
+                   "shapes": len(calls), "scales": "A 1x128, B 128x128, fp32", "out": "bf16"}
+
+
+def build_contiguous():
+    import torch
+    import moe_grouped_gemm_x128_amd as dg
+    from harness import inputs, workloads
+
+    calls = []
+    for s in workloads.contiguous_sweep():
+        c = inputs.make_contiguous(s["g"], s["rows_per_expert"], s["n"], s["k"], s["seed"])
+        da, dsa, db, dsb, ids = _dev(c.a), _dev(c.sa), _dev(c.b), _dev(c.sb), _dev(c.m_indices)
+        out = torch.empty((c.m_total, c.n), dtype=torch.bfloat16, device="cuda")
+        fn = (lambda da=da, dsa=dsa, db=db, dsb=dsb, out=out, ids=ids:
+              dg.dg_grouped_fp8_contiguous(da, dsa, db, dsb, out, ids))
+        mv = int(c.valid.sum())
+        kb, nb = c.k // 128, (c.n + 127) // 128
+        nbytes = mv * c.k + mv * kb * 4 + c.g * c.n * c.k + c.g * nb * kb * 4 + c.m_total * 4 + mv * c.n * 2
+        calls.append(Call(s["name"], 2.0 * mv * c.n * c.k, nbytes, fn, None))
+    return calls, {"workload": "contiguous_sweep", "description":
+                   "MoE contiguous: G in {4,8}, 8192 rows per expert minus U{0..127} padding rows, "
+                   "(N,K) in {(4096,7168),(7168,2048)}"}
+
+
+def build_masked():
+    import torch
+    import moe_grouped_gemm_x128_amd as dg
+    from harness import inputs, workloads
+
+    calls = []
+    for s in workloads.masked_sweep():
+        x = inputs.make_masked(s["g"], s["m_max"], s["n"], s["k"], s["seed"])
+        da, dsa, db, dsb, mm = _dev(x.a), _dev(x.sa), _dev(x.b), _dev(x.sb), _dev(x.masked_m)
+        out = torch.empty((x.g, x.m_max, x.n), dtype=torch.bfloat16, device="cuda")
+        fn = (lambda da=da, dsa=dsa, db=db, dsb=dsb, out=out, mm=mm:
+              dg.dg_grouped_fp8_masked(da, dsa, db, dsb, out, mm))
+        mv = int(np.clip(x.masked_m, 0, x.m_max).sum())
+        kb, nb = x.k // 128, (x.n + 127) // 128
+        nbytes = mv * x.k + mv * kb * 4 + x.g * x.n * x.k + x.g * nb * kb * 4 + x.g * 4 + mv * x.n * 2
+        calls.append(Call(s["name"], 2.0 * mv * x.n * x.k, nbytes, fn, None))
+    return calls, {"workload": "masked_sweep", "description":
+                   "MoE masked decode: G in {1,2,4,16}, M_max=256, masked_m ~ U{64..192}, "
+                   "(N,K) in {(4096,7168),(7168,2048)}"}
+
+
+def build_wgrad(kgrouped=False):
+    import moe_grouped_gemm_x128_amd as dg
+    from harness import inputs, workloads
+
+    s = workloads.K_GROUPED_WGRAD if kgrouped else workloads.WGRAD
+    w = inputs.make_wgrad(s["m"], s["n"], s["ks"], s["seed"])
+    da, dsa, db, dsb = _dev(w.a), _dev(w.sa), _dev(w.b), _dev(w.sb)
+    d = _dev(w.d0 if kgrouped else w.d0[0])
+    t = sum(w.ks)
+    g = len(w.ks)
+    if kgrouped:
+        fn = lambda: dg.dg_k_grouped_wgrad_fp8_nt(da, dsa, db, dsb, d, w.ks)
+    else:
+        fn = lambda: dg.dg_wgrad_fp8_nt(da, dsa, db, dsb, d)
+    nbytes = (w.m + w.n) * t + (w.m + w.n) * (t // 128) * 4 + g * 2 * 4 * w.m * w.n
+    calls = [Call(s["name"], 2.0 * w.m * w.n * t, nbytes, fn, None)]
+    return calls, {"workload": s["name"], "description":
+                   f"weight gradient D[{w.m},{w.n}] += over tokens {w.ks}, 1x128 scales on both operands, fp32 D"}
+
+
+# --------------------------------------------------------------- timing ---
+
+def time_steps(calls, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        for c in calls:
+            c.fn()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+          for _ in range(steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for s in range(steps):
+        for i, c in enumerate(calls):
+            ev[s][i][0].record()
+            c.fn()
+            ev[s][i][1].record()
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    per = np.array([[ev[s][i][0].elapsed_time(ev[s][i][1]) for i in range(len(calls))] for s in range(steps)])
+    return total_ms, per.mean(axis=0)
+
+
+def cpu_baseline(calls, seconds):
+    """Time the CPU oracle on a bounded sample of the workload's outputs."""
+    import oracle
+    usable = [c for c in calls if c.sample is not None]
+    if not usable:
+        return None
+    rng = np.random.default_rng(12345)
+    total_k = sum(c.sample[1] for c in usable)
+    # calibrate: grow the sample until one pass takes a measurable share of
+    # the budget, then size the timed sample to the whole budget
+    per_shape = 64
+    while True:
+        t = time.perf_counter()
+        for c in usable:
+            c.sample[0](rng, per_shape)
+        dt = time.perf_counter() - t
+        if dt >= 0.1 * seconds or per_shape >= 1 << 22:
+            break
+        per_shape *= 4
+    rate = 2.0 * total_k * per_shape / max(dt, 1e-9)
+    per_shape = int(max(64, seconds * rate / (2.0 * total_k)))
+    t = time.perf_counter()
+    flops = 0.0
+    for c in usable:
+        c.sample[0](rng, per_shape)
+        flops += 2.0 * c.sample[1] * per_shape
+    dt = time.perf_counter() - t
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{per_shape} uniformly drawn outputs of each of the {len(usable)} GEMMs "
+                      f"({flops / 1e9:.1f} GFLOP, {dt:.1f} s, fp64 C oracle with OpenMP)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="dense",
+                    choices=["dense", "small", "contiguous", "masked", "wgrad", "k_grouped_wgrad"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path (the kernel runs on one "
+              "GPU's share of the work); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    log(f"device {torch.cuda.get_device_name(0)}, building workload {args.workload}")
+    builders = {"dense": build_dense, "small": lambda: build_dense(small=True),
+                "contiguous": build_contiguous, "masked": build_masked,
+                "wgrad": build_wgrad, "k_grouped_wgrad": lambda: build_wgrad(kgrouped=True)}
+    calls, config = builders[args.workload]()
+    log(f"{len(calls)} GEMMs per step; timing {args.steps} steps after {args.warmup} warmup")
+    total_ms, per_ms = time_steps(calls, args.steps, args.warmup)
+    ms_per_step = total_ms / args.steps
+    step_flops = sum(c.flops for c in calls)
+
+    shapes = []
+    for c, ms in zip(calls, per_ms):
+        tf = c.flops / (ms * 1e-3) / 1e12
+        gbs = c.bytes / (ms * 1e-3) / 1e9
+        frac = tf / PEAK_FP8_TFLOPS if c.bound == "mfma" else gbs / PEAK_HBM_GBS
+        shapes.append({"name": c.name, "us": round(ms * 1e3, 2), "tflops": round(tf, 1),
+                       "gbs": round(gbs, 1), "bound": c.bound, "frac": round(frac, 4)})
+        log(f"{c.name:52s} {ms * 1e3:9.1f} us {tf:8.1f} TFLOP/s {gbs:8.1f} GB/s {c.bound} {frac:.3f}")
+    dom = int(np.argmax(per_ms))
+    dc, dms = calls[dom], per_ms[dom]
+    if dc.bound == "mfma":
+        achieved, peak, unit = dc.flops / (dms * 1e-3) / 1e12, PEAK_FP8_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = dc.bytes / (dms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
+    roofline = {"bound": dc.bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": None, "kernel": dc.name,
+                "flops_per_launch": dc.flops, "bytes_per_launch": dc.bytes, "avg_us": round(dms * 1e3, 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(calls, args.cpu_seconds)
+
+    line = {"metric": METRIC, "value": round(step_flops / (ms_per_step * 1e-3) / 1e12, 2),
+            "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "fp8", "data": "synthetic (seeded N(0,1), e4m3-quantised)",
+            "config": config, "roofline": roofline, "cpu_baseline": cpu, "per_shape": shapes}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
