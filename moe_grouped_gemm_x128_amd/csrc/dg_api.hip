@@ -37,11 +37,13 @@ int device_cus(int* out) {
   return 0;
 }
 
-// Workgroups per CU an instance can keep resident: LDS-limited (160 KB per CU).
-int occupancy(const dg::TileShape& s) {
-  const int lds = 2 * (s.bm + s.bn) * 128 + 2 * 4 * (s.bm + s.bn) + 4 * s.bm + 64;
-  int occ = (160 * 1024) / lds;
-  if (occ > 2) occ = 2;  // register file: two 4-wave workgroups per CU
+// Workgroups per CU an instance can keep resident: LDS-limited (160 KB per
+// CU), at most two 4-wave or one 8-wave workgroup (register file).
+int occupancy(int kind, const dg::TileShape& s) {
+  const int lds = dg::lds_bytes_of(kind, s);
+  int occ = lds > 0 ? (160 * 1024) / lds : 1;
+  const int cap = dg::threads_of(s) >= 512 ? 1 : 2;
+  if (occ > cap) occ = cap;
   return occ < 1 ? 1 : occ;
 }
 
@@ -54,30 +56,52 @@ bool parse_forced(dg::TileShape* s) {
   return true;
 }
 
+struct Candidate {
+  dg::TileShape s;
+  double eff;  // relative matrix-unit efficiency of the tile shape
+};
+
 // Per-shape tile choice (DeepGEMM pages: block sizes and wave counts are
 // selected per shape; small M underuses the matrix units).  `rows` is the
 // output rows per group, `groups` the number of groups whose tiles share the
 // launch (masked: an upper bound from M_max).
+//   * few rows (<= 128 per group): narrow column tiles, the widest that still
+//     gives every CU a workgroup, because such shapes stream B from HBM;
+//   * otherwise: minimise (full waves of tiles over the CUs) x (tile area /
+//     tile efficiency), so a large tile wins unless it leaves CUs idle.
 dg::TileShape heuristic(int kind, int rows, int n, int k, int groups, int num_cus) {
   (void)k;
-  const dg::TileShape big{128, 128, 2, 2};
-  const dg::TileShape mid{128, 64, 2, 2};
-  const dg::TileShape small_m{64, 128, 1, 4};
-  const dg::TileShape small_mn{64, 64, 1, 4};
-  const dg::TileShape tiny{64, 32, 2, 2};
-  if (kind == DG_KIND_MASKED || rows <= 64) {
-    // few rows: narrow column tiles so enough workgroups stream B
-    const int per_group_m = ceil_div(rows, 64);
-    const dg::TileShape cands[3] = {small_m, small_mn, tiny};
+  if (rows <= 128) {
+    const int bm = rows <= 64 ? 64 : 128;
+    const dg::TileShape cands[4] = {{bm, 128, bm / 64 == 1 ? 1 : 2, bm / 64 == 1 ? 4 : 2},
+                                    {bm, 64, bm / 64 == 1 ? 1 : 2, bm / 64 == 1 ? 4 : 2},
+                                    {64, 32, 2, 2},
+                                    {64, 32, 2, 2}};
     for (const auto& c : cands) {
-      const long tiles = (long)groups * per_group_m * ceil_div(n, c.bn);
-      if (tiles >= num_cus) return c;
+      const long tiles = (long)groups * ceil_div(rows, c.bm) * ceil_div(n, c.bn);
+      if (tiles >= num_cus && dg::has_instance(kind, c)) return c;
     }
-    return tiny;
+    return dg::TileShape{64, 32, 2, 2};
   }
-  const long tiles_big = (long)groups * ceil_div(rows, 128) * ceil_div(n, 128);
-  if (tiles_big >= num_cus) return big;
-  return mid;
+  static const Candidate cands[] = {
+      {{256, 256, 2, 4}, 1.00}, {{256, 128, 2, 2}, 0.95}, {{128, 128, 2, 2}, 0.80},
+      {{128, 64, 2, 2}, 0.60},  {{64, 128, 1, 4}, 0.60},  {{64, 64, 1, 4}, 0.45},
+  };
+  double best = 1e300;
+  dg::TileShape pick{128, 128, 2, 2};
+  for (const auto& c : cands) {
+    if (kind == DG_KIND_CONTIGUOUS && 128 % c.s.bm != 0) continue;
+    if (!dg::has_instance(kind, c.s)) continue;
+    const long tiles = (long)groups * ceil_div(rows, c.s.bm) * ceil_div(n, c.s.bn);
+    const long slots = (long)num_cus * occupancy(kind, c.s);
+    const long waves = (tiles + slots - 1) / slots;
+    const double cost = (double)waves * c.s.bm * c.s.bn / (c.eff * occupancy(kind, c.s));
+    if (cost < best * 0.999) {
+      best = cost;
+      pick = c.s;
+    }
+  }
+  return pick;
 }
 
 struct Launch {
@@ -95,7 +119,7 @@ dg_status plan(int kind, int rows, int n, int k, int groups, int num_cus, dg::Pa
   const long tiles = (long)groups * p.tiles_m * p.tiles_n;
   if (tiles > 0x7fffffffL) return DG_ERROR_UNSUPPORTED;
   p.tiles = (int)tiles;
-  const long slots = (long)num_cus * occupancy(s);
+  const long slots = (long)num_cus * occupancy(kind, s);
   long grid = tiles < slots ? tiles : slots;
   if (grid > 8) grid -= grid % 8;  // keep workgroup -> XCD round robin aligned
   if (grid < 1) grid = 1;

@@ -49,4 +49,9 @@ hipError_t launch(int kind, const TileShape& shape, const Params& p, int grid,
 // True if an instance exists for (kind, shape).
 bool has_instance(int kind, const TileShape& shape);
 
+// Threads per workgroup (64 per wave) and LDS bytes per workgroup of an
+// instance; 0 if there is none.
+int threads_of(const TileShape& shape);
+int lds_bytes_of(int kind, const TileShape& shape);
+
 }  // namespace dg

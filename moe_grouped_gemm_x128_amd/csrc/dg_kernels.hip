@@ -4,15 +4,21 @@
 // a single core GEMM kernel); the layouts differ only in how a tile id maps
 // to (group, rows, columns, K range) and in the epilogue.
 //
-// Per workgroup tile (BM x BN outputs, 4 waves of 64 lanes):
-//   * operands go HBM -> registers -> LDS, 128-wide K block at a time, double
-//     buffered: the next block's global loads are in flight while the current
-//     block is multiplied;
+// Per workgroup tile (BM x BN outputs, WM x WN waves of 64 lanes):
+//   * operands and their scales move HBM -> LDS with the gfx950 LDS-DMA loads
+//     (global_load_lds_dwordx4 / _dword): no staging registers, and the loads
+//     for the next S-1 K blocks stay in flight while the current one is
+//     multiplied (an S-stage ring, one barrier per 128-wide K block).  The
+//     DMA writes each wave's 1 KB piece contiguously, so the XOR bank swizzle
+//     is applied on the global side: the lane that lands on LDS chunk c of row
+//     r fetches logical chunk c ^ swz(r);
 //   * each 16x16 output subtile of a K block is one v_mfma_f32_16x16x128_f8f6f4
 //     with a zero accumulator: the exact fp32 block partial (DeepGEMM pages,
 //     "主要特点": tensor-core FP8 accumulation alone is imprecise);
 //   * the partial is promoted into the fp32 main accumulator with one VALU
-//     FMA by sa[m,kb]*sb[n/128,kb] (the pages' two-level accumulation);
+//     FMA by sa[m,kb]*sb[n/128,kb] (the pages' two-level accumulation); the
+//     promotion of one fragment group is placed after the MFMAs of the next,
+//     so the vector unit works while the matrix unit is busy;
 //   * the epilogue rounds to bf16 (or adds into fp32 D) with row/column masks.
 //
 // The MFMA is fed B rows as its first operand and A rows as its second, so a
@@ -30,13 +36,12 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
 constexpr int kBK = 128;      // K block = scale granularity
 constexpr int kGroupM = 8;    // tile rows per raster group
 
-// LDS row = 128 bytes = 8 chunks of 16 bytes.  Chunk c of row r is stored at
-// chunk position c ^ swz(r).  A wave's 16-lane phase of ds_read_b128 reads one
-// chunk from each of 16 consecutive rows; this swizzle spreads them over all
+// LDS row = 128 bytes = 8 chunks of 16 bytes; logical chunk c of row r sits
+// at chunk position c ^ swz(r).  A 16-lane phase of ds_read_b128 reads one
+// chunk from each of 16 consecutive rows; the swizzle spreads them over all
 // banks for both a 32-bank (8 rows per phase) and a 64-bank (16 rows) view.
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
@@ -45,16 +50,45 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
-struct TileInfo {
-  int g;          // group (expert)
-  int m0, n0;     // first row (within the group) and column
-  int rows;       // valid rows from m0 (<= BM)
-  int kb0, kb1;   // K block range
-  int64_t a_row0; // absolute LHS row of m0
-  int64_t out_row0;  // absolute output row of m0
-};
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
 
-template <int BM>
+__device__ __forceinline__ const uint8_t* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const uint8_t*)(((uint64_t)hi << 32) | lo);
+}
+
+// LDS DMA.  Lane i's bytes go to LDS address m0 + i*size.  Issued through
+// inline asm so the compiler's wait-count pass does not treat every later
+// LDS read as dependent on every in-flight DMA; the waits are explicit below.
+// Nothing else in these kernels uses m0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(uint32_t lds, const uint8_t* sbase, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(uint32_t lds, const uint8_t* sbase, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+               :: "s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier that also orders LDS accesses for the compiler.
+__device__ __forceinline__ void barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ void raster(int L, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int group = kGroupM * tiles_n;
   const int gid = L / group;
@@ -65,8 +99,23 @@ __device__ __forceinline__ void raster(int L, int tiles_m, int tiles_n, int& tm,
   tn = r / gm;
 }
 
-template <int BM, int BN, int WM, int WN, int KIND>
-__global__ __launch_bounds__(kThreads) void fp8_gemm_kernel(const Params p) {
+__device__ __forceinline__ v8i load_frag(const uint8_t* tile, int row, int lq) {
+  const uint8_t* base = tile + row * kBK;
+  const uint4 lo = *reinterpret_cast<const uint4*>(base + (((2 * lq) ^ swz(row)) << 4));
+  const uint4 hi = *reinterpret_cast<const uint4*>(base + (((2 * lq + 1) ^ swz(row)) << 4));
+  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+__device__ __forceinline__ v4f mfma_block(const v8i& b_rows, const v8i& a_rows) {
+  // D[n][m] = sum over the 128 k of the block; both operands use the same
+  // (lane, byte) -> k assignment, so the sum covers exactly the block.
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b_rows, a_rows, v4f{0.f, 0.f, 0.f, 0.f},
+                                                          0, 0, 0, 0, 0, 0);
+}
+
+template <int BM, int BN, int WM, int WN, int S, int KIND>
+__global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) {
+  constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM;   // wave tile rows
   constexpr int WTN = BN / WN;   // wave tile columns
   constexpr int FM = WTM / 16;   // 16-row fragments per wave
@@ -75,49 +124,58 @@ __global__ __launch_bounds__(kThreads) void fp8_gemm_kernel(const Params p) {
   constexpr bool kFp32Out = kRowScaleB;
   // the columns of one wave tile sit inside one 128-block: one sb per wave
   constexpr bool kWaveUniformSb = !kRowScaleB && (kBK % WTN == 0) && (BN % WTN == 0);
-  static_assert(WM * WN == 4, "4 waves per workgroup");
+  constexpr bool kStreamM = FM >= FN;  // keep the smaller fragment set resident
   static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile is a multiple of 16");
-  constexpr int A_CH = BM * 8;  // 16-byte chunks per stage
-  constexpr int B_CH = BN * 8;
-  constexpr int A_PT = (A_CH + kThreads - 1) / kThreads;
-  constexpr int B_PT = (B_CH + kThreads - 1) / kThreads;
+  static_assert(S >= 2, "at least double buffering");
 
-  __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * kBK];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * kBK];
-  __shared__ float sSA[2][BM];
-  __shared__ float sSB[2][BN];
+  // ---- LDS stage layout and DMA pieces ----
+  constexpr int SA_N = ((BM + 63) / 64) * 64;                   // floats
+  constexpr int SB_N = kRowScaleB ? ((BN + 63) / 64) * 64 : 64;  // floats
+  constexpr int OFF_A = 0;
+  constexpr int OFF_B = BM * kBK;
+  constexpr int OFF_SA = OFF_B + BN * kBK;
+  constexpr int OFF_SB = OFF_SA + SA_N * 4;
+  constexpr int STAGE = OFF_SB + SB_N * 4;
+  constexpr int PA = BM / 8, PB = BN / 8, PSA = SA_N / 64, PSB = SB_N / 64;  // pieces
+  constexpr int P = PA + PB + PSA + PSB;
+  constexpr int DMAX = (P + NW - 1) / NW;  // pieces per wave (some waves one fewer)
+  constexpr int DMIN = P / NW;
+  static_assert(BM % 8 == 0 && BN % 8 == 0, "1 KB DMA pieces");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
   __shared__ int sRowOk[KIND == KIND_CONTIGUOUS ? BM : 1];
   __shared__ int sExpert;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN;
   const int wn = wave % WN;
   const int l16 = lane & 15;
   const int lq = lane >> 4;
+  const uint32_t smem_lds = lds_addr(smem);
 
   // ---- tile count (masked: from masked_m on the device, no host sync) ----
   int T = p.tiles;
   if constexpr (KIND == KIND_MASKED) {
     T = 0;
     for (int g = 0; g < p.groups; ++g) {
-      int v = min(max(p.ctrl[g], 0), p.m);
+      const int v = min(max(p.ctrl[g], 0), p.m);
       T += ((v + BM - 1) / BM) * p.tiles_n;
     }
   }
   const int per_xcd = (T + 7) >> 3;
+  const int nb_rows = (p.n + kBK - 1) / kBK;
 
   for (int t = blockIdx.x; t < per_xcd * 8; t += gridDim.x) {
     const int L = (t & 7) * per_xcd + (t >> 3);
     if (L >= T) continue;
 
     // ---- decode tile ----
-    TileInfo ti;
-    ti.kb0 = 0;
-    ti.kb1 = p.kbs;
+    int g = 0, m0, n0, rows, kb0 = 0, kb1 = p.kbs;
+    int64_t a_row0, out_row0;
     if constexpr (KIND == KIND_MASKED) {
-      int rem = L, g = 0, mt = 0, v = 0;
+      int rem = L, mt = 0, v = 0;
       for (; g < p.groups; ++g) {
         v = min(max(p.ctrl[g], 0), p.m);
         mt = (v + BM - 1) / BM;
@@ -126,125 +184,101 @@ __global__ __launch_bounds__(kThreads) void fp8_gemm_kernel(const Params p) {
         rem -= cnt;
       }
       if (g >= p.groups) continue;  // unreachable for L < T
-      ti.g = g;
-      ti.m0 = (rem % mt) * BM;   // m fastest: tiles sharing a B tile run together
-      ti.n0 = (rem / mt) * BN;
-      ti.rows = min(BM, v - ti.m0);
-      ti.a_row0 = (int64_t)g * p.m + ti.m0;
-      ti.out_row0 = ti.a_row0;
+      m0 = (rem % mt) * BM;        // m fastest: tiles sharing a B tile run together
+      n0 = (rem / mt) * BN;
+      rows = min(BM, v - m0);
+      a_row0 = (int64_t)g * p.m + m0;
+      out_row0 = a_row0;
     } else if constexpr (KIND == KIND_KGROUPED) {
       const int per_g = p.tiles_m * p.tiles_n;
-      const int g = L / per_g;
+      g = L / per_g;
       int tm, tn;
-      raster<BM>(L - g * per_g, p.tiles_m, p.tiles_n, tm, tn);
-      ti.g = g;
-      ti.m0 = tm * BM;
-      ti.n0 = tn * BN;
-      ti.rows = min(BM, p.m - ti.m0);
-      ti.kb0 = p.kb_begin[g];
-      ti.kb1 = p.kb_begin[g + 1];
-      ti.a_row0 = ti.m0;
-      ti.out_row0 = (int64_t)g * p.m + ti.m0;
+      raster(L - g * per_g, p.tiles_m, p.tiles_n, tm, tn);
+      m0 = tm * BM;
+      n0 = tn * BN;
+      rows = min(BM, p.m - m0);
+      kb0 = p.kb_begin[g];
+      kb1 = p.kb_begin[g + 1];
+      a_row0 = m0;
+      out_row0 = (int64_t)g * p.m + m0;
     } else {
       int tm, tn;
-      raster<BM>(L, p.tiles_m, p.tiles_n, tm, tn);
-      ti.g = 0;
-      ti.m0 = tm * BM;
-      ti.n0 = tn * BN;
-      ti.rows = min(BM, p.m - ti.m0);
-      ti.a_row0 = ti.m0;
-      ti.out_row0 = ti.m0;
+      raster(L, p.tiles_m, p.tiles_n, tm, tn);
+      m0 = tm * BM;
+      n0 = tn * BN;
+      rows = min(BM, p.m - m0);
+      a_row0 = m0;
+      out_row0 = m0;
     }
-    if (ti.kb0 >= ti.kb1) continue;  // empty K range: D unchanged
+    const int nkb = kb1 - kb0;
+    if (nkb <= 0) continue;  // empty K range: D unchanged
 
     if constexpr (KIND == KIND_CONTIGUOUS) {
       // expert of this 128-aligned row block: the (single) valid id in it
-      __syncthreads();  // previous tile's epilogue is done with sRowOk
+      barrier();  // previous tile's epilogue is done with sRowOk
       if (tid == 0) sExpert = -1;
-      __syncthreads();
-      for (int r = tid; r < BM; r += kThreads) {
-        const int id = p.ctrl[ti.m0 + r];
+      barrier();
+      for (int r = tid; r < BM; r += NW * 64) {
+        const int id = p.ctrl[m0 + r];
         if (id >= 0 && id < p.groups) atomicMax(&sExpert, id);
       }
-      __syncthreads();
+      barrier();
       const int e = sExpert;
-      for (int r = tid; r < BM; r += kThreads) sRowOk[r] = (p.ctrl[ti.m0 + r] == e);
+      for (int r = tid; r < BM; r += NW * 64) sRowOk[r] = (p.ctrl[m0 + r] == e);
       if (e < 0) continue;  // block-uniform: all padding
-      ti.g = e;
+      g = e;
     }
 
-    const uint8_t* gA = p.a + ti.a_row0 * (int64_t)p.lda;
-    const float* gSA = p.sa + ti.a_row0 * (int64_t)p.kbs;
+    // ---- per-tile DMA addressing ----
     // K-grouped weight gradients share one B [N,T]; the group picks the K range
-    const int bg = (KIND == KIND_KGROUPED) ? 0 : ti.g;
-    const uint8_t* gB = p.b + ((int64_t)bg * p.n + ti.n0) * (int64_t)p.lda;
-    const int nb_rows = (p.n + kBK - 1) / kBK;
-    const int a_last = max(ti.rows, 1) - 1;     // clamp rows beyond the valid ones
-    const int b_last = min(BN, p.n - ti.n0) - 1;
-
-    uint4 ra[A_PT], rb[B_PT];
-    float rsa[(BM + kThreads - 1) / kThreads], rsb[(BN + kThreads - 1) / kThreads];
-
-    auto load_stage = [&](int kb) {
+    const int bg = (KIND == KIND_KGROUPED) ? 0 : g;
+    const uint8_t* gA = uniform_ptr(p.a + a_row0 * (int64_t)p.lda);
+    const uint8_t* gB = uniform_ptr(p.b + ((int64_t)bg * p.n + n0) * (int64_t)p.lda);
+    const uint8_t* gSA = uniform_ptr(p.sa + a_row0 * (int64_t)p.kbs);
+    const uint8_t* gSB = kRowScaleB ? uniform_ptr(p.sb + (int64_t)n0 * p.kbs)
+                                    : uniform_ptr(p.sb + (int64_t)g * nb_rows * p.kbs);
+    const int a_last = max(rows, 1) - 1;       // rows past the valid ones re-read the last
+    const int b_last = min(BN, p.n - n0) - 1;
+    uint32_t voff[DMAX];
 #pragma unroll
-      for (int q = 0; q < A_PT; ++q) {
-        const int c = tid + q * kThreads;
-        if (A_CH % kThreads == 0 || c < A_CH) {
-          const int row = min(c >> 3, a_last);
-          ra[q] = *reinterpret_cast<const uint4*>(gA + (int64_t)row * p.lda + kb * kBK + (c & 7) * 16);
+    for (int q = 0; q < DMAX; ++q) {
+      const int pc = wave + NW * q;
+      uint32_t v = 0;
+      if (pc < PA) {
+        const int r = pc * 8 + (lane >> 3);
+        v = (uint32_t)min(r, a_last) * p.lda + (((lane & 7) ^ swz(r)) << 4);
+      } else if (pc < PA + PB) {
+        const int r = (pc - PA) * 8 + (lane >> 3);
+        v = (uint32_t)min(r, b_last) * p.lda + (((lane & 7) ^ swz(r)) << 4);
+      } else if (pc < PA + PB + PSA) {
+        const int r = (pc - PA - PB) * 64 + lane;
+        v = (uint32_t)min(r, a_last) * p.kbs * 4;
+      } else if (pc < P) {
+        if constexpr (kRowScaleB) {
+          const int c = (pc - PA - PB - PSA) * 64 + lane;
+          v = (uint32_t)min(c, b_last) * p.kbs * 4;
+        } else {
+          const int nb = min(n0 / kBK + lane, nb_rows - 1);
+          v = (uint32_t)nb * p.kbs * 4;
         }
       }
+      voff[q] = v;
+    }
+    // this wave's DMAs for K block kb0 + rel into ring stage `st`
+    auto issue = [&](int rel, int st) {
+      const int kb = kb0 + rel;
+      const uint32_t base = smem_lds + st * STAGE;
 #pragma unroll
-      for (int q = 0; q < B_PT; ++q) {
-        const int c = tid + q * kThreads;
-        if (B_CH % kThreads == 0 || c < B_CH) {
-          const int row = min(c >> 3, b_last);
-          rb[q] = *reinterpret_cast<const uint4*>(gB + (int64_t)row * p.lda + kb * kBK + (c & 7) * 16);
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < (BM + kThreads - 1) / kThreads; ++q) {
-        const int r = tid + q * kThreads;
-        if (r < BM) rsa[q] = gSA[(int64_t)min(r, a_last) * p.kbs + kb];
-      }
-#pragma unroll
-      for (int q = 0; q < (BN + kThreads - 1) / kThreads; ++q) {
-        const int c = tid + q * kThreads;
-        if (c < BN) {
-          const int n = ti.n0 + min(c, b_last);
-          if constexpr (kRowScaleB)
-            rsb[q] = p.sb[(int64_t)n * p.kbs + kb];
-          else
-            rsb[q] = p.sb[((int64_t)ti.g * nb_rows + n / kBK) * p.kbs + kb];
-        }
-      }
-    };
-    auto store_stage = [&](int buf) {
-#pragma unroll
-      for (int q = 0; q < A_PT; ++q) {
-        const int c = tid + q * kThreads;
-        if (A_CH % kThreads == 0 || c < A_CH) {
-          const int row = c >> 3;
-          *reinterpret_cast<uint4*>(&sA[buf][row * kBK + (((c & 7) ^ swz(row)) << 4)]) = ra[q];
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < B_PT; ++q) {
-        const int c = tid + q * kThreads;
-        if (B_CH % kThreads == 0 || c < B_CH) {
-          const int row = c >> 3;
-          *reinterpret_cast<uint4*>(&sB[buf][row * kBK + (((c & 7) ^ swz(row)) << 4)]) = rb[q];
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < (BM + kThreads - 1) / kThreads; ++q) {
-        const int r = tid + q * kThreads;
-        if (r < BM) sSA[buf][r] = rsa[q];
-      }
-#pragma unroll
-      for (int q = 0; q < (BN + kThreads - 1) / kThreads; ++q) {
-        const int c = tid + q * kThreads;
-        if (c < BN) sSB[buf][c] = rsb[q];
+      for (int q = 0; q < DMAX; ++q) {
+        const int pc = wave + NW * q;
+        if (pc < PA)
+          dma16(base + OFF_A + pc * 1024, gA + kb * kBK, voff[q]);
+        else if (pc < PA + PB)
+          dma16(base + OFF_B + (pc - PA) * 1024, gB + kb * kBK, voff[q]);
+        else if (pc < PA + PB + PSA)
+          dma4(base + OFF_SA + (pc - PA - PB) * 256, gSA + kb * 4, voff[q]);
+        else if (pc < P)
+          dma4(base + OFF_SB + (pc - PA - PB - PSA) * 256, gSB + kb * 4, voff[q]);
       }
     };
 
@@ -254,87 +288,107 @@ __global__ __launch_bounds__(kThreads) void fp8_gemm_kernel(const Params p) {
 #pragma unroll
       for (int j = 0; j < FM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    load_stage(ti.kb0);
-    store_stage(0);
-    __syncthreads();
-
-    for (int kb = ti.kb0; kb < ti.kb1; ++kb) {
-      const int cur = (kb - ti.kb0) & 1;
-      const bool more = kb + 1 < ti.kb1;
-      if (more) load_stage(kb + 1);
-
-      // fragments: lane (l16, lq) takes row l16 of a 16-row slice and the
-      // 32 bytes [32*lq, 32*lq+32) of the K block.  Both operands use the
-      // same (lane, byte) -> k assignment, so the MFMA sums exactly the 128
-      // products of the block.
-      v8i bfr[FN], afr[FM];
+    // prologue: the first S-1 K blocks in flight
 #pragma unroll
-      for (int i = 0; i < FN; ++i) {
-        const int row = wn * WTN + 16 * i + l16;
-        const uint8_t* base = &sB[cur][row * kBK];
-        const uint4 lo = *reinterpret_cast<const uint4*>(base + (((2 * lq) ^ swz(row)) << 4));
-        const uint4 hi = *reinterpret_cast<const uint4*>(base + (((2 * lq + 1) ^ swz(row)) << 4));
-        bfr[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    for (int s = 0; s < S - 1; ++s)
+      if (s < nkb) issue(s, s);
+
+    for (int rel = 0; rel < nkb; ++rel) {
+      const int st = rel % S;
+      // this wave's DMAs for block `rel` are done once at most
+      // (blocks issued after it) x DMIN of its operations remain in flight
+      const int later = min(S - 2, nkb - 1 - rel);
+      if constexpr (S == 2) {
+        wait_vm<0>();
+      } else if constexpr (S == 3) {
+        if (later >= 1) wait_vm<DMIN>(); else wait_vm<0>();
+      } else {
+        static_assert(S == 4, "ring depth 2..4");
+        if (later >= 2) wait_vm<2 * DMIN>(); else if (later == 1) wait_vm<DMIN>(); else wait_vm<0>();
       }
-#pragma unroll
-      for (int j = 0; j < FM; ++j) {
-        const int row = wm * WTM + 16 * j + l16;
-        const uint8_t* base = &sA[cur][row * kBK];
-        const uint4 lo = *reinterpret_cast<const uint4*>(base + (((2 * lq) ^ swz(row)) << 4));
-        const uint4 hi = *reinterpret_cast<const uint4*>(base + (((2 * lq + 1) ^ swz(row)) << 4));
-        afr[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      }
+      barrier();  // every wave's block `rel` landed; every wave is done with rel-1
+      if (rel + S - 1 < nkb) issue(rel + S - 1, (rel + S - 1) % S);
+
+      const uint8_t* sA = smem + st * STAGE + OFF_A;
+      const uint8_t* sB = smem + st * STAGE + OFF_B;
+      const float* sSA = reinterpret_cast<const float*>(smem + st * STAGE + OFF_SA);
+      const float* sSB = reinterpret_cast<const float*>(smem + st * STAGE + OFF_SB);
+
       float sav[FM];
 #pragma unroll
-      for (int j = 0; j < FM; ++j) sav[j] = sSA[cur][wm * WTM + 16 * j + l16];
-
-      if constexpr (kWaveUniformSb) {
-        const float sbw = sSB[cur][wn * WTN];
-        float s[FM];
-#pragma unroll
-        for (int j = 0; j < FM; ++j) s[j] = sav[j] * sbw;
+      for (int j = 0; j < FM; ++j) sav[j] = sSA[wm * WTM + 16 * j + l16];
+      // per n-fragment B scale (block scales) or per column quad (row scales)
+      float sbv[FN];
+      v4f sbq[kRowScaleB ? FN : 1];
+      if constexpr (kRowScaleB) {
 #pragma unroll
         for (int i = 0; i < FN; ++i)
+          sbq[i] = *reinterpret_cast<const v4f*>(&sSB[wn * WTN + 16 * i + 4 * lq]);
+      } else if constexpr (kWaveUniformSb) {
+        const float s = sSB[(n0 + wn * WTN) / kBK - n0 / kBK];
 #pragma unroll
-          for (int j = 0; j < FM; ++j) {
-            const v4f pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                bfr[i], afr[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(s[j], pr[r], acc[i][j][r]);
-          }
-      } else if constexpr (!kRowScaleB) {
-#pragma unroll
-        for (int i = 0; i < FN; ++i) {
-          const float sbi = sSB[cur][wn * WTN + 16 * i];
-#pragma unroll
-          for (int j = 0; j < FM; ++j) {
-            const v4f pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                bfr[i], afr[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-            const float s = sav[j] * sbi;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(s, pr[r], acc[i][j][r]);
-          }
-        }
+        for (int i = 0; i < FN; ++i) sbv[i] = s;
       } else {
 #pragma unroll
-        for (int i = 0; i < FN; ++i) {
-          float sbr[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sbr[r] = sSB[cur][wn * WTN + 16 * i + 4 * lq + r];
-#pragma unroll
-          for (int j = 0; j < FM; ++j) {
-            const v4f pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                bfr[i], afr[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              acc[i][j][r] = __builtin_fmaf(sav[j] * sbr[r], pr[r], acc[i][j][r]);
-          }
-        }
+        for (int i = 0; i < FN; ++i) sbv[i] = sSB[(n0 + wn * WTN + 16 * i) / kBK - n0 / kBK];
       }
 
-      if (more) store_stage(cur ^ 1);
-      __syncthreads();
+      auto promote = [&](int i, int j, const v4f& pr) {
+        if constexpr (kRowScaleB) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(sav[j] * sbq[i][r], pr[r], acc[i][j][r]);
+        } else {
+          const float s = sav[j] * sbv[i];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(s, pr[r], acc[i][j][r]);
+        }
+      };
+
+      if constexpr (kStreamM) {
+        // resident: the FN column fragments; streamed: the FM row fragments
+        v8i bres[FN];
+#pragma unroll
+        for (int i = 0; i < FN; ++i) bres[i] = load_frag(sB, wn * WTN + 16 * i + l16, lq);
+        v8i acur = load_frag(sA, wm * WTM + l16, lq);
+        v4f part[2][FN];
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+          v8i anext = acur;
+          if (j + 1 < FM) anext = load_frag(sA, wm * WTM + 16 * (j + 1) + l16, lq);
+#pragma unroll
+          for (int i = 0; i < FN; ++i) part[j & 1][i] = mfma_block(bres[i], acur);
+          if (j > 0) {
+#pragma unroll
+            for (int i = 0; i < FN; ++i) promote(i, j - 1, part[(j - 1) & 1][i]);
+          }
+          acur = anext;
+        }
+#pragma unroll
+        for (int i = 0; i < FN; ++i) promote(i, FM - 1, part[(FM - 1) & 1][i]);
+      } else {
+        // resident: the FM row fragments; streamed: the FN column fragments
+        v8i ares[FM];
+#pragma unroll
+        for (int j = 0; j < FM; ++j) ares[j] = load_frag(sA, wm * WTM + 16 * j + l16, lq);
+        v8i bcur = load_frag(sB, wn * WTN + l16, lq);
+        v4f part[2][FM];
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+          v8i bnext = bcur;
+          if (i + 1 < FN) bnext = load_frag(sB, wn * WTN + 16 * (i + 1) + l16, lq);
+#pragma unroll
+          for (int j = 0; j < FM; ++j) part[i & 1][j] = mfma_block(bcur, ares[j]);
+          if (i > 0) {
+#pragma unroll
+            for (int j = 0; j < FM; ++j) promote(i - 1, j, part[(i - 1) & 1][j]);
+          }
+          bcur = bnext;
+        }
+#pragma unroll
+        for (int j = 0; j < FM; ++j) promote(FN - 1, j, part[(FN - 1) & 1][j]);
+      }
     }
+    barrier();  // all waves are done with the ring before the next tile refills it
 
     // ---- epilogue ----
 #pragma unroll
@@ -344,12 +398,12 @@ __global__ __launch_bounds__(kThreads) void fp8_gemm_kernel(const Params p) {
       if constexpr (KIND == KIND_CONTIGUOUS)
         row_ok = sRowOk[ml] != 0;
       else
-        row_ok = ml < ti.rows;
+        row_ok = ml < rows;
       if (!row_ok) continue;
-      const int64_t orow = ti.out_row0 + ml;
+      const int64_t orow = out_row0 + ml;
 #pragma unroll
       for (int i = 0; i < FN; ++i) {
-        const int n = ti.n0 + wn * WTN + 16 * i + 4 * lq;
+        const int n = n0 + wn * WTN + 16 * i + 4 * lq;
         if (n >= p.n) continue;
         if constexpr (kFp32Out) {
           float* d = static_cast<float*>(p.out) + orow * p.n + n;
@@ -382,24 +436,24 @@ __global__ __launch_bounds__(kThreads) void fp8_gemm_kernel(const Params p) {
   }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int S>
 hipError_t launch_shape(int kind, const Params& p, int grid, hipStream_t stream) {
-  dim3 g(grid), b(kThreads);
+  dim3 g(grid), b(WM * WN * 64);
   switch (kind) {
     case KIND_DENSE:
-      hipLaunchKernelGGL((fp8_gemm_kernel<BM, BN, WM, WN, KIND_DENSE>), g, b, 0, stream, p);
+      hipLaunchKernelGGL((fp8_gemm_kernel<BM, BN, WM, WN, S, KIND_DENSE>), g, b, 0, stream, p);
       break;
     case KIND_CONTIGUOUS:
-      hipLaunchKernelGGL((fp8_gemm_kernel<BM, BN, WM, WN, KIND_CONTIGUOUS>), g, b, 0, stream, p);
+      hipLaunchKernelGGL((fp8_gemm_kernel<BM, BN, WM, WN, S, KIND_CONTIGUOUS>), g, b, 0, stream, p);
       break;
     case KIND_MASKED:
-      hipLaunchKernelGGL((fp8_gemm_kernel<BM, BN, WM, WN, KIND_MASKED>), g, b, 0, stream, p);
+      hipLaunchKernelGGL((fp8_gemm_kernel<BM, BN, WM, WN, S, KIND_MASKED>), g, b, 0, stream, p);
       break;
     case KIND_WGRAD:
-      hipLaunchKernelGGL((fp8_gemm_kernel<BM, BN, WM, WN, KIND_WGRAD>), g, b, 0, stream, p);
+      hipLaunchKernelGGL((fp8_gemm_kernel<BM, BN, WM, WN, S, KIND_WGRAD>), g, b, 0, stream, p);
       break;
     case KIND_KGROUPED:
-      hipLaunchKernelGGL((fp8_gemm_kernel<BM, BN, WM, WN, KIND_KGROUPED>), g, b, 0, stream, p);
+      hipLaunchKernelGGL((fp8_gemm_kernel<BM, BN, WM, WN, S, KIND_KGROUPED>), g, b, 0, stream, p);
       break;
     default:
       return hipErrorInvalidValue;
@@ -407,27 +461,44 @@ hipError_t launch_shape(int kind, const Params& p, int grid, hipStream_t stream)
   return hipGetLastError();
 }
 
-#define DG_SHAPES(X) \
-  X(128, 128, 2, 2)  \
-  X(128, 64, 2, 2)   \
-  X(64, 128, 1, 4)   \
-  X(64, 64, 1, 4)    \
-  X(64, 32, 2, 2)
+// (BM, BN, waves along M, waves along N, LDS ring stages)
+#define DG_SHAPES(X)      \
+  X(256, 128, 2, 2, 3)    \
+  X(256, 256, 2, 4, 2)    \
+  X(128, 128, 2, 2, 4)    \
+  X(128, 64, 2, 2, 4)     \
+  X(64, 128, 1, 4, 4)     \
+  X(64, 64, 1, 4, 4)      \
+  X(64, 32, 2, 2, 4)
 
 }  // namespace
 
 bool has_instance(int kind, const TileShape& s) {
   if (kind < KIND_DENSE || kind > KIND_KGROUPED) return false;
-#define X(BM, BN, WM, WN) \
+#define X(BM, BN, WM, WN, S) \
   if (s.bm == BM && s.bn == BN && s.wm == WM && s.wn == WN) return true;
   DG_SHAPES(X)
 #undef X
   return false;
 }
 
+int threads_of(const TileShape& s) { return s.wm * s.wn * 64; }
+
+int lds_bytes_of(int kind, const TileShape& s) {
+  const bool row_sb = (kind == KIND_WGRAD || kind == KIND_KGROUPED);
+  const int sa_n = ((s.bm + 63) / 64) * 64;
+  const int sb_n = row_sb ? ((s.bn + 63) / 64) * 64 : 64;
+  const int stage = (s.bm + s.bn) * kBK + 4 * (sa_n + sb_n);
+#define X(BM, BN, WM, WN, S) \
+  if (s.bm == BM && s.bn == BN && s.wm == WM && s.wn == WN) return S * stage + 4 * BM + 64;
+  DG_SHAPES(X)
+#undef X
+  return 0;
+}
+
 hipError_t launch(int kind, const TileShape& s, const Params& p, int grid, hipStream_t stream) {
-#define X(BM, BN, WM, WN) \
-  if (s.bm == BM && s.bn == BN && s.wm == WM && s.wn == WN) return launch_shape<BM, BN, WM, WN>(kind, p, grid, stream);
+#define X(BM, BN, WM, WN, S) \
+  if (s.bm == BM && s.bn == BN && s.wm == WM && s.wn == WN) return launch_shape<BM, BN, WM, WN, S>(kind, p, grid, stream);
   DG_SHAPES(X)
 #undef X
   return hipErrorInvalidValue;

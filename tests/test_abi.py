@@ -137,7 +137,7 @@ SHAPES += [(1, 32768, 4096, 7168, 4), (1, 65536, 7168, 2048, 8), (2, 256, 4096, 
 @pytest.mark.parametrize("kind,m,n,k,g", SHAPES)
 def test_heuristic_invariants(lib, kind, m, n, k, g):
     c = _cfg(lib, kind, m, n, k, g)
-    assert c["waves_m"] * c["waves_n"] == 4
+    assert c["waves_m"] * c["waves_n"] in (4, 8)
     assert c["block_m"] % (16 * c["waves_m"]) == 0 and c["block_n"] % (16 * c["waves_n"]) == 0
     groups = g if kind in (2, 4) else 1
     tiles = groups * -(-m // c["block_m"]) * -(-n // c["block_n"])
