@@ -54,28 +54,41 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
 }
 
-__device__ __forceinline__ const uint8_t* uniform_ptr(const void* p) {
-  const uint64_t v = (uint64_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (const uint8_t*)(((uint64_t)hi << 32) | lo);
+// LDS DMA through buffer loads.  Lane i's bytes go to LDS address m0 +
+// i*size; the address is rsrc.base + voffset + soffset, and bytes at or past
+// rsrc.num_records (range-checked on the per-lane offset) read as zero, so
+// rows and columns past the tile's valid ones need no clamping.  Issued
+// through inline asm so the compiler's wait-count pass does not treat every
+// later LDS read as dependent on every in-flight DMA; the waits are explicit
+// below.  Nothing else in these kernels uses m0.
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource: 48-bit base, stride 0, byte range, 32-bit data format.
+__device__ __forceinline__ v4i buffer_rsrc(const void* base, uint32_t num_bytes) {
+  const uint64_t b = (uint64_t)base;
+  return v4i{(int)__builtin_amdgcn_readfirstlane((uint32_t)b),
+             (int)(__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) & 0xffffu),
+             (int)__builtin_amdgcn_readfirstlane(num_bytes), 0x00020000};
 }
 
-// LDS DMA.  Lane i's bytes go to LDS address m0 + i*size.  Issued through
-// inline asm so the compiler's wait-count pass does not treat every later
-// LDS read as dependent on every in-flight DMA; the waits are explicit below.
-// Nothing else in these kernels uses m0.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(uint32_t lds, const uint8_t* sbase, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :: "s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
+__device__ __forceinline__ void dma16(uint32_t lds, v4i rsrc, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
 }
-__device__ __forceinline__ void dma4(uint32_t lds, const uint8_t* sbase, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
-               :: "s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
+__device__ __forceinline__ void dma4(uint32_t lds, v4i rsrc, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
 }
 #pragma clang diagnostic pop
+
+// An opaque copy: keeps the compiler from hoisting (and keeping live) values
+// that are cheaper to recompute next to their use.
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
 
 // Wait until at most N vector-memory operations of this wave are in flight.
 template <int N>
@@ -99,11 +112,13 @@ __device__ __forceinline__ void raster(int L, int tiles_m, int tiles_n, int& tm,
   tn = r / gm;
 }
 
-__device__ __forceinline__ v8i load_frag(const uint8_t* tile, int row, int lq) {
-  const uint8_t* base = tile + row * kBK;
-  const uint4 lo = *reinterpret_cast<const uint4*>(base + (((2 * lq) ^ swz(row)) << 4));
-  const uint4 hi = *reinterpret_cast<const uint4*>(base + (((2 * lq + 1) ^ swz(row)) << 4));
-  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+// A lane reads two 16-byte chunks of row (16f + l16) of a 16-row fragment f.
+// Fragments start on multiples of 16 rows, so the swizzle of the row is
+// swz(l16) and the lane's two in-fragment offsets are fixed: `lo` and `hi`.
+__device__ __forceinline__ v8i load_frag(const uint8_t* frag_base, uint32_t lo, uint32_t hi) {
+  const uint4 a = *reinterpret_cast<const uint4*>(frag_base + lo);
+  const uint4 b = *reinterpret_cast<const uint4*>(frag_base + hi);
+  return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
 }
 
 __device__ __forceinline__ v4f mfma_block(const v8i& b_rows, const v8i& a_rows) {
@@ -136,13 +151,18 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   constexpr int OFF_SA = OFF_B + BN * kBK;
   constexpr int OFF_SB = OFF_SA + SA_N * 4;
   constexpr int STAGE = OFF_SB + SB_N * 4;
-  constexpr int PA = BM / 8, PB = BN / 8, PSA = SA_N / 64, PSB = SB_N / 64;  // pieces
-  constexpr int P = PA + PB + PSA + PSB;
-  constexpr int DMAX = (P + NW - 1) / NW;  // pieces per wave (some waves one fewer)
-  constexpr int DMIN = P / NW;
-  static_assert(BM % 8 == 0 && BN % 8 == 0, "1 KB DMA pieces");
+  // DMA pieces per stage: 1 KB operand pieces (8 LDS rows) and 256 B scale
+  // pieces.  Wave w issues operand pieces w, w+NW, ... (the same count on
+  // every wave) and scale pieces w, w+NW, ... (some waves one fewer).
+  constexpr int PA = BM / 8, PB = BN / 8, PSA = SA_N / 64, PSB = SB_N / 64;
+  constexpr int PS = PSA + PSB;
+  constexpr int QA = PA / NW, QB = PB / NW, QS = (PS + NW - 1) / NW;
+  // every wave issues QA + QB + QS DMAs per stage: scale pieces past PS are
+  // padding that reads nothing and lands in a sink slot after the ring
+  constexpr int DMIN = QA + QB + QS;
+  static_assert(PA % NW == 0 && PB % NW == 0, "operand pieces split evenly over the waves");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE + 256];  // + padding-DMA sink
   __shared__ int sRowOk[KIND == KIND_CONTIGUOUS ? BM : 1];
   __shared__ int sExpert;
 
@@ -154,6 +174,8 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   const int l16 = lane & 15;
   const int lq = lane >> 4;
   const uint32_t smem_lds = lds_addr(smem);
+  const uint32_t frag_lo = l16 * kBK + (((2 * lq) ^ swz(l16)) << 4);
+  const uint32_t frag_hi = l16 * kBK + (((2 * lq + 1) ^ swz(l16)) << 4);
 
   // ---- tile count (masked: from masked_m on the device, no host sync) ----
   int T = p.tiles;
@@ -232,53 +254,53 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     // ---- per-tile DMA addressing ----
     // K-grouped weight gradients share one B [N,T]; the group picks the K range
     const int bg = (KIND == KIND_KGROUPED) ? 0 : g;
-    const uint8_t* gA = uniform_ptr(p.a + a_row0 * (int64_t)p.lda);
-    const uint8_t* gB = uniform_ptr(p.b + ((int64_t)bg * p.n + n0) * (int64_t)p.lda);
-    const uint8_t* gSA = uniform_ptr(p.sa + a_row0 * (int64_t)p.kbs);
-    const uint8_t* gSB = kRowScaleB ? uniform_ptr(p.sb + (int64_t)n0 * p.kbs)
-                                    : uniform_ptr(p.sb + (int64_t)g * nb_rows * p.kbs);
-    const int a_last = max(rows, 1) - 1;       // rows past the valid ones re-read the last
-    const int b_last = min(BN, p.n - n0) - 1;
-    uint32_t voff[DMAX];
-#pragma unroll
-    for (int q = 0; q < DMAX; ++q) {
-      const int pc = wave + NW * q;
-      uint32_t v = 0;
-      if (pc < PA) {
-        const int r = pc * 8 + (lane >> 3);
-        v = (uint32_t)min(r, a_last) * p.lda + (((lane & 7) ^ swz(r)) << 4);
-      } else if (pc < PA + PB) {
-        const int r = (pc - PA) * 8 + (lane >> 3);
-        v = (uint32_t)min(r, b_last) * p.lda + (((lane & 7) ^ swz(r)) << 4);
-      } else if (pc < PA + PB + PSA) {
-        const int r = (pc - PA - PB) * 64 + lane;
-        v = (uint32_t)min(r, a_last) * p.kbs * 4;
-      } else if (pc < P) {
-        if constexpr (kRowScaleB) {
-          const int c = (pc - PA - PB - PSA) * 64 + lane;
-          v = (uint32_t)min(c, b_last) * p.kbs * 4;
-        } else {
-          const int nb = min(n0 / kBK + lane, nb_rows - 1);
-          v = (uint32_t)nb * p.kbs * 4;
-        }
-      }
-      voff[q] = v;
-    }
-    // this wave's DMAs for K block kb0 + rel into ring stage `st`
-    auto issue = [&](int rel, int st) {
+    const int bcols = min(BN, p.n - n0);  // valid B rows (output columns) of the tile
+    const v4i rsA = buffer_rsrc(p.a + a_row0 * (int64_t)p.lda, (uint32_t)rows * p.lda);
+    const v4i rsB = buffer_rsrc(p.b + ((int64_t)bg * p.n + n0) * (int64_t)p.lda, (uint32_t)bcols * p.lda);
+    const v4i rsSA = buffer_rsrc(p.sa + a_row0 * (int64_t)p.kbs, (uint32_t)rows * p.kbs * 4);
+    const v4i rsSB = kRowScaleB
+        ? buffer_rsrc(p.sb + (int64_t)n0 * p.kbs, (uint32_t)bcols * p.kbs * 4)
+        : buffer_rsrc(p.sb + ((int64_t)g * nb_rows + n0 / kBK) * p.kbs,
+                      (uint32_t)(nb_rows - n0 / kBK) * p.kbs * 4);
+    // Lane l of operand piece q lands on LDS row 8*(wave + NW*q) + l/8, chunk
+    // l%8.  Row steps between a wave's pieces are multiples of 16, so the
+    // swizzle term is fixed per lane; only the row step changes with q.
+    const int r0 = wave * 8 + (lane >> 3);
+    const uint32_t voff0 = (uint32_t)r0 * p.lda + (((lane & 7) ^ swz(r0)) << 4);
+    const uint32_t step = (uint32_t)(NW * 8) * p.lda;  // bytes between a wave's pieces
+    // scale pieces: 64 rows (or columns / 128-blocks) each, one float per lane
+    const uint32_t svoff = (uint32_t)lane * p.kbs * 4;
+    const uint32_t sstep = 64u * p.kbs * 4;
+
+    const v4i rsNull = buffer_rsrc(p.a, 0);  // every byte out of range: reads zeros, no traffic
+    // this wave's DMAs for K block kb0 + rel into ring stage `st`; only the
+    // pieces with index in [lo, hi) (A pieces first, then B, then scales), so
+    // a block's DMAs can be spread over the fragment groups of the previous
+    // block instead of stalling every wave at the same point.  Branch-free: a
+    // block past the tile's K range reads nothing (null resource) into a
+    // stage no later block of the tile uses.
+    constexpr int ND = QA + QB + QS;
+    auto issue = [&](int rel, int st, int lo, int hi) {
+      const bool live = rel < nkb;
       const int kb = kb0 + rel;
       const uint32_t base = smem_lds + st * STAGE;
+      const uint32_t soff = __builtin_amdgcn_readfirstlane(kb * kBK);
+      const uint32_t ssoff = __builtin_amdgcn_readfirstlane(kb * 4);
+      const v4i ra = live ? rsA : rsNull, rb = live ? rsB : rsNull;
 #pragma unroll
-      for (int q = 0; q < DMAX; ++q) {
-        const int pc = wave + NW * q;
-        if (pc < PA)
-          dma16(base + OFF_A + pc * 1024, gA + kb * kBK, voff[q]);
-        else if (pc < PA + PB)
-          dma16(base + OFF_B + (pc - PA) * 1024, gB + kb * kBK, voff[q]);
-        else if (pc < PA + PB + PSA)
-          dma4(base + OFF_SA + (pc - PA - PB) * 256, gSA + kb * 4, voff[q]);
-        else if (pc < P)
-          dma4(base + OFF_SB + (pc - PA - PB - PSA) * 256, gSB + kb * 4, voff[q]);
+      for (int q = 0; q < QA; ++q)
+        if (q >= lo && q < hi) dma16(base + OFF_A + (wave + NW * q) * 1024, ra, voff0 + q * step, soff);
+#pragma unroll
+      for (int q = 0; q < QB; ++q)
+        if (QA + q >= lo && QA + q < hi) dma16(base + OFF_B + (wave + NW * q) * 1024, rb, voff0 + q * step, soff);
+#pragma unroll
+      for (int q = 0; q < QS; ++q) {
+        if (QA + QB + q < lo || QA + QB + q >= hi) continue;
+        const int sp = wave + NW * q;  // scale piece: sa rows 64*sp.., then sb
+        const bool is_a = sp < PSA, real = sp < PS && live;
+        const v4i rs = !real ? rsNull : (is_a ? rsSA : rsSB);
+        const uint32_t lds = sp < PS ? base + OFF_SA + sp * 256 : smem_lds + S * STAGE;
+        dma4(lds, rs, svoff + (uint32_t)(is_a ? sp : sp - PSA) * sstep, ssoff);
       }
     };
 
@@ -288,11 +310,45 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
 #pragma unroll
       for (int j = 0; j < FM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
+    // Fragments: NR resident ones are read once per K block, NO streamed
+    // ones one at a time.  MFMA M(o, r) multiplies streamed fragment o by
+    // resident fragment r into part[r]; its promotion F(o, r) (one FMA per
+    // element by sa*sb) is issued NR-1 MFMAs later, in the rotation
+    //   M(o,0) F(o-1,1) M(o,1) F(o-1,2) ... M(o,NR-1) F(o,0) M(o+1,0) ...
+    // so every FMA finds its partial ready and every MFMA finds its part
+    // register already consumed.  The rotation runs on across K blocks: the
+    // last group's F(NO-1, 1..NR-1) follow the next block's first MFMAs.
+    constexpr int NO = kStreamM ? FM : FN;
+    constexpr int NR = kStreamM ? FN : FM;
+    // zero partials and scales make the carried-over promotions of the first
+    // K block exact no-ops (fma(0, 0, acc) == acc), so they need no branch
+    v4f part[NR];
+    float pend[NR];  // scales of the group still being promoted
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      part[r] = v4f{0.f, 0.f, 0.f, 0.f};
+      pend[r] = 0.f;
+    }
+    auto acc_at = [&](int o, int r) -> v4f& { return kStreamM ? acc[r][o] : acc[o][r]; };
+    auto fma4 = [&](v4f& a, float s, const v4f& pr) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] = __builtin_fmaf(s, pr[e], a[e]);
+    };
+    // row-scaled B (weight gradients): the scale differs per output column
+    v4f pendq[kRowScaleB ? NR : 1];
+#pragma unroll
+    for (int r = 0; r < (kRowScaleB ? NR : 1); ++r) pendq[r] = v4f{0.f, 0.f, 0.f, 0.f};
+    auto fma4q = [&](v4f& a, float s, const v4f& q, const v4f& pr) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] = __builtin_fmaf(s * q[e], pr[e], a[e]);
+    };
+
     // prologue: the first S-1 K blocks in flight
 #pragma unroll
     for (int s = 0; s < S - 1; ++s)
-      if (s < nkb) issue(s, s);
+      if (s < nkb) issue(s, s, 0, ND);
 
+#pragma unroll 1
     for (int rel = 0; rel < nkb; ++rel) {
       const int st = rel % S;
       // this wave's DMAs for block `rel` are done once at most
@@ -307,17 +363,25 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
         if (later >= 2) wait_vm<2 * DMIN>(); else if (later == 1) wait_vm<DMIN>(); else wait_vm<0>();
       }
       barrier();  // every wave's block `rel` landed; every wave is done with rel-1
-      if (rel + S - 1 < nkb) issue(rel + S - 1, (rel + S - 1) % S);
 
       const uint8_t* sA = smem + st * STAGE + OFF_A;
       const uint8_t* sB = smem + st * STAGE + OFF_B;
       const float* sSA = reinterpret_cast<const float*>(smem + st * STAGE + OFF_SA);
       const float* sSB = reinterpret_cast<const float*>(smem + st * STAGE + OFF_SB);
+      const uint8_t* wA = sA + wm * WTM * kBK;  // this wave's first A row
+      const uint8_t* wB = sB + wn * WTN * kBK;  // this wave's first B row
+      auto frag_a = [&](int j) { return load_frag(wA + j * 16 * kBK, frag_lo, frag_hi); };
+      auto frag_b = [&](int i) { return load_frag(wB + i * 16 * kBK, frag_lo, frag_hi); };
+      auto load_s = [&](int o) -> v8i { return kStreamM ? frag_a(o) : frag_b(o); };  // streamed fragment o
+      v8i res[NR];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) res[r] = kStreamM ? frag_b(r) : frag_a(r);
+      v8i cur = load_s(0);
 
       float sav[FM];
 #pragma unroll
       for (int j = 0; j < FM; ++j) sav[j] = sSA[wm * WTM + 16 * j + l16];
-      // per n-fragment B scale (block scales) or per column quad (row scales)
+      // B scale per n-fragment (block scales) or per column quad (row scales)
       float sbv[FN];
       v4f sbq[kRowScaleB ? FN : 1];
       if constexpr (kRowScaleB) {
@@ -325,70 +389,75 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
         for (int i = 0; i < FN; ++i)
           sbq[i] = *reinterpret_cast<const v4f*>(&sSB[wn * WTN + 16 * i + 4 * lq]);
       } else if constexpr (kWaveUniformSb) {
-        const float s = sSB[(n0 + wn * WTN) / kBK - n0 / kBK];
+        const float sb = sSB[(n0 + wn * WTN) / kBK - n0 / kBK];
 #pragma unroll
-        for (int i = 0; i < FN; ++i) sbv[i] = s;
+        for (int i = 0; i < FN; ++i) sbv[i] = sb;
       } else {
 #pragma unroll
         for (int i = 0; i < FN; ++i) sbv[i] = sSB[(n0 + wn * WTN + 16 * i) / kBK - n0 / kBK];
       }
-
-      auto promote = [&](int i, int j, const v4f& pr) {
-        if constexpr (kRowScaleB) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(sav[j] * sbq[i][r], pr[r], acc[i][j][r]);
-        } else {
-          const float s = sav[j] * sbv[i];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(s, pr[r], acc[i][j][r]);
-        }
+      // F(o, r) of this block
+      auto promote = [&](int o, int r) {
+        const int j = kStreamM ? o : r, i = kStreamM ? r : o;
+        if constexpr (kRowScaleB)
+          fma4q(acc[i][j], sav[j], sbq[i], part[r]);
+        else
+          fma4(acc[i][j], sav[j] * sbv[i], part[r]);
+      };
+      // F(NO-1, r) of the previous block
+      auto promote_pending = [&](int r) {
+        if constexpr (kRowScaleB)
+          fma4q(acc_at(NO - 1, r), pend[r], pendq[r], part[r]);
+        else
+          fma4(acc_at(NO - 1, r), pend[r], part[r]);
       };
 
-      if constexpr (kStreamM) {
-        // resident: the FN column fragments; streamed: the FM row fragments
-        v8i bres[FN];
 #pragma unroll
-        for (int i = 0; i < FN; ++i) bres[i] = load_frag(sB, wn * WTN + 16 * i + l16, lq);
-        v8i acur = load_frag(sA, wm * WTM + l16, lq);
-        v4f part[2][FN];
+      for (int o = 0; o < NO; ++o) {
+        v8i nxt = cur;
+        if (o + 1 < NO) nxt = load_s(o + 1);
 #pragma unroll
-        for (int j = 0; j < FM; ++j) {
-          v8i anext = acur;
-          if (j + 1 < FM) anext = load_frag(sA, wm * WTM + 16 * (j + 1) + l16, lq);
-#pragma unroll
-          for (int i = 0; i < FN; ++i) part[j & 1][i] = mfma_block(bres[i], acur);
-          if (j > 0) {
-#pragma unroll
-            for (int i = 0; i < FN; ++i) promote(i, j - 1, part[(j - 1) & 1][i]);
+        for (int r = 0; r < NR; ++r) {
+          part[r] = kStreamM ? mfma_block(res[r], cur) : mfma_block(cur, res[r]);
+          if (r + 1 < NR) {
+            if (o > 0)
+              promote(o - 1, r + 1);
+            else
+              promote_pending(r + 1);
           }
-          acur = anext;
         }
+        // this group's share of the next block's DMAs (spread over the first
+        // half of the groups so they still land in time)
+        constexpr int kSpread = NO / 2 > 0 ? NO / 2 : 1;
+        if (o < kSpread)
+          issue(rel + S - 1, (rel + S - 1) % S, (o * ND) / kSpread, ((o + 1) * ND) / kSpread);
+        promote(o, 0);
+        cur = nxt;
+        // keep each group's loads, MFMAs and FMAs together: no fragment
+        // reads hoisted further ahead (register pressure)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // the rest of the last group is promoted during the next block
 #pragma unroll
-        for (int i = 0; i < FN; ++i) promote(i, FM - 1, part[(FM - 1) & 1][i]);
-      } else {
-        // resident: the FM row fragments; streamed: the FN column fragments
-        v8i ares[FM];
-#pragma unroll
-        for (int j = 0; j < FM; ++j) ares[j] = load_frag(sA, wm * WTM + 16 * j + l16, lq);
-        v8i bcur = load_frag(sB, wn * WTN + l16, lq);
-        v4f part[2][FM];
-#pragma unroll
-        for (int i = 0; i < FN; ++i) {
-          v8i bnext = bcur;
-          if (i + 1 < FN) bnext = load_frag(sB, wn * WTN + 16 * (i + 1) + l16, lq);
-#pragma unroll
-          for (int j = 0; j < FM; ++j) part[i & 1][j] = mfma_block(bcur, ares[j]);
-          if (i > 0) {
-#pragma unroll
-            for (int j = 0; j < FM; ++j) promote(i - 1, j, part[(i - 1) & 1][j]);
-          }
-          bcur = bnext;
+      for (int r = 0; r < NR; ++r) {
+        const int j = kStreamM ? NO - 1 : r, i = kStreamM ? r : NO - 1;
+        if constexpr (kRowScaleB) {
+          pend[r] = sav[j];
+          pendq[r] = sbq[i];
+        } else {
+          pend[r] = sav[j] * sbv[i];
         }
-#pragma unroll
-        for (int j = 0; j < FM; ++j) promote(FN - 1, j, part[(FN - 1) & 1][j]);
       }
     }
-    barrier();  // all waves are done with the ring before the next tile refills it
+#pragma unroll
+    for (int r = 1; r < NR; ++r) {
+      if constexpr (kRowScaleB)
+        fma4q(acc_at(NO - 1, r), pend[r], pendq[r], part[r]);
+      else
+        fma4(acc_at(NO - 1, r), pend[r], part[r]);
+    }
+    wait_vm<0>();  // padding DMAs of the last blocks have landed
+    barrier();     // all waves are done with the ring before the next tile refills it
 
     // ---- epilogue ----
 #pragma unroll
