@@ -67,11 +67,12 @@ struct Candidate {
 // launch (masked: an upper bound from M_max).
 //   * few rows (<= 128 per group): narrow column tiles, the widest that still
 //     gives every CU a workgroup, because such shapes stream B from HBM;
-//   * otherwise: minimise (full waves of tiles over the CUs) x (tile area /
-//     tile efficiency), so a large tile wins unless it leaves CUs idle.
+//   * otherwise: minimise (full waves of tiles over the CUs) x (workgroups
+//     per CU) x (tile area / tile efficiency), so a large tile wins unless
+//     it leaves CUs idle.
 dg::TileShape heuristic(int kind, int rows, int n, int k, int groups, int num_cus) {
   (void)k;
-  if (rows <= 128) {
+  if (rows <= 128 || kind == DG_KIND_MASKED) {
     const int bm = rows <= 64 ? 64 : 128;
     const dg::TileShape cands[4] = {{bm, 128, bm / 64 == 1 ? 1 : 2, bm / 64 == 1 ? 4 : 2},
                                     {bm, 64, bm / 64 == 1 ? 1 : 2, bm / 64 == 1 ? 4 : 2},
@@ -84,8 +85,9 @@ dg::TileShape heuristic(int kind, int rows, int n, int k, int groups, int num_cu
     return dg::TileShape{64, 32, 2, 2};
   }
   static const Candidate cands[] = {
-      {{256, 256, 2, 4}, 1.00}, {{256, 128, 2, 2}, 0.95}, {{128, 128, 2, 2}, 0.80},
-      {{128, 64, 2, 2}, 0.60},  {{64, 128, 1, 4}, 0.60},  {{64, 64, 1, 4}, 0.45},
+      // efficiencies measured relative to the 256x256 tile on full waves
+      {{256, 256, 2, 4}, 1.00}, {{256, 128, 2, 2}, 0.85}, {{128, 128, 2, 2}, 0.70},
+      {{128, 64, 2, 2}, 0.50},  {{64, 128, 1, 4}, 0.50},  {{64, 64, 1, 4}, 0.35},
   };
   double best = 1e300;
   dg::TileShape pick{128, 128, 2, 2};
@@ -95,7 +97,9 @@ dg::TileShape heuristic(int kind, int rows, int n, int k, int groups, int num_cu
     const long tiles = (long)groups * ceil_div(rows, c.s.bm) * ceil_div(n, c.s.bn);
     const long slots = (long)num_cus * occupancy(kind, c.s);
     const long waves = (tiles + slots - 1) / slots;
-    const double cost = (double)waves * c.s.bm * c.s.bn / (c.eff * occupancy(kind, c.s));
+    // occ workgroups share a CU, so each full wave of tiles takes occ times a
+    // tile's own time
+    const double cost = (double)waves * occupancy(kind, c.s) * c.s.bm * c.s.bn / c.eff;
     if (cost < best * 0.999) {
       best = cost;
       pick = c.s;
