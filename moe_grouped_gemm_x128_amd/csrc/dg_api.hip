@@ -65,6 +65,7 @@ struct Candidate {
 // selected per shape; small M underuses the matrix units).  `rows` is the
 // output rows per group, `groups` the number of groups whose tiles share the
 // launch (masked: an upper bound from M_max).
+//   * masked layout with enough groups: tall 256-row tiles (B read once);
 //   * few rows (<= 128 per group): narrow column tiles, the widest that still
 //     gives every CU a workgroup, because such shapes stream B from HBM;
 //   * otherwise: minimise (full waves of tiles over the CUs) x (workgroups
@@ -72,6 +73,13 @@ struct Candidate {
 //     it leaves CUs idle.
 dg::TileShape heuristic(int kind, int rows, int n, int k, int groups, int num_cus) {
   (void)k;
+  if (kind == DG_KIND_MASKED && rows <= 256) {
+    // one tall tile per (group, column block) covers every row of the group,
+    // so B is streamed once; its waves skip the row quarters past masked_m
+    const dg::TileShape tall256{256, 256, 1, 8}, tall128{256, 128, 1, 4};
+    if ((long)groups * ceil_div(n, 256) * 4 >= 3L * num_cus) return tall256;
+    if ((long)groups * ceil_div(n, 128) * 4 >= 3L * num_cus) return tall128;
+  }
   if (rows <= 128 || kind == DG_KIND_MASKED) {
     const int bm = rows <= 64 ? 64 : 128;
     const dg::TileShape cands[4] = {{bm, 128, bm / 64 == 1 ? 1 : 2, bm / 64 == 1 ? 4 : 2},

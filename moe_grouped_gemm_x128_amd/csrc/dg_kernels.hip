@@ -28,6 +28,8 @@
 // Tiles are walked by a persistent grid.  Workgroup w runs on XCD w % 8;
 // the walk hands each XCD a contiguous range of tile ids so tiles that share
 // A rows or B columns meet in the same L2.
+#include <type_traits>
+
 #include "dg_kernel.h"
 
 namespace dg {
@@ -140,6 +142,11 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   // the columns of one wave tile sit inside one 128-block: one sb per wave
   constexpr bool kWaveUniformSb = !kRowScaleB && (kBK % WTN == 0) && (BN % WTN == 0);
   constexpr bool kStreamM = FM >= FN;  // keep the smaller fragment set resident
+  // Masked layout with tall tiles: a wave whose rows run past the group's
+  // valid rows skips those row fragments (no LDS read, no MFMA; their zero
+  // partials keep the promotion rotation unchanged), so one tile can cover
+  // every row of a group and B is streamed once per group.
+  constexpr bool kSkipRows = (KIND == KIND_MASKED) && kStreamM && (FM > 4) && (FM % 4 == 0) && (FM <= 16);
   static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile is a multiple of 16");
   static_assert(S >= 2, "at least double buffering");
 
@@ -343,118 +350,138 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
       for (int e = 0; e < 4; ++e) a[e] = __builtin_fmaf(s * q[e], pr[e], a[e]);
     };
 
-    // prologue: the first S-1 K blocks in flight
-#pragma unroll
-    for (int s = 0; s < S - 1; ++s)
-      if (s < nkb) issue(s, s, 0, ND);
+    // The K loop for NOV live streamed fragments per wave (NOV == NO except
+    // for the masked layout, whose waves skip the row quarters past the
+    // group's valid rows; the rotation then ends at fragment NOV-1).
+    auto k_loop = [&](auto nov_c) {
+    constexpr int NOV = decltype(nov_c)::value;
+      // prologue: the first S-1 K blocks in flight
+  #pragma unroll
+      for (int s = 0; s < S - 1; ++s)
+        if (s < nkb) issue(s, s, 0, ND);
 
-#pragma unroll 1
-    for (int rel = 0; rel < nkb; ++rel) {
-      const int st = rel % S;
-      // this wave's DMAs for block `rel` are done once at most
-      // (blocks issued after it) x DMIN of its operations remain in flight
-      const int later = min(S - 2, nkb - 1 - rel);
-      if constexpr (S == 2) {
-        wait_vm<0>();
-      } else if constexpr (S == 3) {
-        if (later >= 1) wait_vm<DMIN>(); else wait_vm<0>();
-      } else {
-        static_assert(S == 4, "ring depth 2..4");
-        if (later >= 2) wait_vm<2 * DMIN>(); else if (later == 1) wait_vm<DMIN>(); else wait_vm<0>();
-      }
-      barrier();  // every wave's block `rel` landed; every wave is done with rel-1
+  #pragma unroll 1
+      for (int rel = 0; rel < nkb; ++rel) {
+        const int st = rel % S;
+        // this wave's DMAs for block `rel` are done once at most
+        // (blocks issued after it) x DMIN of its operations remain in flight
+        const int later = min(S - 2, nkb - 1 - rel);
+        if constexpr (S == 2) {
+          wait_vm<0>();
+        } else if constexpr (S == 3) {
+          if (later >= 1) wait_vm<DMIN>(); else wait_vm<0>();
+        } else {
+          static_assert(S == 4, "ring depth 2..4");
+          if (later >= 2) wait_vm<2 * DMIN>(); else if (later == 1) wait_vm<DMIN>(); else wait_vm<0>();
+        }
+        barrier();  // every wave's block `rel` landed; every wave is done with rel-1
 
-      const uint8_t* sA = smem + st * STAGE + OFF_A;
-      const uint8_t* sB = smem + st * STAGE + OFF_B;
-      const float* sSA = reinterpret_cast<const float*>(smem + st * STAGE + OFF_SA);
-      const float* sSB = reinterpret_cast<const float*>(smem + st * STAGE + OFF_SB);
-      const uint8_t* wA = sA + wm * WTM * kBK;  // this wave's first A row
-      const uint8_t* wB = sB + wn * WTN * kBK;  // this wave's first B row
-      auto frag_a = [&](int j) { return load_frag(wA + j * 16 * kBK, frag_lo, frag_hi); };
-      auto frag_b = [&](int i) { return load_frag(wB + i * 16 * kBK, frag_lo, frag_hi); };
-      auto load_s = [&](int o) -> v8i { return kStreamM ? frag_a(o) : frag_b(o); };  // streamed fragment o
-      v8i res[NR];
-#pragma unroll
-      for (int r = 0; r < NR; ++r) res[r] = kStreamM ? frag_b(r) : frag_a(r);
-      v8i cur = load_s(0);
+        const uint8_t* sA = smem + st * STAGE + OFF_A;
+        const uint8_t* sB = smem + st * STAGE + OFF_B;
+        const float* sSA = reinterpret_cast<const float*>(smem + st * STAGE + OFF_SA);
+        const float* sSB = reinterpret_cast<const float*>(smem + st * STAGE + OFF_SB);
+        const uint8_t* wA = sA + wm * WTM * kBK;  // this wave's first A row
+        const uint8_t* wB = sB + wn * WTN * kBK;  // this wave's first B row
+        auto frag_a = [&](int j) { return load_frag(wA + j * 16 * kBK, frag_lo, frag_hi); };
+        auto frag_b = [&](int i) { return load_frag(wB + i * 16 * kBK, frag_lo, frag_hi); };
+        auto load_s = [&](int o) -> v8i { return kStreamM ? frag_a(o) : frag_b(o); };  // streamed fragment o
+        v8i res[NR];
+  #pragma unroll
+        for (int r = 0; r < NR; ++r)
+          res[r] = NOV > 0 ? (kStreamM ? frag_b(r) : frag_a(r)) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+        v8i cur = NOV > 0 ? load_s(0) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
 
-      float sav[FM];
-#pragma unroll
-      for (int j = 0; j < FM; ++j) sav[j] = sSA[wm * WTM + 16 * j + l16];
-      // B scale per n-fragment (block scales) or per column quad (row scales)
-      float sbv[FN];
-      v4f sbq[kRowScaleB ? FN : 1];
-      if constexpr (kRowScaleB) {
-#pragma unroll
-        for (int i = 0; i < FN; ++i)
-          sbq[i] = *reinterpret_cast<const v4f*>(&sSB[wn * WTN + 16 * i + 4 * lq]);
-      } else if constexpr (kWaveUniformSb) {
-        const float sb = sSB[(n0 + wn * WTN) / kBK - n0 / kBK];
-#pragma unroll
-        for (int i = 0; i < FN; ++i) sbv[i] = sb;
-      } else {
-#pragma unroll
-        for (int i = 0; i < FN; ++i) sbv[i] = sSB[(n0 + wn * WTN + 16 * i) / kBK - n0 / kBK];
-      }
-      // F(o, r) of this block
-      auto promote = [&](int o, int r) {
-        const int j = kStreamM ? o : r, i = kStreamM ? r : o;
-        if constexpr (kRowScaleB)
-          fma4q(acc[i][j], sav[j], sbq[i], part[r]);
-        else
-          fma4(acc[i][j], sav[j] * sbv[i], part[r]);
-      };
-      // F(NO-1, r) of the previous block
-      auto promote_pending = [&](int r) {
-        if constexpr (kRowScaleB)
-          fma4q(acc_at(NO - 1, r), pend[r], pendq[r], part[r]);
-        else
-          fma4(acc_at(NO - 1, r), pend[r], part[r]);
-      };
+        float sav[FM];
+  #pragma unroll
+        for (int j = 0; j < FM; ++j) sav[j] = sSA[wm * WTM + 16 * j + l16];
+        // B scale per n-fragment (block scales) or per column quad (row scales)
+        float sbv[FN];
+        v4f sbq[kRowScaleB ? FN : 1];
+        if constexpr (kRowScaleB) {
+  #pragma unroll
+          for (int i = 0; i < FN; ++i)
+            sbq[i] = *reinterpret_cast<const v4f*>(&sSB[wn * WTN + 16 * i + 4 * lq]);
+        } else if constexpr (kWaveUniformSb) {
+          const float sb = sSB[(n0 + wn * WTN) / kBK - n0 / kBK];
+  #pragma unroll
+          for (int i = 0; i < FN; ++i) sbv[i] = sb;
+        } else {
+  #pragma unroll
+          for (int i = 0; i < FN; ++i) sbv[i] = sSB[(n0 + wn * WTN + 16 * i) / kBK - n0 / kBK];
+        }
+        // F(o, r) of this block
+        auto promote = [&](int o, int r) {
+          const int j = kStreamM ? o : r, i = kStreamM ? r : o;
+          if constexpr (kRowScaleB)
+            fma4q(acc[i][j], sav[j], sbq[i], part[r]);
+          else
+            fma4(acc[i][j], sav[j] * sbv[i], part[r]);
+        };
+        // F(NOV-1, r) of the previous block
+        auto promote_pending = [&](int r) {
+          if constexpr (kRowScaleB)
+            fma4q(acc_at(NOV - 1, r), pend[r], pendq[r], part[r]);
+          else
+            fma4(acc_at(NOV - 1, r), pend[r], part[r]);
+        };
+        if constexpr (NOV == 0) issue(rel + S - 1, (rel + S - 1) % S, 0, ND);  // no groups to spread over
 
-#pragma unroll
-      for (int o = 0; o < NO; ++o) {
-        v8i nxt = cur;
-        if (o + 1 < NO) nxt = load_s(o + 1);
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          part[r] = kStreamM ? mfma_block(res[r], cur) : mfma_block(cur, res[r]);
-          if (r + 1 < NR) {
-            if (o > 0)
-              promote(o - 1, r + 1);
-            else
-              promote_pending(r + 1);
+  #pragma unroll
+        for (int o = 0; o < NOV; ++o) {
+          v8i nxt = cur;
+          if (o + 1 < NOV) nxt = load_s(o + 1);
+  #pragma unroll
+          for (int r = 0; r < NR; ++r) {
+            part[r] = kStreamM ? mfma_block(res[r], cur) : mfma_block(cur, res[r]);
+            if (r + 1 < NR) {
+              if (o > 0)
+                promote(o - 1, r + 1);
+              else
+                promote_pending(r + 1);
+            }
+          }
+          // this group's share of the next block's DMAs (spread over the first
+          // half of the groups so they still land in time)
+          constexpr int kSpread = NOV / 2 > 0 ? NOV / 2 : 1;
+          if (o < kSpread)
+            issue(rel + S - 1, (rel + S - 1) % S, (o * ND) / kSpread, ((o + 1) * ND) / kSpread);
+          promote(o, 0);
+          cur = nxt;
+          // keep each group's loads, MFMAs and FMAs together: no fragment
+          // reads hoisted further ahead (register pressure)
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // the rest of the last group is promoted during the next block
+  #pragma unroll
+        for (int r = 0; r < NR && NOV > 0; ++r) {
+          const int j = kStreamM ? NOV - 1 : r, i = kStreamM ? r : NOV - 1;
+          if constexpr (kRowScaleB) {
+            pend[r] = sav[j];
+            pendq[r] = sbq[i];
+          } else {
+            pend[r] = sav[j] * sbv[i];
           }
         }
-        // this group's share of the next block's DMAs (spread over the first
-        // half of the groups so they still land in time)
-        constexpr int kSpread = NO / 2 > 0 ? NO / 2 : 1;
-        if (o < kSpread)
-          issue(rel + S - 1, (rel + S - 1) % S, (o * ND) / kSpread, ((o + 1) * ND) / kSpread);
-        promote(o, 0);
-        cur = nxt;
-        // keep each group's loads, MFMAs and FMAs together: no fragment
-        // reads hoisted further ahead (register pressure)
-        __builtin_amdgcn_sched_barrier(0);
       }
-      // the rest of the last group is promoted during the next block
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        const int j = kStreamM ? NO - 1 : r, i = kStreamM ? r : NO - 1;
-        if constexpr (kRowScaleB) {
-          pend[r] = sav[j];
-          pendq[r] = sbq[i];
-        } else {
-          pend[r] = sav[j] * sbv[i];
-        }
+  #pragma unroll
+      for (int r = 1; r < NR && NOV > 0; ++r) {
+        if constexpr (kRowScaleB)
+          fma4q(acc_at(NOV - 1, r), pend[r], pendq[r], part[r]);
+        else
+          fma4(acc_at(NOV - 1, r), pend[r], part[r]);
       }
-    }
-#pragma unroll
-    for (int r = 1; r < NR; ++r) {
-      if constexpr (kRowScaleB)
-        fma4q(acc_at(NO - 1, r), pend[r], pendq[r], part[r]);
-      else
-        fma4(acc_at(NO - 1, r), pend[r], part[r]);
+    };
+    if constexpr (kSkipRows) {
+      const int quarters = min(NO / 4, max(0, (rows - wm * WTM + 63) / 64));
+      switch (quarters) {
+        case 0: k_loop(std::integral_constant<int, 0>{}); break;
+        case 1: k_loop(std::integral_constant<int, (NO >= 4 ? 4 : NO)>{}); break;
+        case 2: k_loop(std::integral_constant<int, (NO >= 8 ? 8 : NO)>{}); break;
+        case 3: k_loop(std::integral_constant<int, (NO >= 12 ? 12 : NO)>{}); break;
+        default: k_loop(std::integral_constant<int, NO>{}); break;
+      }
+    } else {
+      k_loop(std::integral_constant<int, NO>{});
     }
     wait_vm<0>();  // padding DMAs of the last blocks have landed
     barrier();     // all waves are done with the ring before the next tile refills it
@@ -532,6 +559,8 @@ hipError_t launch_shape(int kind, const Params& p, int grid, hipStream_t stream)
 
 // (BM, BN, waves along M, waves along N, LDS ring stages)
 #define DG_SHAPES(X)      \
+  X(256, 256, 1, 8, 2)    \
+  X(256, 128, 1, 4, 3)    \
   X(256, 128, 2, 2, 3)    \
   X(256, 256, 2, 4, 2)    \
   X(128, 128, 2, 2, 4)    \

@@ -102,7 +102,7 @@ def test_contiguous_small(dg, force_tile, tile):
     check_close(bits_to_f64(got[valid]), bits_to_f64(ref[valid]), "contiguous small")
 
 
-@pytest.mark.parametrize("tile", [None, "256x128x2x2", "128x128x2x2", "64x32x2x2"])
+@pytest.mark.parametrize("tile", [None, "256x256x1x8", "256x128x1x4", "256x128x2x2", "128x128x2x2", "64x32x2x2"])
 def test_masked_small(dg, force_tile, tile):
     g, m_max, n, k = 5, 96, 260, 256
     mm = np.array([0, 1, 96, 200, 50], np.int32)  # empty, one row, full, clamped, partial
@@ -157,3 +157,21 @@ def test_page_call_style(dg):
     torch.cuda.synchronize()
     ref, _ = oracle.gemm_fp8_nt(d.a, d.sa, d.b, d.sb)
     check_close(bits_to_f64(bf16_bits(out)), bits_to_f64(ref), "page-style dense")
+
+
+@pytest.mark.parametrize("tile", [None, "256x256x1x8", "256x128x1x4", "256x256x2x4"])
+def test_masked_row_quarters(dg, force_tile, tile):
+    """Tall masked tiles skip 64-row quarters past masked_m: every boundary."""
+    mm = np.array([0, 1, 63, 64, 65, 127, 128, 129, 191, 192, 193, 255, 256, 300], np.int32)
+    g, m_max, n, k = mm.size, 256, 136, 256
+    x = inputs.make_masked(g, m_max, n, k, seed=inputs.SEED_BASE + 31, masked_m=mm)
+    force_tile(tile)
+    out = sentinel_bf16((g, m_max, n))
+    say(f"masked quarters G={g} tile={tile}")
+    dg.dg_grouped_fp8_masked(dev(x.a), dev(x.sa), dev(x.b), dev(x.sb), out, dev(mm))
+    torch.cuda.synchronize()
+    got = bf16_bits(out)
+    ref, _ = oracle.grouped_masked(x.a, x.sa, x.b, x.sb, mm, np.full((g, m_max, n), SENTINEL_BF16, np.uint16))
+    rows = np.arange(m_max)[None, :] < np.clip(mm, 0, m_max)[:, None]
+    assert np.all(got[~rows] == SENTINEL_BF16), "masked rows were written"
+    check_close(bits_to_f64(got[rows]), bits_to_f64(ref[rows]), "masked quarters")
