@@ -59,29 +59,46 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // LDS DMA through buffer loads.  Lane i's bytes go to LDS address m0 +
 // i*size; the address is rsrc.base + voffset + soffset, and bytes at or past
 // rsrc.num_records (range-checked on the per-lane offset) read as zero, so
-// rows and columns past the tile's valid ones need no clamping.  Issued
+// rows and columns past the tile's valid ones need no clamping.  The K-block
+// offset moves the resource base (soffset stays 0): since that offset is
+// less than one row, the range check still ends at the first invalid row.  Issued
 // through inline asm so the compiler's wait-count pass does not treat every
 // later LDS read as dependent on every in-flight DMA; the waits are explicit
 // below.  Nothing else in these kernels uses m0.
 typedef int v4i __attribute__((ext_vector_type(4)));
 
 // Raw buffer resource: 48-bit base, stride 0, byte range, 32-bit data format.
-__device__ __forceinline__ v4i buffer_rsrc(const void* base, uint32_t num_bytes) {
+// Kept as four wave-uniform scalars (scalar-unit arithmetic) and packed into
+// the 128-bit instruction operand only at the DMA.
+struct Rsrc {
+  uint32_t lo, hi, num, flags;
+};
+
+__device__ __forceinline__ Rsrc buffer_rsrc(const void* base, uint32_t num_bytes) {
   const uint64_t b = (uint64_t)base;
-  return v4i{(int)__builtin_amdgcn_readfirstlane((uint32_t)b),
-             (int)(__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) & 0xffffu),
-             (int)__builtin_amdgcn_readfirstlane(num_bytes), 0x00020000};
+  return Rsrc{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b),
+              (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) & 0xffffu,
+              (uint32_t)__builtin_amdgcn_readfirstlane(num_bytes), 0x00020000u};
+}
+
+// The resource moved `bytes` further along (bytes <= num), with its range cut
+// to zero unless `live`: the range check still ends where the original one
+// did, and a dead resource reads zeros without touching memory.
+__device__ __forceinline__ v4i at(const Rsrc& r, uint32_t bytes, bool live) {
+  const uint64_t b = (((uint64_t)r.hi << 32) | r.lo) + bytes;
+  return v4i{(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xffffu), (int)(live ? r.num - bytes : 0u),
+             (int)r.flags};
 }
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(uint32_t lds, v4i rsrc, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+__device__ __forceinline__ void dma16(uint32_t lds, v4i rsrc, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc) : "memory", "m0");
 }
-__device__ __forceinline__ void dma4(uint32_t lds, v4i rsrc, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-               :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+__device__ __forceinline__ void dma4(uint32_t lds, v4i rsrc, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -262,10 +279,10 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     // K-grouped weight gradients share one B [N,T]; the group picks the K range
     const int bg = (KIND == KIND_KGROUPED) ? 0 : g;
     const int bcols = min(BN, p.n - n0);  // valid B rows (output columns) of the tile
-    const v4i rsA = buffer_rsrc(p.a + a_row0 * (int64_t)p.lda, (uint32_t)rows * p.lda);
-    const v4i rsB = buffer_rsrc(p.b + ((int64_t)bg * p.n + n0) * (int64_t)p.lda, (uint32_t)bcols * p.lda);
-    const v4i rsSA = buffer_rsrc(p.sa + a_row0 * (int64_t)p.kbs, (uint32_t)rows * p.kbs * 4);
-    const v4i rsSB = kRowScaleB
+    const Rsrc rsA = buffer_rsrc(p.a + a_row0 * (int64_t)p.lda, (uint32_t)rows * p.lda);
+    const Rsrc rsB = buffer_rsrc(p.b + ((int64_t)bg * p.n + n0) * (int64_t)p.lda, (uint32_t)bcols * p.lda);
+    const Rsrc rsSA = buffer_rsrc(p.sa + a_row0 * (int64_t)p.kbs, (uint32_t)rows * p.kbs * 4);
+    const Rsrc rsSB = kRowScaleB
         ? buffer_rsrc(p.sb + (int64_t)n0 * p.kbs, (uint32_t)bcols * p.kbs * 4)
         : buffer_rsrc(p.sb + ((int64_t)g * nb_rows + n0 / kBK) * p.kbs,
                       (uint32_t)(nb_rows - n0 / kBK) * p.kbs * 4);
@@ -279,35 +296,46 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     const uint32_t svoff = (uint32_t)lane * p.kbs * 4;
     const uint32_t sstep = 64u * p.kbs * 4;
 
-    const v4i rsNull = buffer_rsrc(p.a, 0);  // every byte out of range: reads zeros, no traffic
     // this wave's DMAs for K block kb0 + rel into ring stage `st`; only the
     // pieces with index in [lo, hi) (A pieces first, then B, then scales), so
     // a block's DMAs can be spread over the fragment groups of the previous
     // block instead of stalling every wave at the same point.  Branch-free: a
     // block past the tile's K range reads nothing (null resource) into a
-    // stage no later block of the tile uses.
+    // stage no later block of the tile uses; its resources have an empty
+    // range (they read zeros and touch no memory).
     constexpr int ND = QA + QB + QS;
     auto issue = [&](int rel, int st, int lo, int hi) {
       const bool live = rel < nkb;
       const int kb = kb0 + rel;
       const uint32_t base = smem_lds + st * STAGE;
-      const uint32_t soff = __builtin_amdgcn_readfirstlane(kb * kBK);
-      const uint32_t ssoff = __builtin_amdgcn_readfirstlane(kb * 4);
-      const v4i ra = live ? rsA : rsNull, rb = live ? rsB : rsNull;
+      const uint32_t koff = __builtin_amdgcn_readfirstlane(kb * kBK);
+      const uint32_t skoff = __builtin_amdgcn_readfirstlane(kb * 4);
+      const v4i ra = at(rsA, koff, live);
+      const v4i rb = at(rsB, koff, live);
 #pragma unroll
       for (int q = 0; q < QA; ++q)
-        if (q >= lo && q < hi) dma16(base + OFF_A + (wave + NW * q) * 1024, ra, voff0 + q * step, soff);
+        if (q >= lo && q < hi) dma16(base + OFF_A + (wave + NW * q) * 1024, ra, voff0 + q * step);
 #pragma unroll
       for (int q = 0; q < QB; ++q)
-        if (QA + q >= lo && QA + q < hi) dma16(base + OFF_B + (wave + NW * q) * 1024, rb, voff0 + q * step, soff);
+        if (QA + q >= lo && QA + q < hi) dma16(base + OFF_B + (wave + NW * q) * 1024, rb, voff0 + q * step);
 #pragma unroll
       for (int q = 0; q < QS; ++q) {
         if (QA + QB + q < lo || QA + QB + q >= hi) continue;
         const int sp = wave + NW * q;  // scale piece: sa rows 64*sp.., then sb
         const bool is_a = sp < PSA, real = sp < PS && live;
-        const v4i rs = !real ? rsNull : (is_a ? rsSA : rsSB);
-        const uint32_t lds = sp < PS ? base + OFF_SA + sp * 256 : smem_lds + S * STAGE;
-        dma4(lds, rs, svoff + (uint32_t)(is_a ? sp : sp - PSA) * sstep, ssoff);
+        // select the sa or sb resource arithmetically (a select here is lowered
+        // to an indexed stack array)
+        const uint32_t f = (uint32_t)__builtin_amdgcn_readfirstlane(is_a ? 1 : 0);
+        Rsrc sel;
+        sel.lo = rsSB.lo + (rsSA.lo - rsSB.lo) * f;
+        sel.hi = rsSB.hi + (rsSA.hi - rsSB.hi) * f;
+        sel.num = rsSB.num + (rsSA.num - rsSB.num) * f;
+        sel.flags = rsSA.flags;
+        const v4i r4 = at(sel, skoff, real);
+        const v4i rs = v4i{(int)__builtin_amdgcn_readfirstlane(r4[0]), (int)__builtin_amdgcn_readfirstlane(r4[1]),
+                           (int)__builtin_amdgcn_readfirstlane(r4[2]), (int)__builtin_amdgcn_readfirstlane(r4[3])};
+        const uint32_t lds = __builtin_amdgcn_readfirstlane(sp < PS ? base + OFF_SA + sp * 256 : smem_lds + S * STAGE);
+        dma4(lds, rs, svoff + (uint32_t)(is_a ? sp : sp - PSA) * sstep);
       }
     };
 
@@ -560,6 +588,8 @@ hipError_t launch_shape(int kind, const Params& p, int grid, hipStream_t stream)
 // (BM, BN, waves along M, waves along N, LDS ring stages)
 #define DG_SHAPES(X)      \
   X(256, 256, 1, 8, 2)    \
+  X(256, 128, 1, 8, 3)    \
+  X(256, 64, 1, 4, 3)     \
   X(256, 128, 1, 4, 3)    \
   X(256, 128, 2, 2, 3)    \
   X(256, 256, 2, 4, 2)    \
