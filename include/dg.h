@@ -14,8 +14,16 @@
  *
  * Conventions shared by every entry point:
  *   - every tensor pointer is a DEVICE pointer owned by the caller; the
- *     library never allocates, frees or keeps user memory and holds no
- *     workspace, so calls may be captured into a HIP graph;
+ *     library never allocates, frees or keeps user memory;
+ *   - split K: for shapes with too few output tiles to occupy every compute
+ *     unit (few rows, long K), the dense and masked calls split K over several
+ *     workgroups and add the fp32 partials in a second kernel, in a fixed
+ *     order (results are deterministic).  The partials live in a temporary
+ *     workspace (splits * rows * N * 4 bytes) taken from a memory pool the
+ *     library owns per device, allocated and returned in stream order; the
+ *     pool keeps freed blocks for reuse until the process ends.  A call made
+ *     while `stream` is being captured into a HIP graph never splits, so it
+ *     allocates nothing and records only the GEMM kernel;
  *   - tensors are row-major with the last dimension contiguous;
  *   - fp8 = OCP E4M3FN bytes (what torch calls float8_e4m3fn); scales fp32;
  *   - K_b = K/128, NB = ceil(N/128);
@@ -121,10 +129,11 @@ typedef enum {
 typedef struct {
   int block_m;      /* output rows per workgroup tile                        */
   int block_n;      /* output columns per workgroup tile                     */
-  int waves_m;      /* waves along M (4 waves per workgroup in total)        */
+  int waves_m;      /* waves along M (waves_m * waves_n is 4 or 8)           */
   int waves_n;      /* waves along N                                         */
   int tiles;        /* tile count (an upper bound for the masked layout)     */
   int grid;         /* persistent workgroups launched                        */
+  int k_splits;     /* workgroups sharing one output tile along K (1 = none) */
 } dg_tile_config;
 
 dg_status dg_select_config(int kind, int m, int n, int k, int num_groups, int num_cus,

@@ -2,9 +2,11 @@
 // tile heuristic and kernel dispatch.  Validation runs before any HIP call, so
 // every error path can be exercised on a machine without a GPU.
 #include <atomic>
+#include <cstdint>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/dg.h"
 #include "dg_kernel.h"
@@ -56,6 +58,24 @@ bool parse_forced(dg::TileShape* s) {
   return true;
 }
 
+// Split K (dense and masked): when a shape's output tiles cannot occupy the
+// CUs and K is long, kSplitTarget workgroups share each tile, each covering
+// at least kSplitMinBlocks K blocks -- fewer or shorter splits lose more to
+// the extra reduction pass than they gain (measured).
+constexpr int kMaxSplits = 16;
+constexpr int kSplitTarget = 4;
+constexpr int kSplitMinBlocks = 12;
+constexpr size_t kMaxWorkspaceBytes = size_t(256) << 20;  // split-K partials per stream
+
+int choose_splits(int kind, long tiles, int num_cus, int kbs) {
+  if (kind != DG_KIND_DENSE && kind != DG_KIND_MASKED) return 1;
+  if (tiles * 10 >= num_cus * 7L) return 1;  // enough tiles already
+  long s = (num_cus + tiles - 1) / tiles;
+  if (s > kSplitTarget) s = kSplitTarget;
+  if (s > kbs / kSplitMinBlocks) s = kbs / kSplitMinBlocks;
+  return s < 2 ? 1 : (int)s;
+}
+
 struct Candidate {
   dg::TileShape s;
   double eff;  // relative matrix-unit efficiency of the tile shape
@@ -64,31 +84,39 @@ struct Candidate {
 // Per-shape tile choice (DeepGEMM pages: block sizes and wave counts are
 // selected per shape; small M underuses the matrix units).  `rows` is the
 // output rows per group, `groups` the number of groups whose tiles share the
-// launch (masked: an upper bound from M_max).
-//   * masked layout with enough groups: tall 256-row tiles (B read once);
-//   * few rows (<= 128 per group): narrow column tiles, the widest that still
-//     gives every CU a workgroup, because such shapes stream B from HBM;
+// launch (masked: an upper bound from M_max).  `allow_split`: K may be split
+// over workgroups (choose_splits).  Thresholds are from measured sweeps on
+// MI355X:
+//   * masked layout: tall 256-row tiles (B read once per group, the waves
+//     skip the row quarters past masked_m), as wide as the group count allows;
+//   * few rows (<= 128 per group): the largest tile that still leaves enough
+//     tiles -- about 0.7 of the CUs, or a quarter of that when a long K is
+//     split four ways -- since such shapes stream B from HBM;
 //   * otherwise: minimise (full waves of tiles over the CUs) x (workgroups
 //     per CU) x (tile area / tile efficiency), so a large tile wins unless
 //     it leaves CUs idle.
-dg::TileShape heuristic(int kind, int rows, int n, int k, int groups, int num_cus) {
-  (void)k;
+dg::TileShape heuristic(int kind, int rows, int n, int k, int groups, int num_cus, bool allow_split) {
+  const int kbs = k / 128;
+  const bool long_k = allow_split && kbs >= 3 * kSplitMinBlocks;
   if (kind == DG_KIND_MASKED && rows <= 256) {
-    // one tall tile per (group, column block) covers every row of the group,
-    // so B is streamed once; its waves skip the row quarters past masked_m
-    const dg::TileShape tall256{256, 256, 1, 8}, tall128{256, 128, 1, 4};
-    if ((long)groups * ceil_div(n, 256) * 4 >= 3L * num_cus) return tall256;
-    if ((long)groups * ceil_div(n, 128) * 4 >= 3L * num_cus) return tall128;
+    const dg::TileShape tall256{256, 256, 1, 8}, tall128{256, 128, 1, 8}, tall64{256, 64, 1, 4};
+    const long cols128 = (long)groups * ceil_div(n, 128);
+    if (cols128 * 2 >= 3L * num_cus) return tall256;   // enough tiles at 256 columns
+    if (long_k) return cols128 >= num_cus / 4 ? tall128 : tall64;
+    return cols128 * 4 >= 3L * num_cus ? tall128 : tall64;
   }
   if (rows <= 128 || kind == DG_KIND_MASKED) {
     const int bm = rows <= 64 ? 64 : 128;
-    const dg::TileShape cands[4] = {{bm, 128, bm / 64 == 1 ? 1 : 2, bm / 64 == 1 ? 4 : 2},
-                                    {bm, 64, bm / 64 == 1 ? 1 : 2, bm / 64 == 1 ? 4 : 2},
-                                    {64, 32, 2, 2},
-                                    {64, 32, 2, 2}};
+    const dg::TileShape wide = bm == 64 ? dg::TileShape{64, 128, 1, 4} : dg::TileShape{128, 128, 2, 2};
+    const dg::TileShape mid = bm == 64 ? dg::TileShape{64, 64, 1, 4} : dg::TileShape{128, 64, 2, 2};
+    const dg::TileShape cands[5] = {wide, mid, {64, 128, 1, 4}, {64, 64, 1, 4}, {64, 32, 2, 2}};
+    const long need = long_k && (kind == DG_KIND_DENSE) ? (num_cus * 7L) / (10L * kSplitTarget)
+                                                         : (num_cus * 7L) / 10L;
     for (const auto& c : cands) {
+      if (kind == DG_KIND_CONTIGUOUS && 128 % c.bm != 0) continue;
+      if (!dg::has_instance(kind, c)) continue;
       const long tiles = (long)groups * ceil_div(rows, c.bm) * ceil_div(n, c.bn);
-      if (tiles >= num_cus && dg::has_instance(kind, c)) return c;
+      if (tiles >= need) return c;
     }
     return dg::TileShape{64, 32, 2, 2};
   }
@@ -113,6 +141,9 @@ dg::TileShape heuristic(int kind, int rows, int n, int k, int groups, int num_cu
       pick = c.s;
     }
   }
+  // short K (few K blocks per tile): the 1x8 wave layout of the 256x256 tile
+  // keeps its epilogue stores shorter per wave (measured faster at K <= 1024)
+  if (pick.bm == 256 && pick.bn == 256 && kbs <= 8 && kind == DG_KIND_DENSE) pick = dg::TileShape{256, 256, 1, 8};
   return pick;
 }
 
@@ -121,36 +152,132 @@ struct Launch {
   int grid;
 };
 
-dg_status plan(int kind, int rows, int n, int k, int groups, int num_cus, dg::Params& p, Launch& l) {
+// `allow_split`: split-K needs a temporary workspace, so it is planned only
+// for calls that may allocate (not under stream capture).
+dg_status plan(int kind, int rows, int n, int k, int groups, int num_cus, bool allow_split, dg::Params& p,
+               Launch& l) {
   dg::TileShape s;
-  if (!parse_forced(&s)) s = heuristic(kind, rows, n, k, groups, num_cus);
+  if (!parse_forced(&s)) s = heuristic(kind, rows, n, k, groups, num_cus, allow_split);
   if (!dg::has_instance(kind, s)) return DG_ERROR_UNSUPPORTED;
   if (kind == DG_KIND_CONTIGUOUS && 128 % s.bm != 0) return DG_ERROR_UNSUPPORTED;
   p.tiles_m = ceil_div(rows, s.bm);
   p.tiles_n = ceil_div(n, s.bn);
   const long tiles = (long)groups * p.tiles_m * p.tiles_n;
-  if (tiles > 0x7fffffffL) return DG_ERROR_UNSUPPORTED;
+  if (tiles > 0x7fffffffL / kMaxSplits) return DG_ERROR_UNSUPPORTED;
   p.tiles = (int)tiles;
   const long slots = (long)num_cus * occupancy(kind, s);
-  long grid = tiles < slots ? tiles : slots;
+  const int kbs = k / 128;
+  int splits = allow_split ? choose_splits(kind, tiles, num_cus, kbs) : 1;
+  if (const char* e = std::getenv("DG_FORCE_SPLITS"))
+    if (allow_split && (kind == DG_KIND_DENSE || kind == DG_KIND_MASKED)) splits = std::atoi(e);
+  if (splits < 1) splits = 1;
+  if (splits > kMaxSplits) splits = kMaxSplits;
+  if (splits > kbs) splits = kbs;
+  const double split_bytes = 4.0 * groups * rows * (double)n;  // one fp32 partial of every output
+  while (splits > 1 && splits * split_bytes > (double)kMaxWorkspaceBytes) --splits;
+  // equal chunks with no empty split: every partial the reduction reads is written
+  const int chunk = ceil_div(kbs, splits);
+  splits = ceil_div(kbs, chunk);
+  p.splits = splits;
+  p.kchunk = chunk;
+  const long work = tiles * splits;
+  long grid = work < slots ? work : slots;
   if (grid > 8) grid -= grid % 8;  // keep workgroup -> XCD round robin aligned
   if (grid < 1) grid = 1;
   l.shape = s;
   l.grid = (int)grid;
   if (std::getenv("DG_LOG"))
-    std::fprintf(stderr, "[dg] kind=%d rows=%d n=%d k=%d G=%d -> tile %dx%d waves %dx%d tiles=%ld grid=%ld\n",
-                 kind, rows, n, k, groups, s.bm, s.bn, s.wm, s.wn, tiles, grid);
+    std::fprintf(stderr, "[dg] kind=%d rows=%d n=%d k=%d G=%d -> tile %dx%d waves %dx%d tiles=%ld splits=%d grid=%ld\n",
+                 kind, rows, n, k, groups, s.bm, s.bn, s.wm, s.wn, tiles, splits, grid);
   return DG_SUCCESS;
+}
+
+// Split-K partials live in a workspace cached per (device, stream): calls on
+// one stream run in order, so they can share it; calls on different streams
+// get different buffers.  A workspace grows when a call needs more: the new
+// buffer comes from a memory pool the library owns per device and the old one
+// goes back to it, both in stream order (no device synchronisation).  The
+// buffers stay with the library until the process ends.
+struct StreamWorkspace {
+  int dev;
+  hipStream_t stream;
+  void* ptr;
+  size_t bytes;
+};
+
+std::mutex g_ws_mutex;
+hipMemPool_t g_pool[kMaxDevices];
+StreamWorkspace g_ws[256];
+int g_ws_count = 0;
+
+hipMemPool_t device_pool(int dev) {  // caller holds g_ws_mutex
+  if (!g_pool[dev]) {
+    hipMemPoolProps props;
+    std::memset(&props, 0, sizeof(props));
+    props.allocType = hipMemAllocationTypePinned;
+    props.handleTypes = hipMemHandleTypeNone;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t pool = nullptr;
+    if (hipMemPoolCreate(&pool, &props) != hipSuccess) return nullptr;
+    uint64_t keep = UINT64_MAX;
+    (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+    g_pool[dev] = pool;
+  }
+  return g_pool[dev];
+}
+
+// A workspace of at least `bytes` usable in the order of `stream`, or null.
+void* stream_workspace(hipStream_t stream, size_t bytes) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  StreamWorkspace* w = nullptr;
+  for (int i = 0; i < g_ws_count; ++i)
+    if (g_ws[i].dev == dev && g_ws[i].stream == stream) w = &g_ws[i];
+  if (w && w->bytes >= bytes) return w->ptr;
+  if (!w) {
+    if (g_ws_count == (int)(sizeof(g_ws) / sizeof(g_ws[0]))) return nullptr;
+    w = &g_ws[g_ws_count++];
+    *w = StreamWorkspace{dev, stream, nullptr, 0};
+  }
+  hipMemPool_t pool = device_pool(dev);
+  if (!pool) return nullptr;
+  // grow geometrically so a sequence of slightly larger calls allocates rarely
+  size_t want = w->bytes * 2 > bytes ? w->bytes * 2 : bytes;
+  if (want > kMaxWorkspaceBytes) want = bytes;
+  void* p = nullptr;
+  if (hipMallocFromPoolAsync(&p, want, pool, stream) != hipSuccess) return nullptr;
+  if (w->ptr) (void)hipFreeAsync(w->ptr, stream);  // after the calls that used it
+  w->ptr = p;
+  w->bytes = want;
+  return p;
+}
+
+bool stream_capturing(hipStream_t stream) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return true;  // unknown: do not allocate
+  return cs != hipStreamCaptureStatusNone;
 }
 
 dg_status run(int kind, dg::Params& p, int rows, int n, int k, int groups, hipStream_t stream) {
   int cus = 0;
   if (device_cus(&cus) != 0) return DG_ERROR_LAUNCH;
-  Launch l;
-  dg_status st = plan(kind, rows, n, k, groups, cus, p, l);
-  if (st != DG_SUCCESS) return st;
   (void)hipGetLastError();  // clear a stale error from unrelated work
+  const bool may_split = (kind == DG_KIND_DENSE || kind == DG_KIND_MASKED) && !stream_capturing(stream);
+  Launch l;
+  dg_status st = plan(kind, rows, n, k, groups, cus, may_split, p, l);
+  if (st != DG_SUCCESS) return st;
+  if (p.splits <= 1) {
+    if (dg::launch(kind, l.shape, p, l.grid, stream) != hipSuccess) return DG_ERROR_LAUNCH;
+    return DG_SUCCESS;
+  }
+  p.ws_stride = (int64_t)groups * rows * n;
+  void* ws = stream_workspace(stream, (size_t)p.splits * p.ws_stride * sizeof(float));
+  if (!ws) return DG_ERROR_LAUNCH;
+  p.ws = static_cast<float*>(ws);
   if (dg::launch(kind, l.shape, p, l.grid, stream) != hipSuccess) return DG_ERROR_LAUNCH;
+  if (dg::launch_splitk_reduce(kind, p, stream) != hipSuccess) return DG_ERROR_LAUNCH;
   return DG_SUCCESS;
 }
 
@@ -309,7 +436,7 @@ dg_status dg_select_config(int kind, int m, int n, int k, int num_groups, int nu
   dg::Params p = base_params();
   Launch l;
   const int groups = (kind == DG_KIND_MASKED || kind == DG_KIND_K_GROUPED_WGRAD) ? num_groups : 1;
-  dg_status st = plan(kind, m, n, k, groups, num_cus, p, l);
+  dg_status st = plan(kind, m, n, k, groups, num_cus, true, p, l);
   if (st != DG_SUCCESS) return st;
   out->block_m = l.shape.bm;
   out->block_n = l.shape.bn;
@@ -317,6 +444,7 @@ dg_status dg_select_config(int kind, int m, int n, int k, int num_groups, int nu
   out->waves_n = l.shape.wn;
   out->tiles = p.tiles;
   out->grid = l.grid;
+  out->k_splits = p.splits;
   return DG_SUCCESS;
 }
 

@@ -34,6 +34,14 @@ struct Params {
   int tiles_n;           // ceil(n / BN)
   int tiles;             // tile count (upper bound for the masked layout)
   int vec_out;           // 1 if 4 consecutive outputs may be stored as one vector
+  // split-K (dense and masked): `splits` workgroups share one output tile,
+  // split s covering K blocks [s*kchunk, min(kbs, (s+1)*kchunk)) and writing
+  // its fp32 partial tile to ws + s*ws_stride (same row/column indexing as
+  // the output); the reduction kernel then sums the partials in split order.
+  int splits;            // 1 = no split
+  int kchunk;            // K blocks per split
+  float* ws;             // fp32 partials [splits][rows of all groups][n]
+  int64_t ws_stride;     // floats per split
   int kb_begin[kMaxKGroups + 1];  // K-grouped: first 128-block of each group
 };
 
@@ -45,6 +53,10 @@ struct TileShape {
 // hipErrorInvalidValue if no instance exists for that shape.
 hipError_t launch(int kind, const TileShape& shape, const Params& p, int grid,
                   hipStream_t stream);
+
+// Sums the split-K partials of p.ws in split order and writes bf16 p.out
+// (dense: every row; masked: rows below masked_m of each group).
+hipError_t launch_splitk_reduce(int kind, const Params& p, hipStream_t stream);
 
 // True if an instance exists for (kind, shape).
 bool has_instance(int kind, const TileShape& shape);

@@ -210,12 +210,18 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
       T += ((v + BM - 1) / BM) * p.tiles_n;
     }
   }
-  const int per_xcd = (T + 7) >> 3;
+  // split-K: `splits` consecutive work items share one output tile
+  constexpr bool kCanSplit = (KIND == KIND_DENSE || KIND == KIND_MASKED);
+  const int splits = kCanSplit ? p.splits : 1;
+  const int TS = T * splits;
+  const int per_xcd = (TS + 7) >> 3;
   const int nb_rows = (p.n + kBK - 1) / kBK;
 
   for (int t = blockIdx.x; t < per_xcd * 8; t += gridDim.x) {
-    const int L = (t & 7) * per_xcd + (t >> 3);
-    if (L >= T) continue;
+    const int LS = (t & 7) * per_xcd + (t >> 3);
+    if (LS >= TS) continue;
+    const int L = splits > 1 ? LS / splits : LS;
+    const int split = LS - L * splits;
 
     // ---- decode tile ----
     int g = 0, m0, n0, rows, kb0 = 0, kb1 = p.kbs;
@@ -255,6 +261,10 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
       rows = min(BM, p.m - m0);
       a_row0 = m0;
       out_row0 = m0;
+    }
+    if (kCanSplit && splits > 1) {
+      kb0 = split * p.kchunk;
+      kb1 = min(p.kbs, kb0 + p.kchunk);
     }
     const int nkb = kb1 - kb0;
     if (nkb <= 0) continue;  // empty K range: D unchanged
@@ -525,6 +535,23 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
         row_ok = ml < rows;
       if (!row_ok) continue;
       const int64_t orow = out_row0 + ml;
+      if (kCanSplit && splits > 1) {
+        // this split's fp32 partial tile (plain stores, summed later)
+        float* w = p.ws + split * p.ws_stride + orow * p.n;
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+          const int n = n0 + wn * WTN + 16 * i + 4 * lq;
+          if (n >= p.n) continue;
+          if (p.vec_out && n + 3 < p.n) {
+            *reinterpret_cast<float4*>(w + n) = float4{acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (n + r < p.n) w[n + r] = acc[i][j][r];
+          }
+        }
+        continue;
+      }
 #pragma unroll
       for (int i = 0; i < FN; ++i) {
         const int n = n0 + wn * WTN + 16 * i + 4 * lq;
@@ -585,6 +612,44 @@ hipError_t launch_shape(int kind, const Params& p, int grid, hipStream_t stream)
   return hipGetLastError();
 }
 
+// Split-K reduction: C = bf16(sum of the fp32 partials in split order).  One
+// thread per 4 consecutive outputs of a row, one 16-byte load per split; the
+// masked layout skips rows at or past masked_m of their group, which the
+// GEMM kernel did not write either.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const Params p, int masked) {
+  const int nq = (p.n + 3) / 4;
+  const int64_t items = (int64_t)p.groups * p.m * nq;
+  for (int64_t it = blockIdx.x * 256LL + threadIdx.x; it < items; it += (int64_t)gridDim.x * 256) {
+    const int64_t row = it / nq;
+    const int c = (int)(it - row * nq) * 4;
+    if (masked) {
+      const int g = (int)(row / p.m);
+      if (row - (int64_t)g * p.m >= min(max(p.ctrl[g], 0), p.m)) continue;
+    }
+    const float* w = p.ws + row * p.n + c;
+    uint16_t* o = static_cast<uint16_t*>(p.out) + row * p.n + c;
+    if (p.vec_out && c + 3 < p.n) {
+      float4 v = *reinterpret_cast<const float4*>(w);
+      for (int sp = 1; sp < p.splits; ++sp) {
+        const float4 u = *reinterpret_cast<const float4*>(w + sp * p.ws_stride);
+        v.x += u.x;
+        v.y += u.y;
+        v.z += u.z;
+        v.w += u.w;
+      }
+      const uint32_t lo = (uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16);
+      *reinterpret_cast<uint2*>(o) = uint2{lo, hi};
+    } else {
+      for (int r = 0; r < 4 && c + r < p.n; ++r) {
+        float v = w[r];
+        for (int sp = 1; sp < p.splits; ++sp) v += w[sp * p.ws_stride + r];
+        o[r] = f32_to_bf16(v);
+      }
+    }
+  }
+}
+
 // (BM, BN, waves along M, waves along N, LDS ring stages)
 #define DG_SHAPES(X)      \
   X(256, 256, 1, 8, 2)    \
@@ -622,6 +687,15 @@ int lds_bytes_of(int kind, const TileShape& s) {
   DG_SHAPES(X)
 #undef X
   return 0;
+}
+
+hipError_t launch_splitk_reduce(int kind, const Params& p, hipStream_t stream) {
+  if (kind != KIND_DENSE && kind != KIND_MASKED) return hipErrorInvalidValue;
+  const int64_t items = (int64_t)p.groups * p.m * ((p.n + 3) / 4);
+  const int64_t blocks = (items + 255) / 256;
+  const int grid = (int)(blocks < 4096 ? (blocks > 0 ? blocks : 1) : 4096);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid), dim3(256), 0, stream, p, kind == KIND_MASKED ? 1 : 0);
+  return hipGetLastError();
 }
 
 hipError_t launch(int kind, const TileShape& s, const Params& p, int grid, hipStream_t stream) {

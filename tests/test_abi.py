@@ -120,7 +120,8 @@ def test_wgrad_argument_errors(lib):
 
 def _cfg(lib, kind, m, n, k, g=1, cus=256):
     class Cfg(ctypes.Structure):
-        _fields_ = [(f, ctypes.c_int) for f in ("block_m", "block_n", "waves_m", "waves_n", "tiles", "grid")]
+        _fields_ = [(f, ctypes.c_int) for f in ("block_m", "block_n", "waves_m", "waves_n", "tiles", "grid",
+                                                "k_splits")]
     c = Cfg()
     lib.dg_select_config.argtypes = [ctypes.c_int] * 6 + [ctypes.POINTER(Cfg)]
     st = lib.dg_select_config(kind, m, n, k, g, cus, ctypes.byref(c))
@@ -142,7 +143,16 @@ def test_heuristic_invariants(lib, kind, m, n, k, g):
     groups = g if kind in (2, 4) else 1
     tiles = groups * -(-m // c["block_m"]) * -(-n // c["block_n"])
     assert c["tiles"] == tiles
-    assert 1 <= c["grid"] <= tiles
+    s = c["k_splits"]
+    assert 1 <= s <= 16
+    if kind not in (0, 2):
+        assert s == 1  # split K only for the bf16-output dense and masked layouts
+    kbs = k // 128
+    if s > 1:
+        chunk = -(-kbs // s)
+        assert -(-kbs // chunk) == s, "a split would be empty"
+        assert chunk >= 4
+    assert 1 <= c["grid"] <= tiles * s
     if c["grid"] > 8:
         assert c["grid"] % 8 == 0
     assert c["grid"] <= 2 * 256
@@ -151,8 +161,20 @@ def test_heuristic_invariants(lib, kind, m, n, k, g):
     assert _cfg(lib, kind, m, n, k, g) == c  # deterministic
 
 
+def test_split_k_planning(lib):
+    """Few output tiles and a long K: split K to give every CU work; many
+    tiles: no split."""
+    c = _cfg(lib, 0, 64, 2112, 7168)
+    assert c["k_splits"] > 1 and c["tiles"] * c["k_splits"] >= 256
+    c = _cfg(lib, 2, 256, 4096, 7168, 1)
+    assert c["k_splits"] > 1
+    assert _cfg(lib, 0, 4096, 7168, 16384)["k_splits"] == 1
+    assert _cfg(lib, 0, 64, 2112, 384)["k_splits"] == 1  # K too short to split
+    assert _cfg(lib, 3, 64, 2112, 7168)["k_splits"] == 1  # fp32-accumulate layouts never split
+
+
 def test_heuristic_rejects_bad_queries(lib):
-    c = ctypes.c_int * 6
+    c = ctypes.c_int * 7
     out = c()
     lib.dg_select_config.argtypes = [ctypes.c_int] * 6 + [ctypes.c_void_p]
     assert lib.dg_select_config(9, 1, 1, 128, 1, 256, ctypes.addressof(out)) == INVALID

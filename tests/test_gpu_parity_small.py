@@ -175,3 +175,82 @@ def test_masked_row_quarters(dg, force_tile, tile):
     rows = np.arange(m_max)[None, :] < np.clip(mm, 0, m_max)[:, None]
     assert np.all(got[~rows] == SENTINEL_BF16), "masked rows were written"
     check_close(bits_to_f64(got[rows]), bits_to_f64(ref[rows]), "masked quarters")
+
+
+@pytest.fixture
+def force_splits():
+    def _set(s):
+        if s is None:
+            os.environ.pop("DG_FORCE_SPLITS", None)
+        else:
+            os.environ["DG_FORCE_SPLITS"] = str(s)
+    yield _set
+    os.environ.pop("DG_FORCE_SPLITS", None)
+
+
+@pytest.mark.parametrize("tile", ["64x32x2x2", "128x128x2x2", "256x256x1x8"])
+@pytest.mark.parametrize("splits", [2, 3, 4, 10])
+@pytest.mark.parametrize("m,n,k", [(70, 300, 1280), (1, 130, 512), (200, 2112, 1792)])
+def test_dense_split_k(dg, force_tile, force_splits, m, n, k, tile, splits):
+    """K split over workgroups, partials summed by the reduction kernel; K
+    blocks not divisible by the split count (uneven last chunk)."""
+    d = inputs.make_dense(m, n, k, seed=inputs.SEED_BASE + 41 + m + k)
+    force_tile(tile)
+    force_splits(splits)
+    say(f"dense split-K {m}x{n}x{k} tile={tile} splits={splits}")
+    got = _dense_run(dg, d)
+    ref, _ = oracle.gemm_fp8_nt(d.a, d.sa, d.b, d.sb)
+    check_close(bits_to_f64(got), bits_to_f64(ref), f"dense split {m}x{n}x{k} {tile} s{splits}")
+    assert np.array_equal(got, _dense_run(dg, d)), "split-K result not deterministic"
+
+
+@pytest.mark.parametrize("tile", ["256x256x1x8", "256x64x1x4", "64x32x2x2"])
+@pytest.mark.parametrize("splits", [2, 5])
+def test_masked_split_k(dg, force_tile, force_splits, tile, splits):
+    mm = np.array([0, 1, 96, 300, 50, 64, 65], np.int32)  # empty, one row, full, clamped, partial
+    g, m_max, n, k = mm.size, 96, 260, 1280
+    x = inputs.make_masked(g, m_max, n, k, seed=inputs.SEED_BASE + 43, masked_m=mm)
+    force_tile(tile)
+    force_splits(splits)
+    say(f"masked split-K G={g} tile={tile} splits={splits}")
+
+    def run():
+        out = sentinel_bf16((g, m_max, n))
+        dg.dg_grouped_fp8_masked(dev(x.a), dev(x.sa), dev(x.b), dev(x.sb), out, dev(mm))
+        torch.cuda.synchronize()
+        return bf16_bits(out)
+    got = run()
+    ref, _ = oracle.grouped_masked(x.a, x.sa, x.b, x.sb, mm, np.full((g, m_max, n), SENTINEL_BF16, np.uint16))
+    rows = np.arange(m_max)[None, :] < np.clip(mm, 0, m_max)[:, None]
+    assert np.all(got[~rows] == SENTINEL_BF16), "masked rows were written"
+    check_close(bits_to_f64(got[rows]), bits_to_f64(ref[rows]), f"masked split {tile} s{splits}")
+    assert np.array_equal(got, run()), "split-K result not deterministic"
+
+
+def test_split_k_under_graph_capture(dg):
+    """A call captured into a HIP graph does not split (no allocation while
+    capturing); its replays match the eager split-K result."""
+    d = inputs.make_dense(64, 2112, 7168, seed=inputs.SEED_BASE + 47)
+    assert dg.select_config(dg.KIND_DENSE, 64, 2112, 7168)["k_splits"] > 1
+    say("dense 64x2112x7168 eager (split) vs graph (no split)")
+    a, sa, b, sb = dev(d.a), dev(d.sa), dev(d.b), dev(d.sb)
+    eager = sentinel_bf16((d.m, d.n))
+    dg.dg_gemm_fp8_nt(a, sa, b, sb, eager)
+    torch.cuda.synchronize()
+    out = sentinel_bf16((d.m, d.n))
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        dg.dg_gemm_fp8_nt(a, sa, b, sb, out)  # warm up on the side stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            dg.dg_gemm_fp8_nt(a, sa, b, sb, out)
+    ref, _ = oracle.gemm_fp8_nt(d.a, d.sa, d.b, d.sb)
+    e = bf16_bits(eager)
+    check_close(bits_to_f64(e), bits_to_f64(ref), "eager split")
+    for rep in range(3):
+        out.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        check_close(bits_to_f64(bf16_bits(out)), bits_to_f64(ref), f"graph replay {rep}")
