@@ -122,7 +122,7 @@ dg::TileShape heuristic(int kind, int rows, int n, int k, int groups, int num_cu
   }
   static const Candidate cands[] = {
       // efficiencies measured relative to the 256x256 tile on full waves
-      {{256, 256, 2, 4}, 1.00}, {{256, 128, 2, 2}, 0.85}, {{128, 128, 2, 2}, 0.70},
+      {{256, 256, 2, 4}, 1.00}, {{256, 256, 1, 8}, 0.98}, {{256, 128, 2, 2}, 0.85}, {{128, 128, 2, 2}, 0.70},
       {{128, 64, 2, 2}, 0.50},  {{64, 128, 1, 4}, 0.50},  {{64, 64, 1, 4}, 0.35},
   };
   double best = 1e300;

@@ -66,6 +66,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // later LDS read as dependent on every in-flight DMA; the waits are explicit
 // below.  Nothing else in these kernels uses m0.
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 
 // Raw buffer resource: 48-bit base, stride 0, byte range, 32-bit data format.
 // Kept as four wave-uniform scalars (scalar-unit arithmetic) and packed into
@@ -187,8 +188,10 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   static_assert(PA % NW == 0 && PB % NW == 0, "operand pieces split evenly over the waves");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE + 256];  // + padding-DMA sink
-  __shared__ int sRowOk[KIND == KIND_CONTIGUOUS ? BM : 1];
-  __shared__ int sExpert;
+  // contiguous: rows of a tile that carry its expert, double-buffered by tile
+  // parity (the next tile is looked up while the current one is computed)
+  __shared__ int sRowOk[2][KIND == KIND_CONTIGUOUS ? BM : 1];
+  __shared__ int sExpert[2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -217,17 +220,25 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   const int per_xcd = (TS + 7) >> 3;
   const int nb_rows = (p.n + kBK - 1) / kBK;
 
-  for (int t = blockIdx.x; t < per_xcd * 8; t += gridDim.x) {
-    const int LS = (t & 7) * per_xcd + (t >> 3);
-    if (LS >= TS) continue;
-    const int L = splits > 1 ? LS / splits : LS;
-    const int split = LS - L * splits;
-
-    // ---- decode tile ----
-    int g = 0, m0, n0, rows, kb0 = 0, kb1 = p.kbs;
+  // ---- work items ----
+  // Item t (a grid-stride index, remapped so each XCD gets a contiguous run
+  // of items) is one (output tile, K split) pair.  decode() gives its Tile;
+  // live == 0: no work (past the end, an empty K range, or -- contiguous -- a
+  // block of padding rows).
+  struct Tile {
+    int live, g, m0, n0, rows, kb0, nkb, split;
     int64_t a_row0, out_row0;
+  };
+  const int t_end = per_xcd * 8;
+  auto decode = [&](int t) -> Tile {
+    Tile x{0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    const int LS = (t & 7) * per_xcd + (t >> 3);
+    if (t >= t_end || LS >= TS) return x;
+    const int L = splits > 1 ? LS / splits : LS;
+    x.split = LS - L * splits;
+    int kb1 = p.kbs;
     if constexpr (KIND == KIND_MASKED) {
-      int rem = L, mt = 0, v = 0;
+      int rem = L, mt = 0, v = 0, g = 0;
       for (; g < p.groups; ++g) {
         v = min(max(p.ctrl[g], 0), p.m);
         mt = (v + BM - 1) / BM;
@@ -235,67 +246,125 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
         if (rem < cnt) break;
         rem -= cnt;
       }
-      if (g >= p.groups) continue;  // unreachable for L < T
-      m0 = (rem % mt) * BM;        // m fastest: tiles sharing a B tile run together
-      n0 = (rem / mt) * BN;
-      rows = min(BM, v - m0);
-      a_row0 = (int64_t)g * p.m + m0;
-      out_row0 = a_row0;
+      if (g >= p.groups) return x;  // unreachable for L < T
+      x.g = g;
+      x.m0 = (rem % mt) * BM;       // m fastest: tiles sharing a B tile run together
+      x.n0 = (rem / mt) * BN;
+      x.rows = min(BM, v - x.m0);
+      x.a_row0 = (int64_t)g * p.m + x.m0;
+      x.out_row0 = x.a_row0;
     } else if constexpr (KIND == KIND_KGROUPED) {
       const int per_g = p.tiles_m * p.tiles_n;
-      g = L / per_g;
+      const int g = L / per_g;
       int tm, tn;
       raster(L - g * per_g, p.tiles_m, p.tiles_n, tm, tn);
-      m0 = tm * BM;
-      n0 = tn * BN;
-      rows = min(BM, p.m - m0);
-      kb0 = p.kb_begin[g];
+      x.g = g;
+      x.m0 = tm * BM;
+      x.n0 = tn * BN;
+      x.rows = min(BM, p.m - x.m0);
+      x.kb0 = p.kb_begin[g];
       kb1 = p.kb_begin[g + 1];
-      a_row0 = m0;
-      out_row0 = (int64_t)g * p.m + m0;
+      x.a_row0 = x.m0;
+      x.out_row0 = (int64_t)g * p.m + x.m0;
     } else {
       int tm, tn;
       raster(L, p.tiles_m, p.tiles_n, tm, tn);
-      m0 = tm * BM;
-      n0 = tn * BN;
-      rows = min(BM, p.m - m0);
-      a_row0 = m0;
-      out_row0 = m0;
+      x.m0 = tm * BM;
+      x.n0 = tn * BN;
+      x.rows = min(BM, p.m - x.m0);
+      x.a_row0 = x.m0;
+      x.out_row0 = x.m0;
     }
     if (kCanSplit && splits > 1) {
-      kb0 = split * p.kchunk;
-      kb1 = min(p.kbs, kb0 + p.kchunk);
+      x.kb0 = x.split * p.kchunk;
+      kb1 = min(p.kbs, x.kb0 + p.kchunk);
     }
-    const int nkb = kb1 - kb0;
-    if (nkb <= 0) continue;  // empty K range: D unchanged
-
-    if constexpr (KIND == KIND_CONTIGUOUS) {
-      // expert of this 128-aligned row block: the (single) valid id in it
-      barrier();  // previous tile's epilogue is done with sRowOk
-      if (tid == 0) sExpert = -1;
-      barrier();
-      for (int r = tid; r < BM; r += NW * 64) {
-        const int id = p.ctrl[m0 + r];
-        if (id >= 0 && id < p.groups) atomicMax(&sExpert, id);
-      }
-      barrier();
-      const int e = sExpert;
-      for (int r = tid; r < BM; r += NW * 64) sRowOk[r] = (p.ctrl[m0 + r] == e);
-      if (e < 0) continue;  // block-uniform: all padding
-      g = e;
+    x.nkb = kb1 - x.kb0;
+    x.live = x.nkb > 0;
+    return x;
+  };
+  // contiguous: the expert of a 128-aligned row block (the single valid id in
+  // it) and the rows that carry it, into parity buffer `par`.  All waves call
+  // this together (it synchronises the workgroup).
+  auto find_expert = [&](Tile& x, int par) {
+    barrier();  // every wave is done with the epilogue that last read `par`
+    if (tid == 0) sExpert[par] = -1;
+    barrier();
+    for (int r = tid; r < BM; r += NW * 64) {
+      const int id = p.ctrl[x.m0 + r];
+      if (id >= 0 && id < p.groups) atomicMax(&sExpert[par], id);
     }
+    barrier();
+    const int e = sExpert[par];
+    for (int r = tid; r < BM; r += NW * 64) sRowOk[par][r] = (p.ctrl[x.m0 + r] == e);
+    x.g = e;
+    x.live = e >= 0;
+  };
+  // the first live item at or after `t`; `t` moves past it
+  auto next_live = [&](int& t, int par) -> Tile {
+    Tile x = decode(t_end);
+    while (t < t_end) {
+      x = decode(t);
+      t += gridDim.x;
+      if constexpr (KIND == KIND_CONTIGUOUS)
+        if (x.live) find_expert(x, par);
+      if (x.live) break;
+    }
+    return x;
+  };
+  // DMA resources of a tile (a dead tile's read nothing)
+  struct Res {
+    Rsrc a, b, sa, sb;
+    int kb0, nkb;
+  };
+  auto make_res = [&](const Tile& x) -> Res {
+    const int bg = (KIND == KIND_KGROUPED) ? 0 : x.g;  // K-grouped: one B [N,T]
+    const int bcols = max(0, min(BN, p.n - x.n0));      // valid B rows (output columns)
+    const uint32_t on = x.live ? 1u : 0u;
+    Res r;
+    r.a = buffer_rsrc(p.a + x.a_row0 * (int64_t)p.lda, on * (uint32_t)x.rows * p.lda);
+    r.b = buffer_rsrc(p.b + ((int64_t)bg * p.n + x.n0) * (int64_t)p.lda, on * (uint32_t)bcols * p.lda);
+    r.sa = buffer_rsrc(p.sa + x.a_row0 * (int64_t)p.kbs, on * (uint32_t)x.rows * p.kbs * 4);
+    if constexpr (kRowScaleB) {
+      r.sb = buffer_rsrc(p.sb + (int64_t)x.n0 * p.kbs, on * (uint32_t)bcols * p.kbs * 4);
+    } else {
+      // only the 128-column blocks the tile touches
+      const int nb0 = x.n0 / kBK;
+      const int nbt = min(nb_rows - nb0, (BN + kBK - 1) / kBK);
+      r.sb = buffer_rsrc(p.sb + ((int64_t)x.g * nb_rows + nb0) * p.kbs, on * (uint32_t)max(nbt, 0) * p.kbs * 4);
+    }
+    r.kb0 = x.kb0;
+    r.nkb = x.live ? x.nkb : 0;
+    return r;
+  };
+  // Cross-tile prefetch: the DMAs of the next tile's first S-1 K blocks are
+  // issued during the current tile's last S-1 blocks, so a tile starts with
+  // its data in flight and its epilogue overlaps them.  Needs every tile to
+  // have at least S-1 K blocks (K-grouped ranges can be empty or short).
+  const int min_nkb = (kCanSplit && splits > 1) ? min(p.kchunk, p.kbs - (splits - 1) * p.kchunk) : p.kbs;
+  const bool xfer = (KIND != KIND_KGROUPED) && (min_nkb >= S - 1);
 
-    // ---- per-tile DMA addressing ----
-    // K-grouped weight gradients share one B [N,T]; the group picks the K range
-    const int bg = (KIND == KIND_KGROUPED) ? 0 : g;
-    const int bcols = min(BN, p.n - n0);  // valid B rows (output columns) of the tile
-    const Rsrc rsA = buffer_rsrc(p.a + a_row0 * (int64_t)p.lda, (uint32_t)rows * p.lda);
-    const Rsrc rsB = buffer_rsrc(p.b + ((int64_t)bg * p.n + n0) * (int64_t)p.lda, (uint32_t)bcols * p.lda);
-    const Rsrc rsSA = buffer_rsrc(p.sa + a_row0 * (int64_t)p.kbs, (uint32_t)rows * p.kbs * 4);
-    const Rsrc rsSB = kRowScaleB
-        ? buffer_rsrc(p.sb + (int64_t)n0 * p.kbs, (uint32_t)bcols * p.kbs * 4)
-        : buffer_rsrc(p.sb + ((int64_t)g * nb_rows + n0 / kBK) * p.kbs,
-                      (uint32_t)(nb_rows - n0 / kBK) * p.kbs * 4);
+  // bf16 output (or split-K partials) in whole 4-column vectors, offsets that
+  // fit the 32-bit buffer range: the epilogue's stores have a fixed count
+  constexpr int kStores = FM * FN;
+  constexpr bool kExactFits = (S - 2) * DMIN + kStores <= 63;  // vmcnt range
+  const bool exact_stores = kExactFits && (!kFp32Out || (kCanSplit && splits > 1)) && p.vec_out &&
+                            (int64_t)BM * p.n * 4 < 0x7fffffffLL;
+  bool stores_pending = false;  // the previous tile's epilogue stores may be in flight
+
+  int t_next = blockIdx.x;
+  int par = 0;
+  Tile cur = next_live(t_next, par);
+  int qbase = 0;        // ring stage of the current tile's first K block
+  bool first = true;
+  while (cur.live) {
+    Tile nxt = decode(t_end);
+    if (xfer) nxt = next_live(t_next, par ^ 1);
+    const Res rc = make_res(cur);
+    const Res rn = make_res(nxt);
+    const int g = cur.g, n0 = cur.n0, rows = cur.rows, nkb = cur.nkb, split = cur.split;
+    const int64_t out_row0 = cur.out_row0;
+
     // Lane l of operand piece q lands on LDS row 8*(wave + NW*q) + l/8, chunk
     // l%8.  Row steps between a wave's pieces are multiples of 16, so the
     // swizzle term is fixed per lane; only the row step changes with q.
@@ -306,22 +375,22 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     const uint32_t svoff = (uint32_t)lane * p.kbs * 4;
     const uint32_t sstep = 64u * p.kbs * 4;
 
-    // this wave's DMAs for K block kb0 + rel into ring stage `st`; only the
-    // pieces with index in [lo, hi) (A pieces first, then B, then scales), so
-    // a block's DMAs can be spread over the fragment groups of the previous
-    // block instead of stalling every wave at the same point.  Branch-free: a
-    // block past the tile's K range reads nothing (null resource) into a
-    // stage no later block of the tile uses; its resources have an empty
-    // range (they read zeros and touch no memory).
+    // this wave's DMAs for K block r.kb0 + rel of a tile into ring stage
+    // `st`; only the pieces with index in [lo, hi) (A pieces first, then B,
+    // then scales), so a block's DMAs can be spread over the fragment groups
+    // of the previous block instead of stalling every wave at the same point.
+    // Branch-free: a block past the tile's K range (or of a dead tile) reads
+    // nothing -- its resources have an empty range, read zeros and touch no
+    // memory -- into a stage no live block of the ring needs.
     constexpr int ND = QA + QB + QS;
-    auto issue = [&](int rel, int st, int lo, int hi) {
-      const bool live = rel < nkb;
-      const int kb = kb0 + rel;
+    auto issue = [&](const Res& r, int rel, int st, int lo, int hi) {
+      const bool live = rel < r.nkb;
+      const int kb = r.kb0 + rel;
       const uint32_t base = smem_lds + st * STAGE;
       const uint32_t koff = __builtin_amdgcn_readfirstlane(kb * kBK);
       const uint32_t skoff = __builtin_amdgcn_readfirstlane(kb * 4);
-      const v4i ra = at(rsA, koff, live);
-      const v4i rb = at(rsB, koff, live);
+      const v4i ra = at(r.a, koff, live);
+      const v4i rb = at(r.b, koff, live);
 #pragma unroll
       for (int q = 0; q < QA; ++q)
         if (q >= lo && q < hi) dma16(base + OFF_A + (wave + NW * q) * 1024, ra, voff0 + q * step);
@@ -337,16 +406,35 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
         // to an indexed stack array)
         const uint32_t f = (uint32_t)__builtin_amdgcn_readfirstlane(is_a ? 1 : 0);
         Rsrc sel;
-        sel.lo = rsSB.lo + (rsSA.lo - rsSB.lo) * f;
-        sel.hi = rsSB.hi + (rsSA.hi - rsSB.hi) * f;
-        sel.num = rsSB.num + (rsSA.num - rsSB.num) * f;
-        sel.flags = rsSA.flags;
+        sel.lo = r.sb.lo + (r.sa.lo - r.sb.lo) * f;
+        sel.hi = r.sb.hi + (r.sa.hi - r.sb.hi) * f;
+        sel.num = r.sb.num + (r.sa.num - r.sb.num) * f;
+        sel.flags = r.sa.flags;
         const v4i r4 = at(sel, skoff, real);
         const v4i rs = v4i{(int)__builtin_amdgcn_readfirstlane(r4[0]), (int)__builtin_amdgcn_readfirstlane(r4[1]),
                            (int)__builtin_amdgcn_readfirstlane(r4[2]), (int)__builtin_amdgcn_readfirstlane(r4[3])};
         const uint32_t lds = __builtin_amdgcn_readfirstlane(sp < PS ? base + OFF_SA + sp * 256 : smem_lds + S * STAGE);
         dma4(lds, rs, svoff + (uint32_t)(is_a ? sp : sp - PSA) * sstep);
       }
+    };
+    // the block S-1 ahead of the current tile's block `rel`: this tile's own,
+    // else (cross-tile prefetch) the next tile's, else a dead block
+    const int qs = qbase % S;
+    auto sel = [](uint32_t c, const Rsrc& x, const Rsrc& y) {  // c ? x : y, scalar arithmetic
+      return Rsrc{y.lo + (x.lo - y.lo) * c, y.hi + (x.hi - y.hi) * c, y.num + (x.num - y.num) * c, x.flags};
+    };
+    auto issue_ahead = [&](int rel, int lo, int hi) {
+      const int q = rel + S - 1;
+      const int st = (qs + q) % S;
+      const uint32_t c = (uint32_t)__builtin_amdgcn_readfirstlane(q < nkb ? 1 : 0);
+      Res r;
+      r.a = sel(c, rc.a, rn.a);
+      r.b = sel(c, rc.b, rn.b);
+      r.sa = sel(c, rc.sa, rn.sa);
+      r.sb = sel(c, rc.sb, rn.sb);
+      r.kb0 = c ? rc.kb0 : rn.kb0;
+      r.nkb = c ? rc.nkb : rn.nkb;
+      issue(r, c ? q : q - nkb, st, lo, hi);
     };
 
     v4f acc[FN][FM];
@@ -393,18 +481,28 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     // group's valid rows; the rotation then ends at fragment NOV-1).
     auto k_loop = [&](auto nov_c) {
     constexpr int NOV = decltype(nov_c)::value;
-      // prologue: the first S-1 K blocks in flight
+      // prologue: the first S-1 K blocks in flight (with cross-tile prefetch
+      // only for a workgroup's first tile; later tiles' were issued ahead)
+      if (first || !xfer) {
   #pragma unroll
-      for (int s = 0; s < S - 1; ++s)
-        if (s < nkb) issue(s, s, 0, ND);
+        for (int s = 0; s < S - 1; ++s)
+          if (s < nkb) issue(rc, s, (qs + s) % S, 0, ND);
+      }
 
   #pragma unroll 1
       for (int rel = 0; rel < nkb; ++rel) {
-        const int st = rel % S;
+        const int st = (qs + rel) % S;
         // this wave's DMAs for block `rel` are done once at most
-        // (blocks issued after it) x DMIN of its operations remain in flight
-        const int later = min(S - 2, nkb - 1 - rel);
-        if constexpr (S == 2) {
+        // (blocks issued after it) x DMIN of its operations remain in flight;
+        // with cross-tile prefetch S-2 blocks always follow (epilogue stores
+        // in between only make the wait stricter)
+        const int later = xfer ? S - 2 : min(S - 2, nkb - 1 - rel);
+        // the previous epilogue's kStores stores were issued after blocks
+        // 0..S-2 of this tile, so they too may stay in flight while waiting
+        // for those blocks
+        if (stores_pending && rel < S - 1) {
+          if constexpr (kExactFits) wait_vm<(S - 2) * DMIN + kStores>(); else wait_vm<0>();
+        } else if constexpr (S == 2) {
           wait_vm<0>();
         } else if constexpr (S == 3) {
           if (later >= 1) wait_vm<DMIN>(); else wait_vm<0>();
@@ -462,7 +560,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
           else
             fma4(acc_at(NOV - 1, r), pend[r], part[r]);
         };
-        if constexpr (NOV == 0) issue(rel + S - 1, (rel + S - 1) % S, 0, ND);  // no groups to spread over
+        if constexpr (NOV == 0) issue_ahead(rel, 0, ND);  // no groups to spread over
 
   #pragma unroll
         for (int o = 0; o < NOV; ++o) {
@@ -482,7 +580,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
           // half of the groups so they still land in time)
           constexpr int kSpread = NOV / 2 > 0 ? NOV / 2 : 1;
           if (o < kSpread)
-            issue(rel + S - 1, (rel + S - 1) % S, (o * ND) / kSpread, ((o + 1) * ND) / kSpread);
+            issue_ahead(rel, (o * ND) / kSpread, ((o + 1) * ND) / kSpread);
           promote(o, 0);
           cur = nxt;
           // keep each group's loads, MFMAs and FMAs together: no fragment
@@ -521,16 +619,54 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     } else {
       k_loop(std::integral_constant<int, NO>{});
     }
-    wait_vm<0>();  // padding DMAs of the last blocks have landed
-    barrier();     // all waves are done with the ring before the next tile refills it
+    if (!xfer) {
+      wait_vm<0>();  // dead DMAs of the last blocks have landed
+      barrier();     // all waves are done with the ring before the next prologue refills it
+    }
 
     // ---- epilogue ----
+    if (exact_stores) {
+      // One buffer store per fragment pair, issued whether or not its lanes
+      // are valid: a lane whose row or columns fall outside the output gets
+      // an offset past the resource's range and the store drops it.  The
+      // wave's store count is then fixed (FM * FN), so the next tile's first
+      // waits can leave exactly these stores in flight.
+      const bool part = kCanSplit && splits > 1;
+      const uint32_t esz = part ? 4u : 2u;
+      void* obase = part ? (void*)(p.ws + split * p.ws_stride + out_row0 * p.n)
+                         : (void*)(static_cast<uint16_t*>(p.out) + out_row0 * p.n);
+      const __amdgpu_buffer_rsrc_t ro =
+          __builtin_amdgcn_make_buffer_rsrc(obase, (short)0, (int)((uint32_t)BM * p.n * esz), 0x00020000);
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        const int ml = wm * WTM + 16 * j + l16;
+        bool row_ok;
+        if constexpr (KIND == KIND_CONTIGUOUS)
+          row_ok = sRowOk[par][ml] != 0;
+        else
+          row_ok = ml < rows;
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+          const int n = n0 + wn * WTN + 16 * i + 4 * lq;
+          const uint32_t off = (row_ok && n < p.n) ? ((uint32_t)ml * p.n + n) * esz : 0x80000000u;
+          if (part) {
+            // (bit-cast the whole vector: a bit-cast of one element of an
+            // ext_vector_type is miscompiled to element 0 by this clang)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, acc[i][j]), ro, off, 0, 0);
+          } else {
+            const uint32_t lo = (uint32_t)f32_to_bf16(acc[i][j][0]) | ((uint32_t)f32_to_bf16(acc[i][j][1]) << 16);
+            const uint32_t hi = (uint32_t)f32_to_bf16(acc[i][j][2]) | ((uint32_t)f32_to_bf16(acc[i][j][3]) << 16);
+            __builtin_amdgcn_raw_buffer_store_b64(v2i{(int)lo, (int)hi}, ro, off, 0, 0);
+          }
+        }
+      }
+    } else {
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
       const int ml = wm * WTM + 16 * j + l16;
       bool row_ok;
       if constexpr (KIND == KIND_CONTIGUOUS)
-        row_ok = sRowOk[ml] != 0;
+        row_ok = sRowOk[par][ml] != 0;
       else
         row_ok = ml < rows;
       if (!row_ok) continue;
@@ -584,27 +720,51 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
         }
       }
     }
+    }
+    stores_pending = xfer && exact_stores;
+
+    // ---- next tile ----
+    if (!xfer) nxt = next_live(t_next, par ^ 1);
+    qbase += nkb;
+    cur = nxt;
+    par ^= 1;
+    first = false;
   }
+  wait_vm<0>();  // no DMA (dead blocks included) outlives the workgroup
+}
+
+// Instances left out: the 256x256 tile with 2x4 waves needs more than the
+// register file for the fp32 read-modify-write epilogue of the weight-gradient
+// kinds (it would spill); those kinds use the 1x8 layout of that tile.
+constexpr bool excluded(int bm, int bn, int wm, int kind) {
+  return bm == 256 && bn == 256 && wm == 2 && (kind == KIND_WGRAD || kind == KIND_KGROUPED);
+}
+
+template <int BM, int BN, int WM, int WN, int S, int KIND>
+void launch_kind(dim3 g, dim3 b, hipStream_t stream, const Params& p) {
+  if constexpr (!excluded(BM, BN, WM, KIND))
+    hipLaunchKernelGGL((fp8_gemm_kernel<BM, BN, WM, WN, S, KIND>), g, b, 0, stream, p);
 }
 
 template <int BM, int BN, int WM, int WN, int S>
 hipError_t launch_shape(int kind, const Params& p, int grid, hipStream_t stream) {
   dim3 g(grid), b(WM * WN * 64);
+  if (excluded(BM, BN, WM, kind)) return hipErrorInvalidValue;
   switch (kind) {
     case KIND_DENSE:
-      hipLaunchKernelGGL((fp8_gemm_kernel<BM, BN, WM, WN, S, KIND_DENSE>), g, b, 0, stream, p);
+      launch_kind<BM, BN, WM, WN, S, KIND_DENSE>(g, b, stream, p);
       break;
     case KIND_CONTIGUOUS:
-      hipLaunchKernelGGL((fp8_gemm_kernel<BM, BN, WM, WN, S, KIND_CONTIGUOUS>), g, b, 0, stream, p);
+      launch_kind<BM, BN, WM, WN, S, KIND_CONTIGUOUS>(g, b, stream, p);
       break;
     case KIND_MASKED:
-      hipLaunchKernelGGL((fp8_gemm_kernel<BM, BN, WM, WN, S, KIND_MASKED>), g, b, 0, stream, p);
+      launch_kind<BM, BN, WM, WN, S, KIND_MASKED>(g, b, stream, p);
       break;
     case KIND_WGRAD:
-      hipLaunchKernelGGL((fp8_gemm_kernel<BM, BN, WM, WN, S, KIND_WGRAD>), g, b, 0, stream, p);
+      launch_kind<BM, BN, WM, WN, S, KIND_WGRAD>(g, b, stream, p);
       break;
     case KIND_KGROUPED:
-      hipLaunchKernelGGL((fp8_gemm_kernel<BM, BN, WM, WN, S, KIND_KGROUPED>), g, b, 0, stream, p);
+      launch_kind<BM, BN, WM, WN, S, KIND_KGROUPED>(g, b, stream, p);
       break;
     default:
       return hipErrorInvalidValue;
@@ -669,7 +829,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const Params p, int 
 bool has_instance(int kind, const TileShape& s) {
   if (kind < KIND_DENSE || kind > KIND_KGROUPED) return false;
 #define X(BM, BN, WM, WN, S) \
-  if (s.bm == BM && s.bn == BN && s.wm == WM && s.wn == WN) return true;
+  if (s.bm == BM && s.bn == BN && s.wm == WM && s.wn == WN) return !excluded(BM, BN, WM, kind);
   DG_SHAPES(X)
 #undef X
   return false;
