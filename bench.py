@@ -13,6 +13,16 @@ the "dominant kernel" whose roofline fraction is reported.  The CPU oracle is
 timed on a bounded sample of the same workload's outputs (`cpu_baseline`).
 Other workloads (contiguous, masked, wgrad, k_grouped_wgrad, small) print a
 line of the same form.  Exactly one JSON line goes to stdout.
+
+Before the W warmup steps the step runs untimed for at least half a second so
+the GPU clock has settled when timing starts.  `roofline.traffic` is the
+dominant GEMM's HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE
+counters (each scaled by what the counter reads for a plain device copy of
+known size), stored in profiles/; it is reported only while the kernel sources
+hash to the version the counters were taken on, else null.
+
+    python bench.py --only NAME[,NAME]   time only the named GEMMs (for counters)
+    python bench.py --copy-calibration   run a plain 1 GiB device-to-device copy
 """
 from __future__ import annotations
 
@@ -35,6 +45,49 @@ RIDGE = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "moe_grouped_gemm_x128_amd", "csrc", f)
+                  for f in ("dg_kernels.hip", "dg_api.hip", "dg_kernel.h")]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name):
+    """HBM bytes per launch of GEMM `name` from the committed counter summary
+    (the json block of profiles/hbm_traffic.md), or None if there is none for
+    it or the kernel sources changed since the counters were taken."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+        block = text.split("```json", 1)[1].split("```", 1)[0]
+        data = json.loads(block)
+    except (OSError, IndexError, ValueError):
+        return None
+    if data.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    entry = data.get("gemms", {}).get(name)
+    return None if entry is None else entry.get("hbm_bytes_per_launch")
+
+
+def copy_calibration():
+    """A plain device-to-device copy of 1 GiB, three times (its FETCH_SIZE and
+    WRITE_SIZE per dispatch calibrate the counters against known bytes)."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "copies": 3}), flush=True)
 
 
 class Call:
@@ -160,8 +213,13 @@ def build_wgrad(kgrouped=False):
 
 # --------------------------------------------------------------- timing ---
 
-def time_steps(calls, steps, warmup):
+def time_steps(calls, steps, warmup, settle_s=0.5):
     import torch
+    t = time.perf_counter()
+    while time.perf_counter() - t < settle_s:  # let the clock settle (untimed)
+        for c in calls:
+            c.fn()
+        torch.cuda.synchronize()
     for _ in range(warmup):
         for c in calls:
             c.fn()
@@ -224,6 +282,9 @@ def main():
                     choices=["dense", "small", "contiguous", "masked", "wgrad", "k_grouped_wgrad"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle-seconds", type=float, default=0.5, help="untimed run before the warmup steps")
+    ap.add_argument("--only", default="", help="comma-separated GEMM names to time (others skipped)")
+    ap.add_argument("--copy-calibration", action="store_true", help="run the counter-calibration copy and exit")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -238,9 +299,17 @@ def main():
     builders = {"dense": build_dense, "small": lambda: build_dense(small=True),
                 "contiguous": build_contiguous, "masked": build_masked,
                 "wgrad": build_wgrad, "k_grouped_wgrad": lambda: build_wgrad(kgrouped=True)}
+    if args.copy_calibration:
+        copy_calibration()
+        return
     calls, config = builders[args.workload]()
+    if args.only:
+        keep = set(args.only.split(","))
+        calls = [c for c in calls if c.name in keep]
+        assert calls, f"--only matched none of the workload's GEMMs"
+        config = dict(config, only=sorted(keep))
     log(f"{len(calls)} GEMMs per step; timing {args.steps} steps after {args.warmup} warmup")
-    total_ms, per_ms = time_steps(calls, args.steps, args.warmup)
+    total_ms, per_ms = time_steps(calls, args.steps, args.warmup, args.settle_seconds)
     ms_per_step = total_ms / args.steps
     step_flops = sum(c.flops for c in calls)
 
@@ -259,7 +328,7 @@ def main():
     else:
         achieved, peak, unit = dc.bytes / (dms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
     roofline = {"bound": dc.bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4), "traffic": None, "kernel": dc.name,
+                "frac": round(achieved / peak, 4), "traffic": measured_traffic(dc.name), "kernel": dc.name,
                 "flops_per_launch": dc.flops, "bytes_per_launch": dc.bytes, "avg_us": round(dms * 1e3, 2)}
 
     cpu = None
