@@ -67,8 +67,9 @@ constexpr int kSplitTarget = 4;
 constexpr int kSplitMinBlocks = 12;
 constexpr size_t kMaxWorkspaceBytes = size_t(256) << 20;  // split-K partials per stream
 
-int choose_splits(int kind, long tiles, int num_cus, int kbs) {
+int choose_splits(int kind, int rows, long tiles, int num_cus, int kbs) {
   if (kind != DG_KIND_DENSE && kind != DG_KIND_MASKED) return 1;
+  if (rows > 256) return 1;  // large M: the extra pass costs more than the idle CUs (measured)
   if (tiles * 10 >= num_cus * 7L) return 1;  // enough tiles already
   long s = (num_cus + tiles - 1) / tiles;
   if (s > kSplitTarget) s = kSplitTarget;
@@ -122,6 +123,8 @@ dg::TileShape heuristic(int kind, int rows, int n, int k, int groups, int num_cu
   }
   static const Candidate cands[] = {
       // efficiencies measured relative to the 256x256 tile on full waves
+      // (the 256x224 tile, 4x2 waves, balances N=7168 over the CUs but ran
+      // slower per tile than 256x256 by more than it gains: not a candidate)
       {{256, 256, 2, 4}, 1.00}, {{256, 256, 1, 8}, 0.98}, {{256, 128, 2, 2}, 0.85}, {{128, 128, 2, 2}, 0.70},
       {{128, 64, 2, 2}, 0.50},  {{64, 128, 1, 4}, 0.50},  {{64, 64, 1, 4}, 0.35},
   };
@@ -167,7 +170,7 @@ dg_status plan(int kind, int rows, int n, int k, int groups, int num_cus, bool a
   p.tiles = (int)tiles;
   const long slots = (long)num_cus * occupancy(kind, s);
   const int kbs = k / 128;
-  int splits = allow_split ? choose_splits(kind, tiles, num_cus, kbs) : 1;
+  int splits = allow_split ? choose_splits(kind, rows, tiles, num_cus, kbs) : 1;
   if (const char* e = std::getenv("DG_FORCE_SPLITS"))
     if (allow_split && (kind == DG_KIND_DENSE || kind == DG_KIND_MASKED)) splits = std::atoi(e);
   if (splits < 1) splits = 1;

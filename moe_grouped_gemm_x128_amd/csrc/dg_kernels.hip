@@ -181,13 +181,16 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   // every wave) and scale pieces w, w+NW, ... (some waves one fewer).
   constexpr int PA = BM / 8, PB = BN / 8, PSA = SA_N / 64, PSB = SB_N / 64;
   constexpr int PS = PSA + PSB;
-  constexpr int QA = PA / NW, QB = PB / NW, QS = (PS + NW - 1) / NW;
+  // (a block width that is not a multiple of 8 * NW rows, e.g. 224, leaves
+  // some waves one piece short: they issue a dead piece into the sink instead)
+  constexpr int QA = (PA + NW - 1) / NW, QB = (PB + NW - 1) / NW, QS = (PS + NW - 1) / NW;
   // every wave issues QA + QB + QS DMAs per stage: scale pieces past PS are
   // padding that reads nothing and lands in a sink slot after the ring
   constexpr int DMIN = QA + QB + QS;
-  static_assert(PA % NW == 0 && PB % NW == 0, "operand pieces split evenly over the waves");
+  static_assert(PA % NW == 0, "A pieces split evenly over the waves");
+  static_assert(BN % 16 == 0, "whole 16-column fragments");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE + 256];  // + padding-DMA sink
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE + 1024];  // + padding-DMA sink
   // contiguous: rows of a tile that carry its expert, double-buffered by tile
   // parity (the next tile is looked up while the current one is computed)
   __shared__ int sRowOk[2][KIND == KIND_CONTIGUOUS ? BM : 1];
@@ -330,7 +333,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     } else {
       // only the 128-column blocks the tile touches
       const int nb0 = x.n0 / kBK;
-      const int nbt = min(nb_rows - nb0, (BN + kBK - 1) / kBK);
+      const int nbt = min(nb_rows - nb0, (x.n0 - nb0 * kBK + BN + kBK - 1) / kBK);  // a tile may straddle blocks
       r.sb = buffer_rsrc(p.sb + ((int64_t)x.g * nb_rows + nb0) * p.kbs, on * (uint32_t)max(nbt, 0) * p.kbs * 4);
     }
     r.kb0 = x.kb0;
@@ -395,8 +398,20 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
       for (int q = 0; q < QA; ++q)
         if (q >= lo && q < hi) dma16(base + OFF_A + (wave + NW * q) * 1024, ra, voff0 + q * step);
 #pragma unroll
-      for (int q = 0; q < QB; ++q)
-        if (QA + q >= lo && QA + q < hi) dma16(base + OFF_B + (wave + NW * q) * 1024, rb, voff0 + q * step);
+      for (int q = 0; q < QB; ++q) {
+        if (QA + q < lo || QA + q >= hi) continue;
+        const int pi = wave + NW * q;
+        if constexpr (PB % NW == 0) {
+          dma16(base + OFF_B + pi * 1024, rb, voff0 + q * step);
+        } else {
+          // past the last B piece: read nothing into the sink
+          const bool real = pi < PB;
+          v4i rq = rb;
+          rq[2] = real ? rb[2] : 0;
+          dma16(__builtin_amdgcn_readfirstlane(real ? base + OFF_B + pi * 1024 : smem_lds + S * STAGE), rq,
+                voff0 + q * step);
+        }
+      }
 #pragma unroll
       for (int q = 0; q < QS; ++q) {
         if (QA + QB + q < lo || QA + QB + q >= hi) continue;
@@ -813,6 +828,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const Params p, int 
 // (BM, BN, waves along M, waves along N, LDS ring stages)
 #define DG_SHAPES(X)      \
   X(256, 256, 1, 8, 2)    \
+  X(256, 224, 4, 2, 2)    \
   X(256, 128, 1, 8, 3)    \
   X(256, 64, 1, 4, 3)     \
   X(256, 128, 1, 4, 3)    \
@@ -843,7 +859,7 @@ int lds_bytes_of(int kind, const TileShape& s) {
   const int sb_n = row_sb ? ((s.bn + 63) / 64) * 64 : 64;
   const int stage = (s.bm + s.bn) * kBK + 4 * (sa_n + sb_n);
 #define X(BM, BN, WM, WN, S) \
-  if (s.bm == BM && s.bn == BN && s.wm == WM && s.wn == WN) return S * stage + 4 * BM + 64;
+  if (s.bm == BM && s.bn == BN && s.wm == WM && s.wn == WN) return S * stage + 1024 + 8 * BM + 64;
   DG_SHAPES(X)
 #undef X
   return 0;

@@ -18,7 +18,8 @@ from tests.parity import (SENTINEL_BF16, bf16_bits, bits_to_f64, check_close, de
 
 pytestmark = pytest.mark.gpu
 
-TILES = [None, "256x128x2x2", "256x256x2x4", "128x128x2x2", "128x64x2x2", "64x128x1x4", "64x64x1x4", "64x32x2x2"]
+TILES = [None, "256x128x2x2", "256x256x2x4", "256x224x4x2", "128x128x2x2", "128x64x2x2", "64x128x1x4", "64x64x1x4",
+         "64x32x2x2"]
 
 
 @pytest.fixture(scope="module")
@@ -102,7 +103,8 @@ def test_contiguous_small(dg, force_tile, tile):
     check_close(bits_to_f64(got[valid]), bits_to_f64(ref[valid]), "contiguous small")
 
 
-@pytest.mark.parametrize("tile", [None, "256x256x1x8", "256x128x1x4", "256x128x2x2", "128x128x2x2", "64x32x2x2"])
+@pytest.mark.parametrize("tile", [None, "256x256x1x8", "256x224x4x2", "256x128x1x4", "256x128x2x2", "128x128x2x2",
+                                  "64x32x2x2"])
 def test_masked_small(dg, force_tile, tile):
     g, m_max, n, k = 5, 96, 260, 256
     mm = np.array([0, 1, 96, 200, 50], np.int32)  # empty, one row, full, clamped, partial
@@ -119,7 +121,7 @@ def test_masked_small(dg, force_tile, tile):
     check_close(bits_to_f64(got[rows]), bits_to_f64(ref[rows]), "masked small")
 
 
-@pytest.mark.parametrize("tile", [None, "256x128x2x2", "128x128x2x2", "64x128x1x4"])
+@pytest.mark.parametrize("tile", [None, "256x224x4x2", "256x128x2x2", "128x128x2x2", "64x128x1x4"])
 def test_wgrad_small(dg, force_tile, tile):
     w = inputs.make_wgrad(200, 130, [384], seed=inputs.SEED_BASE + 4)
     force_tile(tile)
@@ -188,7 +190,7 @@ def force_splits():
     os.environ.pop("DG_FORCE_SPLITS", None)
 
 
-@pytest.mark.parametrize("tile", ["64x32x2x2", "128x128x2x2", "256x256x1x8"])
+@pytest.mark.parametrize("tile", ["64x32x2x2", "128x128x2x2", "256x256x1x8", "256x224x4x2"])
 @pytest.mark.parametrize("splits", [2, 3, 4, 10])
 @pytest.mark.parametrize("m,n,k", [(70, 300, 1280), (1, 130, 512), (200, 2112, 1792)])
 def test_dense_split_k(dg, force_tile, force_splits, m, n, k, tile, splits):
