@@ -114,7 +114,6 @@ dg::TileShape heuristic(int kind, int rows, int n, int k, int groups, int num_cu
     const long need = long_k && (kind == DG_KIND_DENSE) ? (num_cus * 7L) / (10L * kSplitTarget)
                                                          : (num_cus * 7L) / 10L;
     for (const auto& c : cands) {
-      if (kind == DG_KIND_CONTIGUOUS && 128 % c.bm != 0) continue;
       if (!dg::has_instance(kind, c)) continue;
       const long tiles = (long)groups * ceil_div(rows, c.bm) * ceil_div(n, c.bn);
       if (tiles >= need) return c;
@@ -131,7 +130,6 @@ dg::TileShape heuristic(int kind, int rows, int n, int k, int groups, int num_cu
   double best = 1e300;
   dg::TileShape pick{128, 128, 2, 2};
   for (const auto& c : cands) {
-    if (kind == DG_KIND_CONTIGUOUS && 128 % c.s.bm != 0) continue;
     if (!dg::has_instance(kind, c.s)) continue;
     const long tiles = (long)groups * ceil_div(rows, c.s.bm) * ceil_div(n, c.s.bn);
     const long slots = (long)num_cus * occupancy(kind, c.s);
@@ -162,7 +160,6 @@ dg_status plan(int kind, int rows, int n, int k, int groups, int num_cus, bool a
   dg::TileShape s;
   if (!parse_forced(&s)) s = heuristic(kind, rows, n, k, groups, num_cus, allow_split);
   if (!dg::has_instance(kind, s)) return DG_ERROR_UNSUPPORTED;
-  if (kind == DG_KIND_CONTIGUOUS && 128 % s.bm != 0) return DG_ERROR_UNSUPPORTED;
   p.tiles_m = ceil_div(rows, s.bm);
   p.tiles_n = ceil_div(n, s.bn);
   const long tiles = (long)groups * p.tiles_m * p.tiles_n;

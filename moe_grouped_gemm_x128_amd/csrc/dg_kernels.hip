@@ -194,7 +194,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   // contiguous: rows of a tile that carry its expert, double-buffered by tile
   // parity (the next tile is looked up while the current one is computed)
   __shared__ int sRowOk[2][KIND == KIND_CONTIGUOUS ? BM : 1];
-  __shared__ int sExpert[2];
+  __shared__ int sExpert[2][2];  // per parity: experts of the tile's two 128-row blocks
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -286,31 +286,61 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     x.live = x.nkb > 0;
     return x;
   };
-  // contiguous: the expert of a 128-aligned row block (the single valid id in
-  // it) and the rows that carry it, into parity buffer `par`.  All waves call
-  // this together (it synchronises the workgroup).
-  auto find_expert = [&](Tile& x, int par) {
-    barrier();  // every wave is done with the epilogue that last read `par`
-    if (tid == 0) sExpert[par] = -1;
+  // contiguous: which of the tile's rows carry expert `e`, into parity
+  // buffer `par`.  All waves call this together (it synchronises the
+  // workgroup); the first barrier waits for the epilogue that last read `par`.
+  // Only rows of a block whose expert is `e` qualify (lo / hi: the first /
+  // second 128-row block), so a stray id of another expert inside a block is
+  // skipped whatever the tile height.
+  auto mark_rows = [&](const Tile& x, int par, int e, bool lo, bool hi) {
     barrier();
-    for (int r = tid; r < BM; r += NW * 64) {
+    for (int r = tid; r < BM; r += NW * 64)
+      sRowOk[par][r] = r < x.rows && (r < 128 ? lo : hi) && p.ctrl[x.m0 + r] == e;
+  };
+  // contiguous: the expert of each 128-aligned row block of the tile (the
+  // single valid id in it).  A 256-row tile whose two blocks belong to
+  // different experts is computed twice, once per expert (the second pass is
+  // queued in `pend`); each pass stores only its expert's rows.
+  int pend_t = -1, pend_g = -1;  // item and expert of a queued second pass
+  auto find_expert = [&](Tile& x, int t, int par) {
+    barrier();  // every wave is done with the epilogue that last read `par`
+    if (tid < 2) sExpert[par][tid] = -1;
+    barrier();
+    for (int r = tid; r < x.rows; r += NW * 64) {
       const int id = p.ctrl[x.m0 + r];
-      if (id >= 0 && id < p.groups) atomicMax(&sExpert[par], id);
+      if (id >= 0 && id < p.groups) atomicMax(&sExpert[par][r >= 128 ? 1 : 0], id);
     }
     barrier();
-    const int e = sExpert[par];
-    for (int r = tid; r < BM; r += NW * 64) sRowOk[par][r] = (p.ctrl[x.m0 + r] == e);
+    // (read from LDS: made wave-uniform so the loop that depends on it stays scalar)
+    const int e0 = __builtin_amdgcn_readfirstlane(sExpert[par][0]);
+    const int e1 = __builtin_amdgcn_readfirstlane(sExpert[par][1]);
+    const int e = e0 >= 0 ? e0 : e1;
+    mark_rows(x, par, e, e0 == e, e1 == e);
     x.g = e;
     x.live = e >= 0;
+    if (e0 >= 0 && e1 >= 0 && e1 != e0) {
+      pend_t = t;
+      pend_g = e1;
+    }
   };
-  // the first live item at or after `t`; `t` moves past it
+  // the first live item at or after `t` (or a queued second pass); `t`
+  // moves past it
   auto next_live = [&](int& t, int par) -> Tile {
+    if constexpr (KIND == KIND_CONTIGUOUS) {
+      if (pend_t >= 0) {
+        Tile x = decode(pend_t);
+        x.g = pend_g;
+        pend_t = -1;
+        mark_rows(x, par, x.g, false, true);  // the second block's expert
+        return x;
+      }
+    }
     Tile x = decode(t_end);
     while (t < t_end) {
       x = decode(t);
-      t += gridDim.x;
       if constexpr (KIND == KIND_CONTIGUOUS)
-        if (x.live) find_expert(x, par);
+        if (x.live) find_expert(x, t, par);
+      t += gridDim.x;
       if (x.live) break;
     }
     return x;
@@ -434,7 +464,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     };
     // the block S-1 ahead of the current tile's block `rel`: this tile's own,
     // else (cross-tile prefetch) the next tile's, else a dead block
-    const int qs = qbase % S;
+    const int qs = __builtin_amdgcn_readfirstlane(qbase % S);  // uniform: keep the ring stage scalar
     auto sel = [](uint32_t c, const Rsrc& x, const Rsrc& y) {  // c ? x : y, scalar arithmetic
       return Rsrc{y.lo + (x.lo - y.lo) * c, y.hi + (x.hi - y.hi) * c, y.num + (x.num - y.num) * c, x.flags};
     };

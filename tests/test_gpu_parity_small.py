@@ -256,3 +256,30 @@ def test_split_k_under_graph_capture(dg):
         g.replay()
         torch.cuda.synchronize()
         check_close(bits_to_f64(bf16_bits(out)), bits_to_f64(ref), f"graph replay {rep}")
+
+
+@pytest.mark.parametrize("tile", [None, "256x256x2x4", "256x256x1x8", "256x128x2x2", "128x128x2x2"])
+def test_contiguous_tall_tiles(dg, force_tile, tile):
+    """256-row tiles span two 128-row blocks: a pair with one expert, a pair
+    whose blocks belong to different experts (computed in two passes), a
+    padding block next to an expert, a partial block, and a last tile of only
+    128 rows (M_total not a multiple of 256)."""
+    c = inputs.make_contiguous(4, 384, 270, 384, seed=inputs.SEED_BASE + 53, max_pad=0)
+    m_total = 9 * 128
+    blocks = [0, 0, 0, 1, -1, 2, 2, 3, 1]          # expert of each 128-row block
+    valid = [128, 128, 100, 128, 0, 128, 128, 50, 77]  # valid rows at the start of each block
+    ids = np.full(m_total, -1, np.int32)
+    for i, (e, v) in enumerate(zip(blocks, valid)):
+        ids[i * 128:i * 128 + v] = e
+    a, sa = np.ascontiguousarray(c.a[:m_total]), np.ascontiguousarray(c.sa[:m_total])
+    force_tile(tile)
+    out = sentinel_bf16((m_total, c.n))
+    say(f"contiguous tall tiles tile={tile}")
+    dg.dg_grouped_fp8_contiguous(dev(a), dev(sa), dev(c.b), dev(c.sb), out, dev(ids))
+    torch.cuda.synchronize()
+    got = bf16_bits(out)
+    ref, _ = oracle.grouped_contiguous(a, sa, c.b, c.sb, ids, np.full((m_total, c.n), SENTINEL_BF16, np.uint16))
+    ok = ids >= 0
+    assert np.all(got[~ok] == SENTINEL_BF16), "padding rows were written"
+    assert not np.any(got[ok] == SENTINEL_BF16), "valid rows left unwritten"
+    check_close(bits_to_f64(got[ok]), bits_to_f64(ref[ok]), f"contiguous tall {tile}")
