@@ -395,12 +395,15 @@ dg_status dg_k_grouped_wgrad_fp8_nt(const void* a, const float* sa, const void* 
     return DG_ERROR_UNSUPPORTED;
   dg::Params p = base_params();
   long total = 0;
+  int min_blocks = 0x7fffffff;
   for (int g = 0; g < num_groups; ++g) {
     if (ks_host[g] < 0) return DG_ERROR_INVALID_VALUE;
     if (ks_host[g] % 128 != 0) return DG_ERROR_UNSUPPORTED;
     p.kb_begin[g] = (int)(total / 128);
     total += ks_host[g];
+    if (ks_host[g] > 0 && ks_host[g] / 128 < min_blocks) min_blocks = ks_host[g] / 128;
   }
+  p.kg_min_blocks = min_blocks;
   if (total > 0x7fffffffL) return DG_ERROR_UNSUPPORTED;
   p.kb_begin[num_groups] = (int)(total / 128);
   if (total == 0) return DG_SUCCESS;  // no tokens: every D[g] stays as it is

@@ -42,6 +42,7 @@ struct Params {
   int kchunk;            // K blocks per split
   float* ws;             // fp32 partials [splits][rows of all groups][n]
   int64_t ws_stride;     // floats per split
+  int kg_min_blocks;     // K-grouped: fewest K blocks of any non-empty group
   int kb_begin[kMaxKGroups + 1];  // K-grouped: first 128-block of each group
 };
 

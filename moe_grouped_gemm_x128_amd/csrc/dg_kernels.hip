@@ -257,10 +257,11 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
       x.a_row0 = (int64_t)g * p.m + x.m0;
       x.out_row0 = x.a_row0;
     } else if constexpr (KIND == KIND_KGROUPED) {
-      const int per_g = p.tiles_m * p.tiles_n;
-      const int g = L / per_g;
+      // the group is the fastest index: every XCD's contiguous run of items
+      // holds all groups alike, whose K ranges (work per tile) differ
+      const int g = L % p.groups;
       int tm, tn;
-      raster(L - g * per_g, p.tiles_m, p.tiles_n, tm, tn);
+      raster(L / p.groups, p.tiles_m, p.tiles_n, tm, tn);
       x.g = g;
       x.m0 = tm * BM;
       x.n0 = tn * BN;
@@ -374,13 +375,18 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   // issued during the current tile's last S-1 blocks, so a tile starts with
   // its data in flight and its epilogue overlaps them.  Needs every tile to
   // have at least S-1 K blocks (K-grouped ranges can be empty or short).
-  const int min_nkb = (kCanSplit && splits > 1) ? min(p.kchunk, p.kbs - (splits - 1) * p.kchunk) : p.kbs;
-  const bool xfer = (KIND != KIND_KGROUPED) && (min_nkb >= S - 1);
+  // (K-grouped: groups with no tokens have no live tiles and are never in
+  // the ring, so the shortest non-empty group decides)
+  const int min_nkb = (KIND == KIND_KGROUPED)       ? p.kg_min_blocks
+                      : (kCanSplit && splits > 1) ? min(p.kchunk, p.kbs - (splits - 1) * p.kchunk)
+                                                  : p.kbs;
+  const bool xfer = min_nkb >= S - 1;
 
   // bf16 output (or split-K partials) in whole 4-column vectors, offsets that
   // fit the 32-bit buffer range: the epilogue's stores have a fixed count
   constexpr int kStores = FM * FN;
   constexpr bool kExactFits = (S - 2) * DMIN + kStores <= 63;  // vmcnt range
+  // (not for the fp32 D kinds: their row-scale registers leave no room for it)
   const bool exact_stores = kExactFits && (!kFp32Out || (kCanSplit && splits > 1)) && p.vec_out &&
                             (int64_t)BM * p.n * 4 < 0x7fffffffLL;
   bool stores_pending = false;  // the previous tile's epilogue stores may be in flight
@@ -487,6 +493,29 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     for (int i = 0; i < FN; ++i)
 #pragma unroll
       for (int j = 0; j < FM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    if constexpr (kFp32Out) {
+      // D += ...: the accumulators start from D, loaded here so the loads
+      // overlap the tile's first K blocks and the epilogue only stores
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        const int ml = wm * WTM + 16 * j + l16;
+        if (ml >= rows) continue;
+        const float* d = static_cast<const float*>(p.out) + (out_row0 + ml) * p.n;
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+          const int n = n0 + wn * WTN + 16 * i + 4 * lq;
+          if (n >= p.n) continue;
+          if (p.vec_out && n + 3 < p.n) {
+            const float4 v = *reinterpret_cast<const float4*>(d + n);
+            acc[i][j] = v4f{v.x, v.y, v.z, v.w};
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (n + r < p.n) acc[i][j][r] = d[n + r];
+          }
+        }
+      }
+    }
 
     // Fragments: NR resident ones are read once per K block, NO streamed
     // ones one at a time.  MFMA M(o, r) multiplies streamed fragment o by
@@ -676,8 +705,10 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
       // an offset past the resource's range and the store drops it.  The
       // wave's store count is then fixed (FM * FN), so the next tile's first
       // waits can leave exactly these stores in flight.
+      // fp32 split-K partials, else bf16 C
       const bool part = kCanSplit && splits > 1;
-      const uint32_t esz = part ? 4u : 2u;
+      const bool f32 = part;
+      const uint32_t esz = f32 ? 4u : 2u;
       void* obase = part ? (void*)(p.ws + split * p.ws_stride + out_row0 * p.n)
                          : (void*)(static_cast<uint16_t*>(p.out) + out_row0 * p.n);
       const __amdgpu_buffer_rsrc_t ro =
@@ -694,7 +725,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
         for (int i = 0; i < FN; ++i) {
           const int n = n0 + wn * WTN + 16 * i + 4 * lq;
           const uint32_t off = (row_ok && n < p.n) ? ((uint32_t)ml * p.n + n) * esz : 0x80000000u;
-          if (part) {
+          if (f32) {
             // (bit-cast the whole vector: a bit-cast of one element of an
             // ext_vector_type is miscompiled to element 0 by this clang)
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, acc[i][j]), ro, off, 0, 0);
@@ -740,16 +771,11 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
         if constexpr (kFp32Out) {
           float* d = static_cast<float*>(p.out) + orow * p.n + n;
           if (p.vec_out && n + 3 < p.n) {
-            float4 v = *reinterpret_cast<float4*>(d);
-            v.x += acc[i][j][0];
-            v.y += acc[i][j][1];
-            v.z += acc[i][j][2];
-            v.w += acc[i][j][3];
-            *reinterpret_cast<float4*>(d) = v;
+            *reinterpret_cast<float4*>(d) = float4{acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
           } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              if (n + r < p.n) d[r] += acc[i][j][r];
+              if (n + r < p.n) d[r] = acc[i][j][r];  // acc started from D
           }
         } else {
           uint16_t* c = static_cast<uint16_t*>(p.out) + orow * p.n + n;
