@@ -134,6 +134,8 @@ typedef struct {
   int tiles;        /* tile count (an upper bound for the masked layout)     */
   int grid;         /* persistent workgroups launched                        */
   int k_splits;     /* workgroups sharing one output tile along K (1 = none) */
+  int kernel;       /* 0: general kernel; 1: masked decode kernel streaming B
+                       into registers (block 256x256, 8 waves)            */
 } dg_tile_config;
 
 dg_status dg_select_config(int kind, int m, int n, int k, int num_groups, int num_cus,

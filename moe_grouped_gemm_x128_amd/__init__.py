@@ -45,7 +45,7 @@ _lib.dg_version.restype = ctypes.c_int
 class TileConfig(ctypes.Structure):
     _fields_ = [("block_m", ctypes.c_int), ("block_n", ctypes.c_int), ("waves_m", ctypes.c_int),
                 ("waves_n", ctypes.c_int), ("tiles", ctypes.c_int), ("grid", ctypes.c_int),
-                ("k_splits", ctypes.c_int)]
+                ("k_splits", ctypes.c_int), ("kernel", ctypes.c_int)]
 
 
 _lib.dg_select_config.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(TileConfig)]

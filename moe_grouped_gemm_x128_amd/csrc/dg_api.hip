@@ -151,21 +151,41 @@ dg::TileShape heuristic(int kind, int rows, int n, int k, int groups, int num_cu
 struct Launch {
   dg::TileShape shape;
   int grid;
+  bool bdirect;  // masked layout: the B-in-registers decode kernel
 };
+
+// Masked layout: the decode kernel that streams B into registers (256x256
+// tiles, 8 waves, K blocks in pairs).  Measured faster than the general
+// kernel when its work items fill the CUs (G=16: 118 vs 138 us for N=4096,
+// K=7168; G=4 with four K splits: 47 vs 50 us), slower when they cannot.
+// DG_MASKED_BDIRECT=0/1 overrides the choice.
+int choose_splits(int kind, int rows, long tiles, int num_cus, int kbs);
+bool use_bdirect(int kind, bool forced_tile, int rows, int n, int k, int groups, int num_cus, bool allow_split) {
+  if (kind != DG_KIND_MASKED || (k / 128) % 2 != 0) return false;
+  if (const char* e = std::getenv("DG_MASKED_BDIRECT")) return e[0] == '1';
+  if (forced_tile) return false;
+  const long tiles = (long)groups * ceil_div(rows, 256) * ceil_div(n, 256);
+  const int splits = allow_split ? choose_splits(kind, rows, tiles, num_cus, k / 128) : 1;
+  return tiles * splits * 10 >= 9L * num_cus;
+}
 
 // `allow_split`: split-K needs a temporary workspace, so it is planned only
 // for calls that may allocate (not under stream capture).
 dg_status plan(int kind, int rows, int n, int k, int groups, int num_cus, bool allow_split, dg::Params& p,
                Launch& l) {
   dg::TileShape s;
-  if (!parse_forced(&s)) s = heuristic(kind, rows, n, k, groups, num_cus, allow_split);
+  const bool forced = parse_forced(&s);
+  if (!forced) s = heuristic(kind, rows, n, k, groups, num_cus, allow_split);
+  // (the decode kernel takes K blocks in pairs: an even count per work item)
+  l.bdirect = use_bdirect(kind, forced, rows, n, k, groups, num_cus, allow_split);
+  if (l.bdirect) s = dg::TileShape{256, 256, 1, 8};
   if (!dg::has_instance(kind, s)) return DG_ERROR_UNSUPPORTED;
   p.tiles_m = ceil_div(rows, s.bm);
   p.tiles_n = ceil_div(n, s.bn);
   const long tiles = (long)groups * p.tiles_m * p.tiles_n;
   if (tiles > 0x7fffffffL / kMaxSplits) return DG_ERROR_UNSUPPORTED;
   p.tiles = (int)tiles;
-  const long slots = (long)num_cus * occupancy(kind, s);
+  const long slots = l.bdirect ? (long)num_cus : (long)num_cus * occupancy(kind, s);
   const int kbs = k / 128;
   int splits = allow_split ? choose_splits(kind, rows, tiles, num_cus, kbs) : 1;
   if (const char* e = std::getenv("DG_FORCE_SPLITS"))
@@ -176,7 +196,8 @@ dg_status plan(int kind, int rows, int n, int k, int groups, int num_cus, bool a
   const double split_bytes = 4.0 * groups * rows * (double)n;  // one fp32 partial of every output
   while (splits > 1 && splits * split_bytes > (double)kMaxWorkspaceBytes) --splits;
   // equal chunks with no empty split: every partial the reduction reads is written
-  const int chunk = ceil_div(kbs, splits);
+  int chunk = ceil_div(kbs, splits);
+  if (l.bdirect && chunk % 2) ++chunk;  // K blocks in pairs (kbs is even)
   splits = ceil_div(kbs, chunk);
   p.splits = splits;
   p.kchunk = chunk;
@@ -268,15 +289,18 @@ dg_status run(int kind, dg::Params& p, int rows, int n, int k, int groups, hipSt
   Launch l;
   dg_status st = plan(kind, rows, n, k, groups, cus, may_split, p, l);
   if (st != DG_SUCCESS) return st;
+  auto launch_gemm = [&]() {
+    return l.bdirect ? dg::launch_masked_bdirect(p, l.grid, stream) : dg::launch(kind, l.shape, p, l.grid, stream);
+  };
   if (p.splits <= 1) {
-    if (dg::launch(kind, l.shape, p, l.grid, stream) != hipSuccess) return DG_ERROR_LAUNCH;
+    if (launch_gemm() != hipSuccess) return DG_ERROR_LAUNCH;
     return DG_SUCCESS;
   }
   p.ws_stride = (int64_t)groups * rows * n;
   void* ws = stream_workspace(stream, (size_t)p.splits * p.ws_stride * sizeof(float));
   if (!ws) return DG_ERROR_LAUNCH;
   p.ws = static_cast<float*>(ws);
-  if (dg::launch(kind, l.shape, p, l.grid, stream) != hipSuccess) return DG_ERROR_LAUNCH;
+  if (launch_gemm() != hipSuccess) return DG_ERROR_LAUNCH;
   if (dg::launch_splitk_reduce(kind, p, stream) != hipSuccess) return DG_ERROR_LAUNCH;
   return DG_SUCCESS;
 }
@@ -448,6 +472,7 @@ dg_status dg_select_config(int kind, int m, int n, int k, int num_groups, int nu
   out->tiles = p.tiles;
   out->grid = l.grid;
   out->k_splits = p.splits;
+  out->kernel = l.bdirect ? 1 : 0;
   return DG_SUCCESS;
 }
 

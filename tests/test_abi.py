@@ -121,7 +121,7 @@ def test_wgrad_argument_errors(lib):
 def _cfg(lib, kind, m, n, k, g=1, cus=256):
     class Cfg(ctypes.Structure):
         _fields_ = [(f, ctypes.c_int) for f in ("block_m", "block_n", "waves_m", "waves_n", "tiles", "grid",
-                                                "k_splits")]
+                                                "k_splits", "kernel")]
     c = Cfg()
     lib.dg_select_config.argtypes = [ctypes.c_int] * 6 + [ctypes.POINTER(Cfg)]
     st = lib.dg_select_config(kind, m, n, k, g, cus, ctypes.byref(c))
@@ -153,6 +153,9 @@ def test_heuristic_invariants(lib, kind, m, n, k, g):
         assert -(-kbs // chunk) == s, "a split would be empty"
         assert chunk >= 4
     assert 1 <= c["grid"] <= tiles * s
+    assert c["kernel"] in (0, 1) and (c["kernel"] == 0 or (kind == 2 and kbs % 2 == 0))
+    if c["kernel"] == 1:
+        assert (c["block_m"], c["block_n"]) == (256, 256) and -(-kbs // s) % 2 == 0
     if c["grid"] > 8:
         assert c["grid"] % 8 == 0
     assert c["grid"] <= 2 * 256
@@ -172,7 +175,7 @@ def test_split_k_planning(lib):
 
 
 def test_heuristic_rejects_bad_queries(lib):
-    c = ctypes.c_int * 7
+    c = ctypes.c_int * 8
     out = c()
     lib.dg_select_config.argtypes = [ctypes.c_int] * 6 + [ctypes.c_void_p]
     assert lib.dg_select_config(9, 1, 1, 128, 1, 256, ctypes.addressof(out)) == INVALID

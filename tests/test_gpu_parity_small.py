@@ -30,13 +30,18 @@ def dg():
 
 @pytest.fixture
 def force_tile(request):
+    """Force a tile shape; "bdirect" forces the masked decode kernel that
+    streams B into registers (its tile is fixed)."""
     def _set(tile):
-        if tile is None:
-            os.environ.pop("DG_FORCE_TILE", None)
-        else:
+        os.environ.pop("DG_FORCE_TILE", None)
+        os.environ.pop("DG_MASKED_BDIRECT", None)
+        if tile == "bdirect":
+            os.environ["DG_MASKED_BDIRECT"] = "1"
+        elif tile is not None:
             os.environ["DG_FORCE_TILE"] = tile
     yield _set
     os.environ.pop("DG_FORCE_TILE", None)
+    os.environ.pop("DG_MASKED_BDIRECT", None)
 
 
 def _dense_run(dg, d):
@@ -103,8 +108,8 @@ def test_contiguous_small(dg, force_tile, tile):
     check_close(bits_to_f64(got[valid]), bits_to_f64(ref[valid]), "contiguous small")
 
 
-@pytest.mark.parametrize("tile", [None, "256x256x1x8", "256x224x4x2", "256x128x1x4", "256x128x2x2", "128x128x2x2",
-                                  "64x32x2x2"])
+@pytest.mark.parametrize("tile", [None, "bdirect", "256x256x1x8", "256x224x4x2", "256x128x1x4", "256x128x2x2",
+                                  "128x128x2x2", "64x32x2x2"])
 def test_masked_small(dg, force_tile, tile):
     g, m_max, n, k = 5, 96, 260, 256
     mm = np.array([0, 1, 96, 200, 50], np.int32)  # empty, one row, full, clamped, partial
@@ -161,7 +166,7 @@ def test_page_call_style(dg):
     check_close(bits_to_f64(bf16_bits(out)), bits_to_f64(ref), "page-style dense")
 
 
-@pytest.mark.parametrize("tile", [None, "256x256x1x8", "256x128x1x4", "256x256x2x4"])
+@pytest.mark.parametrize("tile", [None, "bdirect", "256x256x1x8", "256x128x1x4", "256x256x2x4"])
 def test_masked_row_quarters(dg, force_tile, tile):
     """Tall masked tiles skip 64-row quarters past masked_m: every boundary."""
     mm = np.array([0, 1, 63, 64, 65, 127, 128, 129, 191, 192, 193, 255, 256, 300], np.int32)
@@ -206,7 +211,7 @@ def test_dense_split_k(dg, force_tile, force_splits, m, n, k, tile, splits):
     assert np.array_equal(got, _dense_run(dg, d)), "split-K result not deterministic"
 
 
-@pytest.mark.parametrize("tile", ["256x256x1x8", "256x64x1x4", "64x32x2x2"])
+@pytest.mark.parametrize("tile", ["bdirect", "256x256x1x8", "256x64x1x4", "64x32x2x2"])
 @pytest.mark.parametrize("splits", [2, 5])
 def test_masked_split_k(dg, force_tile, force_splits, tile, splits):
     mm = np.array([0, 1, 96, 300, 50, 64, 65], np.int32)  # empty, one row, full, clamped, partial
