@@ -195,6 +195,12 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   // parity (the next tile is looked up while the current one is computed)
   __shared__ int sRowOk[2][KIND == KIND_CONTIGUOUS ? BM : 1];
   __shared__ int sExpert[2][2];  // per parity: experts of the tile's two 128-row blocks
+  // bf16 epilogue staging: a wave's 16-row fragment row goes through LDS so
+  // that each store covers whole (64 columns) or half (32 columns) 128-byte
+  // lines; rows padded by 16 bytes against bank conflicts
+  constexpr bool kStage = !kFp32Out && (WTN == 64 || WTN == 32);
+  constexpr int kStageRow = WTN * 2 + 16;
+  __shared__ __attribute__((aligned(16))) uint8_t sOut[kStage ? NW : 1][kStage ? 16 * kStageRow : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -384,11 +390,16 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
 
   // bf16 output (or split-K partials) in whole 4-column vectors, offsets that
   // fit the 32-bit buffer range: the epilogue's stores have a fixed count
-  constexpr int kStores = FM * FN;
+  // staged bf16: 16 B per lane, (WTN*2*16)/1024 stores per fragment row
+  constexpr int kStageStores = FM * (WTN * 2 * 16 / 1024);
+  constexpr int kStores = kStage ? kStageStores : FM * FN;
   constexpr bool kExactFits = (S - 2) * DMIN + kStores <= 63;  // vmcnt range
-  // (not for the fp32 D kinds: their row-scale registers leave no room for it)
-  const bool exact_stores = kExactFits && (!kFp32Out || (kCanSplit && splits > 1)) && p.vec_out &&
-                            (int64_t)BM * p.n * 4 < 0x7fffffffLL;
+  // (not for the fp32 D kinds: their row-scale registers leave no room for
+  // it; staged layouts: bf16 with N % 8 == 0 only, split-K partials take the
+  // per-fragment path with the conservative wait)
+  const bool staged = kStage && !(kCanSplit && splits > 1) && p.vec_out && (p.n % 8 == 0);
+  const bool exact_stores = kExactFits && (kStage ? staged : (!kFp32Out || (kCanSplit && splits > 1))) &&
+                            p.vec_out && (int64_t)BM * p.n * 4 < 0x7fffffffLL;
   bool stores_pending = false;  // the previous tile's epilogue stores may be in flight
 
   int t_next = blockIdx.x;
@@ -601,9 +612,15 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
           res[r] = NOV > 0 ? (kStreamM ? frag_b(r) : frag_a(r)) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
         v8i cur = NOV > 0 ? load_s(0) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
 
-        float sav[FM];
+        // row scales: when A is the streamed operand, group o's scale is read
+        // as the group starts (only this group's and the previous one's are
+        // live); otherwise all FM (resident, few) are read up front
+        float sav[kStreamM ? 1 : FM];
+        if constexpr (!kStreamM) {
   #pragma unroll
-        for (int j = 0; j < FM; ++j) sav[j] = sSA[wm * WTM + 16 * j + l16];
+          for (int j = 0; j < FM; ++j) sav[j] = sSA[wm * WTM + 16 * j + l16];
+        }
+        float sa_prev = 0.f, sa_cur = 0.f;
         // B scale per n-fragment (block scales) or per column quad (row scales)
         float sbv[FN];
         v4f sbq[kRowScaleB ? FN : 1];
@@ -619,13 +636,14 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   #pragma unroll
           for (int i = 0; i < FN; ++i) sbv[i] = sSB[(n0 + wn * WTN + 16 * i) / kBK - n0 / kBK];
         }
-        // F(o, r) of this block
-        auto promote = [&](int o, int r) {
+        // F(o, r) of this block (o is the current or the previous group)
+        auto promote = [&](int o, int r, bool previous) {
           const int j = kStreamM ? o : r, i = kStreamM ? r : o;
+          const float sa = kStreamM ? (previous ? sa_prev : sa_cur) : sav[kStreamM ? 0 : j];
           if constexpr (kRowScaleB)
-            fma4q(acc[i][j], sav[j], sbq[i], part[r]);
+            fma4q(acc[i][j], sa, sbq[i], part[r]);
           else
-            fma4(acc[i][j], sav[j] * sbv[i], part[r]);
+            fma4(acc[i][j], sa * sbv[i], part[r]);
         };
         // F(NOV-1, r) of the previous block
         auto promote_pending = [&](int r) {
@@ -640,12 +658,13 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
         for (int o = 0; o < NOV; ++o) {
           v8i nxt = cur;
           if (o + 1 < NOV) nxt = load_s(o + 1);
+          if constexpr (kStreamM) sa_cur = sSA[wm * WTM + 16 * o + l16];
   #pragma unroll
           for (int r = 0; r < NR; ++r) {
             part[r] = kStreamM ? mfma_block(res[r], cur) : mfma_block(cur, res[r]);
             if (r + 1 < NR) {
               if (o > 0)
-                promote(o - 1, r + 1);
+                promote(o - 1, r + 1, true);
               else
                 promote_pending(r + 1);
             }
@@ -655,7 +674,8 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
           constexpr int kSpread = NOV / 2 > 0 ? NOV / 2 : 1;
           if (o < kSpread)
             issue_ahead(rel, (o * ND) / kSpread, ((o + 1) * ND) / kSpread);
-          promote(o, 0);
+          promote(o, 0, false);
+          sa_prev = sa_cur;
           cur = nxt;
           // keep each group's loads, MFMAs and FMAs together: no fragment
           // reads hoisted further ahead (register pressure)
@@ -665,11 +685,12 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   #pragma unroll
         for (int r = 0; r < NR && NOV > 0; ++r) {
           const int j = kStreamM ? NOV - 1 : r, i = kStreamM ? r : NOV - 1;
+          const float sa = kStreamM ? sa_prev : sav[kStreamM ? 0 : j];
           if constexpr (kRowScaleB) {
-            pend[r] = sav[j];
+            pend[r] = sa;
             pendq[r] = sbq[i];
           } else {
-            pend[r] = sav[j] * sbv[i];
+            pend[r] = sa * sbv[i];
           }
         }
       }
@@ -699,7 +720,43 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     }
 
     // ---- epilogue ----
-    if (exact_stores) {
+    if (kStage && staged) {
+      // fragment row j: lanes write their 4 bf16 per column fragment into the
+      // wave's LDS rows, then read 16 contiguous bytes each along the rows
+      constexpr int kLanesPerRow = WTN * 2 / 16;    // 8 (64 columns) or 4 (32)
+      constexpr int kRowsPerRound = 64 / kLanesPerRow;
+      constexpr int kRounds = 16 / kRowsPerRound;   // 2 or 1
+      uint8_t* so = sOut[kStage ? wave : 0];
+      const uint32_t sbase = lds_addr(so);
+      const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(static_cast<uint16_t*>(p.out) + out_row0 * p.n), (short)0, (int)((uint32_t)BM * p.n * 2), 0x00020000);
+      const int rl = lane / kLanesPerRow, cb = (lane % kLanesPerRow) * 16;  // read-back row and byte
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+          const uint32_t lo = (uint32_t)f32_to_bf16(acc[i][j][0]) | ((uint32_t)f32_to_bf16(acc[i][j][1]) << 16);
+          const uint32_t hi = (uint32_t)f32_to_bf16(acc[i][j][2]) | ((uint32_t)f32_to_bf16(acc[i][j][3]) << 16);
+          *reinterpret_cast<uint2*>(so + l16 * kStageRow + (16 * i + 4 * lq) * 2) = uint2{lo, hi};
+        }
+#pragma unroll
+        for (int h = 0; h < kRounds; ++h) {
+          const int r = h * kRowsPerRound + rl;
+          const uint4 v = *reinterpret_cast<const uint4*>(so + r * kStageRow + cb);
+          const int ml = wm * WTM + 16 * j + r;
+          bool row_ok;
+          if constexpr (KIND == KIND_CONTIGUOUS)
+            row_ok = sRowOk[par][ml] != 0;
+          else
+            row_ok = ml < rows;
+          const int n = n0 + wn * WTN + cb / 2;  // 8 columns, all valid or none (N % 8 == 0)
+          const uint32_t off = (row_ok && n < p.n) ? ((uint32_t)ml * p.n + n) * 2u : 0x80000000u;
+          __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w}, ro, off, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // one fragment row at a time (registers)
+      }
+      (void)sbase;
+    } else if (exact_stores) {
       // One buffer store per fragment pair, issued whether or not its lanes
       // are valid: a lane whose row or columns fall outside the output gets
       // an offset past the resource's range and the store drops it.  The
