@@ -288,3 +288,31 @@ def test_contiguous_tall_tiles(dg, force_tile, tile):
     assert np.all(got[~ok] == SENTINEL_BF16), "padding rows were written"
     assert not np.any(got[ok] == SENTINEL_BF16), "valid rows left unwritten"
     check_close(bits_to_f64(got[ok]), bits_to_f64(ref[ok]), f"contiguous tall {tile}")
+
+
+@pytest.mark.parametrize("tile", ["bdirect", None])
+@pytest.mark.parametrize("splits", [None, 2, 3])
+@pytest.mark.parametrize("k", [512, 2048])
+def test_masked_decode_kernels(dg, force_tile, force_splits, tile, splits, k):
+    """The masked decode kernels at longer K: ragged N (a last column tile
+    narrower than the tile), every row-quarter boundary of masked_m, forced K
+    splits (the B-in-registers kernel takes K blocks in pairs)."""
+    mm = np.array([0, 1, 63, 64, 65, 128, 191, 192, 255, 256, 300], np.int32)
+    g, m_max, n = mm.size, 256, 392
+    x = inputs.make_masked(g, m_max, n, k, seed=inputs.SEED_BASE + 61 + k, masked_m=mm)
+    force_tile(tile)
+    force_splits(splits)
+    say(f"masked decode kernel={tile} K={k} splits={splits}")
+
+    def run():
+        out = sentinel_bf16((g, m_max, n))
+        dg.dg_grouped_fp8_masked(dev(x.a), dev(x.sa), dev(x.b), dev(x.sb), out, dev(mm))
+        torch.cuda.synchronize()
+        return bf16_bits(out)
+    got = run()
+    ref, _ = oracle.grouped_masked(x.a, x.sa, x.b, x.sb, mm, np.full((g, m_max, n), SENTINEL_BF16, np.uint16))
+    rows = np.arange(m_max)[None, :] < np.clip(mm, 0, m_max)[:, None]
+    assert np.all(got[~rows] == SENTINEL_BF16), "masked rows were written"
+    assert not np.any(got[rows] == SENTINEL_BF16), "valid rows left unwritten"
+    check_close(bits_to_f64(got[rows]), bits_to_f64(ref[rows]), f"masked decode {tile} K={k} s{splits}")
+    assert np.array_equal(got, run()), "not deterministic"
