@@ -142,9 +142,6 @@ dg::TileShape heuristic(int kind, int rows, int n, int k, int groups, int num_cu
       pick = c.s;
     }
   }
-  // short K (few K blocks per tile): the 1x8 wave layout of the 256x256 tile
-  // keeps its epilogue stores shorter per wave (measured faster at K <= 1024)
-  if (pick.bm == 256 && pick.bn == 256 && kbs <= 8 && kind == DG_KIND_DENSE) pick = dg::TileShape{256, 256, 1, 8};
   return pick;
 }
 

@@ -613,9 +613,11 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
         v8i cur = NOV > 0 ? load_s(0) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
 
         // row scales: when A is the streamed operand, group o's scale is read
-        // as the group starts (only this group's and the previous one's are
-        // live); otherwise all FM (resident, few) are read up front
+        // one group ahead, with group o's fragment (so no group waits on an
+        // LDS read it has just issued; only three scales are live);
+        // otherwise all FM (resident, few) are read up front
         float sav[kStreamM ? 1 : FM];
+        float sa_next = (kStreamM && NOV > 0) ? sSA[wm * WTM + l16] : 0.f;
         if constexpr (!kStreamM) {
   #pragma unroll
           for (int j = 0; j < FM; ++j) sav[j] = sSA[wm * WTM + 16 * j + l16];
@@ -658,7 +660,10 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
         for (int o = 0; o < NOV; ++o) {
           v8i nxt = cur;
           if (o + 1 < NOV) nxt = load_s(o + 1);
-          if constexpr (kStreamM) sa_cur = sSA[wm * WTM + 16 * o + l16];
+          if constexpr (kStreamM) {
+            sa_cur = sa_next;
+            if (o + 1 < NOV) sa_next = sSA[wm * WTM + 16 * (o + 1) + l16];
+          }
   #pragma unroll
           for (int r = 0; r < NR; ++r) {
             part[r] = kStreamM ? mfma_block(res[r], cur) : mfma_block(cur, res[r]);
