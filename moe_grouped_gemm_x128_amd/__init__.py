@@ -4,7 +4,7 @@ Argument marshalling only: every function below checks tensor dtypes, shapes
 and devices, then calls the C ABI (include/dg.h) of libdg_mi355x.so with raw
 device pointers and the current HIP stream.  All arithmetic runs in the HIP
 kernels; there is no CPU path.  If the library has not been built the import
-fails loudly (build it with `python -m moe_grouped_gemm_x128_amd.build`).
+fails loudly (build it with `python moe_grouped_gemm_x128_amd/build.py`).
 
 The C-named functions mirror the C entry points one to one.  The
 `*_fp8_fp8_*` names follow the call style of the DeepGEMM pages' usage example
@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libdg_mi355x.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"{LIB_PATH} is missing: build the HIP library first "
-        "(python -m moe_grouped_gemm_x128_amd.build); there is no fallback path")
+        "(python moe_grouped_gemm_x128_amd/build.py); there is no fallback path")
 
 _lib = ctypes.CDLL(LIB_PATH)
 

@@ -1,6 +1,6 @@
 """Build the gfx950 HIP library (libdg_mi355x.so) in-tree with hipcc.
 
-    python -m moe_grouped_gemm_x128_amd.build        # or build() from Python
+    python moe_grouped_gemm_x128_amd/build.py        # or build() from Python
 
 Packed-fp32 instructions are disabled for the device code (the flag only
 concerns the gfx950 pass; hipcc's host pass warns that it does not know it).

@@ -19,8 +19,12 @@ INVALID, UNSUPPORTED, SUCCESS = 1, 2, 0
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        from moe_grouped_gemm_x128_amd import build as b
-        b.build()
+        # run build.py as a script: importing it as a submodule would run the
+        # package __init__, which refuses to load an unbuilt library
+        import subprocess
+        import sys
+        subprocess.run([sys.executable, os.path.join(ROOT, "moe_grouped_gemm_x128_amd", "build.py")],
+                       check=True)
     L = ctypes.CDLL(LIB)
     vp, i = ctypes.c_void_p, ctypes.c_int
     L.dg_gemm_fp8_nt.argtypes = [vp, vp, vp, vp, vp, i, i, i, vp]
