@@ -18,6 +18,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "dg_oracle.c")
+_SRCS = [_SRC, os.path.join(_HERE, "dg_quant_oracle.c")]
 _LIB = os.path.join(_HERE, "libdg_oracle.so")
 _lib = None
 
@@ -27,7 +28,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
         cmd = ["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-shared", "-fPIC",
-               "-o", tmp, _SRC, "-lm"]
+               "-o", tmp, *_SRCS, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
     return _LIB
@@ -262,3 +263,44 @@ def k_grouped_wgrad_at(a, sa, b, sb, ks, d0, groups, rows, cols):
                                         _I(n), _p(d0c), _p(groups), _p(rows), _p(cols),
                                         _I(rows.size), _p(out)), "k_grouped_wgrad_at")
     return out
+
+
+# ---- FP8 quantiser (dg_quant_oracle.c) ----
+
+def e4m3_encode(y: np.ndarray) -> np.ndarray:
+    """fp32 values (|y| <= 448) -> nearest e4m3fn codes, ties to even."""
+    y = _c(y, np.float32)
+    out = np.empty(y.shape, np.uint8)
+    lib().dgo_e4m3_encode(_p(y), _p(out), _I(y.size))
+    return out
+
+
+def quantize_1x128(x: np.ndarray):
+    """x fp32 [M,K] -> (q uint8 [M,K], s fp32 [M,K/128])."""
+    x = _c(x, np.float32)
+    m, k = x.shape
+    q = np.empty((m, k), np.uint8)
+    s = np.empty((m, k // 128), np.float32)
+    _check(lib().dgo_quantize_1x128(_p(x), _I(m), _I(k), _p(q), _p(s)), "quantize_1x128")
+    return q, s
+
+
+def quantize_128x128(x: np.ndarray):
+    """x fp32 [N,K] -> (q uint8 [N,K], s fp32 [ceil(N/128),K/128])."""
+    x = _c(x, np.float32)
+    n, k = x.shape
+    q = np.empty((n, k), np.uint8)
+    s = np.empty(((n + 127) // 128, k // 128), np.float32)
+    _check(lib().dgo_quantize_128x128(_p(x), _I(n), _I(k), _p(q), _p(s)), "quantize_128x128")
+    return q, s
+
+
+def quantize_1x128_transposed(x: np.ndarray):
+    """x fp32 [T,F] -> (q uint8 [F,T], s fp32 [F,T/128]): 1x128 groups along T."""
+    x = _c(x, np.float32)
+    t, f = x.shape
+    q = np.empty((f, t), np.uint8)
+    s = np.empty((f, t // 128), np.float32)
+    _check(lib().dgo_quantize_1x128_transposed(_p(x), _I(t), _I(f), _p(q), _p(s)),
+           "quantize_1x128_transposed")
+    return q, s
