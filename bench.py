@@ -213,6 +213,82 @@ def build_wgrad(kgrouped=False):
                    f"weight gradient D[{w.m},{w.n}] += over tokens {w.ks}, 1x128 scales on both operands, fp32 D"}
 
 
+QUANT_METRIC = "FP8 quantiser GB/s (absmax/448 fp32 scales) and % of MI355X HBM peak"
+
+
+def build_quantize():
+    """The quantiser on the GEMM workloads' fp32 operands: the MoE contiguous
+    activations (G=8 x 8192 rows), the dense activations and the largest dense
+    weight, and the two token-contiguous weight-gradient operands (X and dY of
+    4096 tokens, transposed).  Inputs are seeded N(0,1) fp32 drawn on the
+    device; algorithmic bytes = 4 read + 1 written per element + the scales."""
+    import torch
+    import moe_grouped_gemm_x128_amd as dg
+    from harness import inputs
+
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(inputs.SEED_BASE + 5)
+    specs = [("quant_1x128_m65536_k7168", 0, 65536, 7168), ("quant_1x128_m4096_k7168", 0, 4096, 7168),
+             ("quant_128x128_n7168_k16384", 1, 7168, 16384), ("quant_1x128T_t4096_f7168", 2, 4096, 7168),
+             ("quant_1x128T_t4096_f2048", 2, 4096, 2048)]
+    calls = []
+    for name, mode, r, c in specs:
+        x = torch.randn((r, c), generator=gen, device="cuda", dtype=torch.float32)
+        if mode == 0:
+            q = torch.empty((r, c), dtype=torch.uint8, device="cuda")
+            sc = torch.empty((r, c // 128), dtype=torch.float32, device="cuda")
+            fn = lambda x=x, q=q, sc=sc: dg.dg_quantize_fp8_1x128(x, q, sc)
+        elif mode == 1:
+            q = torch.empty((r, c), dtype=torch.uint8, device="cuda")
+            sc = torch.empty(((r + 127) // 128, c // 128), dtype=torch.float32, device="cuda")
+            fn = lambda x=x, q=q, sc=sc: dg.dg_quantize_fp8_128x128(x, q, sc)
+        else:
+            q = torch.empty((c, r), dtype=torch.uint8, device="cuda")
+            sc = torch.empty((c, r // 128), dtype=torch.float32, device="cuda")
+            fn = lambda x=x, q=q, sc=sc: dg.dg_quantize_fp8_1x128_transposed(x, q, sc)
+        nbytes = r * c * 5 + sc.numel() * 4
+
+        def sample(rng, rows, x=x, mode=mode, c=c):
+            """The oracle on the first `rows` rows (a multiple of 128, at most
+            the input's own); returns the algorithmic bytes covered."""
+            import oracle
+            rows = min(rows, x.shape[0])
+            h = x[:rows].cpu().numpy()
+            f = (oracle.quantize_1x128, oracle.quantize_128x128, oracle.quantize_1x128_transposed)[mode]
+            f(h)
+            return rows * c * 5
+
+        calls.append(Call(name, 0.0, nbytes, fn, (sample, c)))
+    return calls, {"workload": "quantize", "description":
+                   "FP8 quantiser: 1x128 activations [65536,7168] and [4096,7168], 128x128 weights "
+                   "[7168,16384], token-contiguous 1x128 transposed [4096,7168] and [4096,2048]",
+                   "scales": "absmax/448 fp32", "in": "fp32", "out": "e4m3"}
+
+
+def cpu_baseline_quantize(calls, seconds):
+    """Time the oracle quantiser on the first rows of each input (GB/s of
+    algorithmic traffic), sized to about `seconds` of CPU work."""
+    import oracle
+    rng = np.random.default_rng(12345)
+    rows = 128
+    while True:
+        t = time.perf_counter()
+        for c in calls:
+            c.sample[0](rng, rows)
+        dt = time.perf_counter() - t
+        if dt >= 0.1 * seconds or rows >= 65536:
+            break
+        rows *= 2
+    rows = int(rows * seconds / max(dt, 1e-9)) // 128 * 128
+    rows = min(65536, max(128, rows))
+    t = time.perf_counter()
+    nbytes = sum(c.sample[0](rng, rows) for c in calls)
+    dt = time.perf_counter() - t
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"first {rows} rows of each of the {len(calls)} inputs ({nbytes / 1e9:.2f} GB of "
+                      f"algorithmic traffic, {dt:.1f} s, C oracle with OpenMP, host copy included)"}
+
+
 # --------------------------------------------------------------- timing ---
 
 def per_call_times(calls, steps):
@@ -312,7 +388,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="dense",
-                    choices=["dense", "small", "contiguous", "masked", "wgrad", "k_grouped_wgrad"])
+                    choices=["dense", "small", "contiguous", "masked", "wgrad", "k_grouped_wgrad", "quantize"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--settle-seconds", type=float, default=0.5, help="untimed run before the warmup steps")
@@ -331,7 +407,8 @@ def main():
     log(f"device {torch.cuda.get_device_name(0)}, building workload {args.workload}")
     builders = {"dense": build_dense, "small": lambda: build_dense(small=True),
                 "contiguous": build_contiguous, "masked": build_masked,
-                "wgrad": build_wgrad, "k_grouped_wgrad": lambda: build_wgrad(kgrouped=True)}
+                "wgrad": build_wgrad, "k_grouped_wgrad": lambda: build_wgrad(kgrouped=True),
+                "quantize": build_quantize}
     if args.copy_calibration:
         copy_calibration()
         return
@@ -363,15 +440,23 @@ def main():
                 "frac": round(achieved / peak, 4), "traffic": measured_traffic(dc.name), "kernel": dc.name,
                 "flops_per_launch": dc.flops, "bytes_per_launch": dc.bytes, "avg_us": round(dms * 1e3, 2)}
 
+    quant = args.workload == "quantize"
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(calls, args.cpu_seconds)
+        cpu = cpu_baseline_quantize(calls, args.cpu_seconds) if quant else cpu_baseline(calls, args.cpu_seconds)
 
-    line = {"metric": METRIC, "value": round(step_flops / (ms_per_step * 1e-3) / 1e12, 2),
-            "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+    if quant:  # a stream, not a contraction: whole-step algorithmic bytes per second
+        value, unit, metric, dtype = sum(c.bytes for c in calls) / (ms_per_step * 1e-3) / 1e9, "GB/s", \
+            QUANT_METRIC, "f32"
+        data = "synthetic (seeded N(0,1) fp32)"
+    else:
+        value, unit, metric, dtype = step_flops / (ms_per_step * 1e-3) / 1e12, "TFLOP/s", METRIC, "fp8"
+        data = "synthetic (seeded N(0,1), e4m3-quantised)"
+    line = {"metric": metric, "value": round(value, 2),
+            "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
-            "vs_baseline": None, "dtype": "fp8", "data": "synthetic (seeded N(0,1), e4m3-quantised)",
+            "vs_baseline": None, "dtype": dtype, "data": data,
             "config": config, "roofline": roofline, "cpu_baseline": cpu, "per_shape": shapes}
     print(json.dumps(line), flush=True)
 

@@ -108,6 +108,39 @@ dg_status dg_k_grouped_wgrad_fp8_nt(const void* a, const float* sa, const void* 
                                     const float* sb, float* d, const int32_t* ks_host,
                                     int num_groups, int m, int n, hipStream_t stream);
 
+/* ---- FP8 quantiser: makes the operands above from fp32 ------------------
+ * DeepGEMM pages (DeepSeek DeepGEMM 中文讲解, "注意事项": FP8 needs dynamic
+ * scale factors from amax; "使用示例": scale granularity [M, K/128] for
+ * activations and [ceil(N/128), K/128] for weights).  For each group:
+ *     amax = max |x|,  s = amax / 448 (s = 1 for an all-zero group),
+ *     q    = e4m3 round-to-nearest-even( clamp(x / s, -448, 448) )
+ * with both divisions in IEEE fp32.  Inputs must be finite (a NaN or
+ * infinity gives unspecified codes and scales for its group, no error).
+ * x must be 16-byte aligned, s 4-byte aligned; every output element is
+ * written.  Sizes must fit the 32-bit arguments. */
+
+/* Activations: one scale per row and 128 consecutive columns.
+ *   x [M,K] fp32 -> q [M,K] fp8 (4-byte aligned), s [M,K/128] fp32.
+ * M >= 1; K >= 128 and K % 128 == 0. */
+dg_status dg_quantize_fp8_1x128(const float* x, void* q, float* s, int m, int k,
+                                hipStream_t stream);
+
+/* Weights: one scale per 128x128 block (the last row block holds the rows
+ * that exist).
+ *   x [N,K] fp32 -> q [N,K] fp8 (4-byte aligned), s [ceil(N/128),K/128] fp32.
+ * N >= 1; K >= 128 and K % 128 == 0. */
+dg_status dg_quantize_fp8_128x128(const float* x, void* q, float* s, int n, int k,
+                                  hipStream_t stream);
+
+/* Token-contiguous operands of the weight-gradient GEMMs (DeepGEMM pages,
+ * "反向传播中的梯度计算"): the 1x128 rule applied to the transpose of x, i.e.
+ * groups of 128 consecutive tokens of one feature.
+ *   x [T,F] fp32 (tokens x features) -> q [F,T] fp8 (16-byte aligned),
+ *   s [F,T/128] fp32.
+ * T >= 128 and T % 128 == 0; F >= 1 and F % 4 == 0. */
+dg_status dg_quantize_fp8_1x128_transposed(const float* x, void* q, float* s, int t, int f,
+                                           hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* dg_status_string(dg_status s);
 

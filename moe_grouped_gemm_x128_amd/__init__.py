@@ -34,8 +34,12 @@ _lib.dg_grouped_fp8_contiguous.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _
 _lib.dg_grouped_fp8_masked.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]
 _lib.dg_wgrad_fp8_nt.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]
 _lib.dg_k_grouped_wgrad_fp8_nt.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]
+_lib.dg_quantize_fp8_1x128.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
+_lib.dg_quantize_fp8_128x128.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
+_lib.dg_quantize_fp8_1x128_transposed.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
 for _f in ("dg_gemm_fp8_nt", "dg_grouped_fp8_contiguous", "dg_grouped_fp8_masked",
-           "dg_wgrad_fp8_nt", "dg_k_grouped_wgrad_fp8_nt"):
+           "dg_wgrad_fp8_nt", "dg_k_grouped_wgrad_fp8_nt", "dg_quantize_fp8_1x128",
+           "dg_quantize_fp8_128x128", "dg_quantize_fp8_1x128_transposed"):
     getattr(_lib, _f).restype = ctypes.c_int
 _lib.dg_status_string.argtypes = [ctypes.c_int]
 _lib.dg_status_string.restype = ctypes.c_char_p
@@ -194,6 +198,37 @@ def dg_k_grouped_wgrad_fp8_nt(a, sa, b, sb, d, ks):
     return d
 
 
+def dg_quantize_fp8_1x128(x, q, s):
+    """x fp32 [M,K] -> q fp8 [M,K], s fp32 [M,K/128] (see include/dg.h)."""
+    _f32(x, "x"); _fp8(q, "q"); _f32(s, "s")
+    _dev(x, q, s)
+    m, k = x.shape
+    _shape(q, (m, k), "q"); _shape(s, (m, k // 128), "s")
+    _check(_lib.dg_quantize_fp8_1x128(_ptr(x), _ptr(q), _ptr(s), m, k, _stream(x)), "dg_quantize_fp8_1x128")
+    return q, s
+
+
+def dg_quantize_fp8_128x128(x, q, s):
+    """x fp32 [N,K] -> q fp8 [N,K], s fp32 [ceil(N/128),K/128] (see include/dg.h)."""
+    _f32(x, "x"); _fp8(q, "q"); _f32(s, "s")
+    _dev(x, q, s)
+    n, k = x.shape
+    _shape(q, (n, k), "q"); _shape(s, ((n + 127) // 128, k // 128), "s")
+    _check(_lib.dg_quantize_fp8_128x128(_ptr(x), _ptr(q), _ptr(s), n, k, _stream(x)), "dg_quantize_fp8_128x128")
+    return q, s
+
+
+def dg_quantize_fp8_1x128_transposed(x, q, s):
+    """x fp32 [T,F] -> q fp8 [F,T], s fp32 [F,T/128] (see include/dg.h)."""
+    _f32(x, "x"); _fp8(q, "q"); _f32(s, "s")
+    _dev(x, q, s)
+    t, f = x.shape
+    _shape(q, (f, t), "q"); _shape(s, (f, t // 128), "s")
+    _check(_lib.dg_quantize_fp8_1x128_transposed(_ptr(x), _ptr(q), _ptr(s), t, f, _stream(x)),
+           "dg_quantize_fp8_1x128_transposed")
+    return q, s
+
+
 # ------------------------------------------------------ page-style names ---
 
 def gemm_fp8_fp8_bf16_nt(lhs, rhs, out):
@@ -214,3 +249,24 @@ def wgrad_gemm_fp8_fp8_fp32_nt(lhs, rhs, out):
 
 def k_grouped_wgrad_gemm_fp8_fp8_fp32_nt(lhs, rhs, out, ks):
     return dg_k_grouped_wgrad_fp8_nt(lhs[0], lhs[1], rhs[0], rhs[1], out, ks)
+
+
+def quantize_fp8_1x128(x):
+    """Activations: (fp8 [M,K], fp32 scales [M,K/128]) for the GEMM calls above."""
+    m, k = x.shape
+    return dg_quantize_fp8_1x128(x, torch.empty((m, k), dtype=FP8, device=x.device),
+                                 torch.empty((m, k // 128), dtype=torch.float32, device=x.device))
+
+
+def quantize_fp8_128x128(x):
+    """Weights: (fp8 [N,K], fp32 scales [ceil(N/128),K/128])."""
+    n, k = x.shape
+    return dg_quantize_fp8_128x128(x, torch.empty((n, k), dtype=FP8, device=x.device),
+                                   torch.empty(((n + 127) // 128, k // 128), dtype=torch.float32, device=x.device))
+
+
+def quantize_fp8_1x128_transposed(x):
+    """Weight-gradient operand from x [T,F]: (fp8 [F,T], fp32 scales [F,T/128])."""
+    t, f = x.shape
+    return dg_quantize_fp8_1x128_transposed(x, torch.empty((f, t), dtype=FP8, device=x.device),
+                                            torch.empty((f, t // 128), dtype=torch.float32, device=x.device))

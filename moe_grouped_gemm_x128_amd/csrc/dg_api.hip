@@ -302,6 +302,15 @@ dg_status run(int kind, dg::Params& p, int rows, int n, int k, int groups, hipSt
   return DG_SUCCESS;
 }
 
+dg_status quantize(int mode, const float* x, void* q, float* s, int rows, int cols, hipStream_t stream) {
+  int cus = 0;
+  if (device_cus(&cus) != 0) return DG_ERROR_LAUNCH;
+  (void)hipGetLastError();  // clear a stale error from unrelated work
+  if (dg::launch_quantize(mode, x, static_cast<uint8_t*>(q), s, rows, cols, cus, stream) != hipSuccess)
+    return DG_ERROR_LAUNCH;
+  return DG_SUCCESS;
+}
+
 dg::Params base_params() {
   dg::Params p;
   std::memset(&p, 0, sizeof(p));
@@ -471,6 +480,31 @@ dg_status dg_select_config(int kind, int m, int n, int k, int num_groups, int nu
   out->k_splits = p.splits;
   out->kernel = l.bdirect ? 1 : 0;
   return DG_SUCCESS;
+}
+
+dg_status dg_quantize_fp8_1x128(const float* x, void* q, float* s, int m, int k, hipStream_t stream) {
+  if (!x || !q || !s) return DG_ERROR_INVALID_VALUE;
+  if (m <= 0 || k <= 0) return DG_ERROR_INVALID_VALUE;
+  if (k % 128 != 0) return DG_ERROR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(q, 4) || !aligned(s, 4)) return DG_ERROR_UNSUPPORTED;
+  return quantize(0, x, q, s, m, k, stream);
+}
+
+dg_status dg_quantize_fp8_128x128(const float* x, void* q, float* s, int n, int k, hipStream_t stream) {
+  if (!x || !q || !s) return DG_ERROR_INVALID_VALUE;
+  if (n <= 0 || k <= 0) return DG_ERROR_INVALID_VALUE;
+  if (k % 128 != 0) return DG_ERROR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(q, 4) || !aligned(s, 4)) return DG_ERROR_UNSUPPORTED;
+  return quantize(1, x, q, s, n, k, stream);
+}
+
+dg_status dg_quantize_fp8_1x128_transposed(const float* x, void* q, float* s, int t, int f,
+                                           hipStream_t stream) {
+  if (!x || !q || !s) return DG_ERROR_INVALID_VALUE;
+  if (t <= 0 || f <= 0) return DG_ERROR_INVALID_VALUE;
+  if (t % 128 != 0 || f % 4 != 0) return DG_ERROR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4)) return DG_ERROR_UNSUPPORTED;
+  return quantize(2, x, q, s, t, f, stream);
 }
 
 int dg_version(void) { return 100; }

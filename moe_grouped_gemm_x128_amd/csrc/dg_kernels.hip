@@ -117,6 +117,18 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Wait for the oldest of the ring's in-flight K blocks: `later` blocks (at
+// most L) were issued after it, each D operations per wave, so at most
+// min(later, L) * D operations may stay in flight.
+template <int L, int D>
+__device__ __forceinline__ void wait_blocks(int later) {
+  if constexpr (L == 0) {
+    wait_vm<0>();
+  } else {
+    if (later >= L) wait_vm<L * D>(); else wait_blocks<L - 1, D>(later);
+  }
+}
+
 // Workgroup barrier that also orders LDS accesses for the compiler.
 __device__ __forceinline__ void barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -587,13 +599,8 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
         // for those blocks
         if (stores_pending && rel < S - 1) {
           if constexpr (kExactFits) wait_vm<(S - 2) * DMIN + kStores>(); else wait_vm<0>();
-        } else if constexpr (S == 2) {
-          wait_vm<0>();
-        } else if constexpr (S == 3) {
-          if (later >= 1) wait_vm<DMIN>(); else wait_vm<0>();
         } else {
-          static_assert(S == 4, "ring depth 2..4");
-          if (later >= 2) wait_vm<2 * DMIN>(); else if (later == 1) wait_vm<DMIN>(); else wait_vm<0>();
+          wait_blocks<S - 2, DMIN>(later);
         }
         barrier();  // every wave's block `rel` landed; every wave is done with rel-1
 
@@ -606,11 +613,16 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
         auto frag_a = [&](int j) { return load_frag(wA + j * 16 * kBK, frag_lo, frag_hi); };
         auto frag_b = [&](int i) { return load_frag(wB + i * 16 * kBK, frag_lo, frag_hi); };
         auto load_s = [&](int o) -> v8i { return kStreamM ? frag_a(o) : frag_b(o); };  // streamed fragment o
+        // the first MFMA's two fragments are read first (and kept first by
+        // the scheduling fence), so it waits only for them, not for every
+        // resident fragment of the block
         v8i res[NR];
-  #pragma unroll
-        for (int r = 0; r < NR; ++r)
-          res[r] = NOV > 0 ? (kStreamM ? frag_b(r) : frag_a(r)) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+        res[0] = NOV > 0 ? (kStreamM ? frag_b(0) : frag_a(0)) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
         v8i cur = NOV > 0 ? load_s(0) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+        __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+        for (int r = 1; r < NR; ++r)
+          res[r] = NOV > 0 ? (kStreamM ? frag_b(r) : frag_a(r)) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
 
         // row scales: when A is the streamed operand, group o's scale is read
         // one group ahead, with group o's fragment (so no group waits on an

@@ -1,0 +1,212 @@
+// dg_quant.hip -- FP8 (e4m3) quantiser with fine-grained fp32 scales for
+// gfx950: it makes the GEMM's operands.
+//
+// The DeepGEMM pages (DeepSeek DeepGEMM 中文讲解, "注意事项") ask for dynamic
+// scale factors from amax; their usage example ("使用示例") fixes the
+// granularity: one fp32 scale per row and 128-wide K group for activations
+// ([M, K/128]) and one per 128x128 block for weights ([ceil(N/128), K/128]).
+// Per group:
+//   amax = max |x|,  s = amax / 448 (1 for an all-zero group),
+//   q    = e4m3 nearest-even( clamp(x / s, -448, 448) )
+// with the two divisions in IEEE fp32 (correctly rounded: HIP's default
+// for `/`), so the codes match a scalar fp32 evaluation bit for bit.
+//
+// The work is a stream (4 bytes read, 1 byte + a few scale bytes written per
+// element), bound by HBM.  One 256-thread workgroup owns a 128 x 128 tile of
+// x: thread t loads float4 number t of each of the tile's 16 strips of 8 rows
+// (32 lanes cover one 512-byte row segment, fully coalesced), keeps its 64
+// values in registers, and writes its codes after the tile's amax is known, so
+// every input byte is read from HBM once.  The three layouts differ in the
+// reduction:
+//   * 1x128: amax per row -- the 32 lanes of a row reduce by lane shuffles;
+//   * 128x128: amax over the tile -- wave shuffles, then 4 waves through LDS;
+//   * 1x128 transposed (x [T, F] -> q [F, T], s [F, T/128], the token-
+//     contiguous operands of the weight-gradient GEMM): amax per column over
+//     the tile's 128 rows -- in-thread, lane l with l + 32, then 4 waves
+//     through LDS; the codes are transposed through an LDS byte tile so each
+//     store writes 16 consecutive tokens of one feature.
+#include "dg_kernel.h"
+
+namespace dg {
+namespace {
+
+constexpr int kQ = 128;          // group / tile edge
+constexpr int kQThreads = 256;   // 4 waves
+constexpr int kQStrips = 16;     // float4 loads per thread: 128 rows x 32 float4 / 256
+constexpr float kE4m3Max = 448.0f;
+
+enum QuantMode : int { Q_ROWS = 0, Q_BLOCKS = 1, Q_TRANSPOSED = 2 };
+
+__device__ __forceinline__ float scale_of(float amax) { return amax == 0.0f ? 1.0f : amax / kE4m3Max; }
+
+__device__ __forceinline__ float quotient(float x, float s) {
+  return fminf(fmaxf(x / s, -kE4m3Max), kE4m3Max);
+}
+
+// Four values (already within +-448) -> four e4m3fn codes, round to nearest
+// even (v_cvt_pk_fp8_f32; gfx950's FP8 conversion uses the OCP E4M3FN encoding).
+__device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+__device__ __forceinline__ float max_xor(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
+
+template <int MODE>
+__global__ __launch_bounds__(kQThreads) void quant_kernel(const float* __restrict__ x, uint8_t* __restrict__ q,
+                                                          float* __restrict__ s, int rows, int cols, int64_t tiles,
+                                                          int col_tiles) {
+  // Q_BLOCKS / Q_TRANSPOSED: per-wave partial maxima; Q_TRANSPOSED: byte tile
+  __shared__ float sMax[4][kQ];
+  __shared__ __attribute__((aligned(16))) uint8_t sT[MODE == Q_TRANSPOSED ? kQ : 1][kQ + 16];
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int c4 = t & 31;       // float4 column of the thread in the tile
+  const int rsub = t >> 5;     // row of the thread within each 8-row strip
+
+  for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+    const int64_t tr = tile / col_tiles;
+    const int tc = (int)(tile - tr * col_tiles);
+    const int64_t r0 = tr * kQ;
+    const int c0 = tc * kQ;
+    const int col = c0 + 4 * c4;
+    // load: strip i covers tile rows 8i .. 8i+7
+    float4 v[kQStrips];
+#pragma unroll
+    for (int i = 0; i < kQStrips; ++i) {
+      const int64_t r = r0 + 8 * i + rsub;
+      const bool ok = r < rows && (MODE != Q_TRANSPOSED || col < cols);
+      v[i] = ok ? *reinterpret_cast<const float4*>(x + r * cols + col) : float4{0.f, 0.f, 0.f, 0.f};
+    }
+    auto amax4 = [](const float4& a) { return fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))); };
+
+    if constexpr (MODE == Q_ROWS) {
+      const int kg = cols / kQ;
+#pragma unroll
+      for (int i = 0; i < kQStrips; ++i) {
+        float m = amax4(v[i]);
+        m = max_xor(m, 16);
+        m = max_xor(m, 8);
+        m = max_xor(m, 4);
+        m = max_xor(m, 2);
+        m = max_xor(m, 1);
+        const float sc = scale_of(m);
+        const int64_t r = r0 + 8 * i + rsub;
+        if (r < rows) {
+          if (c4 == 0) s[r * kg + tc] = sc;
+          *reinterpret_cast<uint32_t*>(q + r * cols + col) =
+              encode4(quotient(v[i].x, sc), quotient(v[i].y, sc), quotient(v[i].z, sc), quotient(v[i].w, sc));
+        }
+      }
+    } else if constexpr (MODE == Q_BLOCKS) {
+      float m = 0.f;
+#pragma unroll
+      for (int i = 0; i < kQStrips; ++i) m = fmaxf(m, amax4(v[i]));
+      m = max_xor(m, 32);
+      m = max_xor(m, 16);
+      m = max_xor(m, 8);
+      m = max_xor(m, 4);
+      m = max_xor(m, 2);
+      m = max_xor(m, 1);
+      __syncthreads();  // the previous tile's readers of sMax are done
+      if (lane == 0) sMax[wave][0] = m;
+      __syncthreads();
+      const float sc = scale_of(fmaxf(fmaxf(sMax[0][0], sMax[1][0]), fmaxf(sMax[2][0], sMax[3][0])));
+      if (t == 0) s[tr * col_tiles + tc] = sc;
+#pragma unroll
+      for (int i = 0; i < kQStrips; ++i) {
+        const int64_t r = r0 + 8 * i + rsub;
+        if (r < rows)
+          *reinterpret_cast<uint32_t*>(q + r * cols + col) =
+              encode4(quotient(v[i].x, sc), quotient(v[i].y, sc), quotient(v[i].z, sc), quotient(v[i].w, sc));
+      }
+    } else {
+      // columns are features, rows are tokens; groups run down a column
+      float4 m = float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < kQStrips; ++i) {
+        m.x = fmaxf(m.x, fabsf(v[i].x));
+        m.y = fmaxf(m.y, fabsf(v[i].y));
+        m.z = fmaxf(m.z, fabsf(v[i].z));
+        m.w = fmaxf(m.w, fabsf(v[i].w));
+      }
+      m.x = max_xor(m.x, 32);
+      m.y = max_xor(m.y, 32);
+      m.z = max_xor(m.z, 32);
+      m.w = max_xor(m.w, 32);
+      __syncthreads();  // the previous tile's readers of sMax and sT are done
+      if (lane < 32) *reinterpret_cast<float4*>(&sMax[wave][4 * c4]) = m;
+      __syncthreads();
+      const float4 a0 = *reinterpret_cast<const float4*>(&sMax[0][4 * c4]);
+      const float4 a1 = *reinterpret_cast<const float4*>(&sMax[1][4 * c4]);
+      const float4 a2 = *reinterpret_cast<const float4*>(&sMax[2][4 * c4]);
+      const float4 a3 = *reinterpret_cast<const float4*>(&sMax[3][4 * c4]);
+      const float sx = scale_of(fmaxf(fmaxf(a0.x, a1.x), fmaxf(a2.x, a3.x)));
+      const float sy = scale_of(fmaxf(fmaxf(a0.y, a1.y), fmaxf(a2.y, a3.y)));
+      const float sz = scale_of(fmaxf(fmaxf(a0.z, a1.z), fmaxf(a2.z, a3.z)));
+      const float sw = scale_of(fmaxf(fmaxf(a0.w, a1.w), fmaxf(a2.w, a3.w)));
+      const int kg = rows / kQ;  // token groups per feature
+      if (t < 32) {
+        const float sv[4] = {sx, sy, sz, sw};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (col + j < cols) s[(int64_t)(col + j) * kg + tr] = sv[j];
+      }
+      // codes into the byte tile [feature][token]
+#pragma unroll
+      for (int i = 0; i < kQStrips; ++i) {
+        const uint32_t w = encode4(quotient(v[i].x, sx), quotient(v[i].y, sy), quotient(v[i].z, sz),
+                                   quotient(v[i].w, sw));
+        const int tok = 8 * i + rsub;
+        sT[4 * c4 + 0][tok] = (uint8_t)(w & 0xffu);
+        sT[4 * c4 + 1][tok] = (uint8_t)((w >> 8) & 0xffu);
+        sT[4 * c4 + 2][tok] = (uint8_t)((w >> 16) & 0xffu);
+        sT[4 * c4 + 3][tok] = (uint8_t)(w >> 24);
+      }
+      __syncthreads();
+      // 8 lanes write one feature's 128 tokens (a whole 128-byte line)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int f = 32 * k + (t >> 3);
+        const int ch = t & 7;
+        if (c0 + f < cols)
+          *reinterpret_cast<uint4*>(q + (int64_t)(c0 + f) * rows + r0 + 16 * ch) =
+              *reinterpret_cast<const uint4*>(&sT[f][16 * ch]);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize(int mode, const float* x, uint8_t* q, float* s, int rows, int cols, int num_cus,
+                           hipStream_t stream) {
+  const int64_t row_tiles = (rows + kQ - 1) / kQ;
+  const int col_tiles = (cols + kQ - 1) / kQ;
+  const int64_t tiles = row_tiles * col_tiles;
+  // enough workgroups to keep eight resident per CU; each walks tiles with a
+  // grid stride
+  const int64_t cap = (int64_t)(num_cus > 0 ? num_cus : 256) * 8;
+  const int grid = (int)(tiles < cap ? tiles : cap);
+  if (grid <= 0) return hipSuccess;
+  switch (mode) {
+    case Q_ROWS:
+      hipLaunchKernelGGL(quant_kernel<Q_ROWS>, dim3(grid), dim3(kQThreads), 0, stream, x, q, s, rows, cols, tiles,
+                         col_tiles);
+      break;
+    case Q_BLOCKS:
+      hipLaunchKernelGGL(quant_kernel<Q_BLOCKS>, dim3(grid), dim3(kQThreads), 0, stream, x, q, s, rows, cols, tiles,
+                         col_tiles);
+      break;
+    case Q_TRANSPOSED:
+      hipLaunchKernelGGL(quant_kernel<Q_TRANSPOSED>, dim3(grid), dim3(kQThreads), 0, stream, x, q, s, rows, cols,
+                         tiles, col_tiles);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dg

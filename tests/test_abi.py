@@ -102,6 +102,29 @@ def test_grouped_argument_errors(lib):
     assert m(A16, A16, A16, A16, A16, A16, 2, 256, 8, 200, None) == UNSUPPORTED
 
 
+def test_quantizer_argument_errors(lib):
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    for name in ("dg_quantize_fp8_1x128", "dg_quantize_fp8_128x128", "dg_quantize_fp8_1x128_transposed"):
+        f = getattr(lib, name)
+        f.argtypes = [vp, vp, vp, i, i, vp]
+        assert f(None, A16, A16, 128, 128, None) == INVALID, name
+        assert f(A16, None, A16, 128, 128, None) == INVALID, name
+        assert f(A16, A16, None, 128, 128, None) == INVALID, name
+        assert f(A16, A16, A16, 0, 128, None) == INVALID, name
+        assert f(A16, A16, A16, 128, -1, None) == INVALID, name
+        assert f(A16 + 4, A16, A16, 128, 128, None) == UNSUPPORTED, name   # x not 16-byte aligned
+        assert f(A16, A16, A16 + 2, 128, 128, None) == UNSUPPORTED, name   # scale alignment
+    q1 = lib.dg_quantize_fp8_1x128
+    assert q1(A16, A16, A16, 128, 100, None) == UNSUPPORTED               # K % 128
+    assert q1(A16, A16 + 2, A16, 128, 128, None) == UNSUPPORTED           # q alignment
+    qb = lib.dg_quantize_fp8_128x128
+    assert qb(A16, A16, A16, 100, 200, None) == UNSUPPORTED
+    qt = lib.dg_quantize_fp8_1x128_transposed
+    assert qt(A16, A16, A16, 100, 128, None) == UNSUPPORTED               # T % 128
+    assert qt(A16, A16, A16, 128, 130, None) == UNSUPPORTED               # F % 4
+    assert qt(A16, A16 + 4, A16, 128, 128, None) == UNSUPPORTED           # q 16-byte alignment
+
+
 def test_wgrad_argument_errors(lib):
     w = lib.dg_wgrad_fp8_nt
     assert w(A16, A16, A16, A16, None, 4, 4, 128, None) == INVALID
