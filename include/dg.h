@@ -115,7 +115,9 @@ dg_status dg_k_grouped_wgrad_fp8_nt(const void* a, const float* sa, const void* 
  *     amax = max |x|,  s = amax / 448 (s = 1 for an all-zero group),
  *     q    = e4m3 round-to-nearest-even( clamp(x / s, -448, 448) )
  * with both divisions in IEEE fp32.  Inputs must be finite (a NaN or
- * infinity gives unspecified codes and scales for its group, no error).
+ * infinity gives unspecified codes and scales for its group, no error), and
+ * a group's amax must be 0 or at least 2^-140 (below that s would underflow
+ * to zero; such a group gets unspecified codes).
  * x must be 16-byte aligned, s 4-byte aligned; every output element is
  * written.  Sizes must fit the 32-bit arguments. */
 

@@ -8,39 +8,57 @@
 // Per group:
 //   amax = max |x|,  s = amax / 448 (1 for an all-zero group),
 //   q    = e4m3 nearest-even( clamp(x / s, -448, 448) )
-// with the two divisions in IEEE fp32 (correctly rounded: HIP's default
-// for `/`), so the codes match a scalar fp32 evaluation bit for bit.
+// with both divisions equal to IEEE fp32 division (round to nearest even),
+// so the codes match a scalar fp32 evaluation bit for bit.
 //
 // The work is a stream (4 bytes read, 1 byte + a few scale bytes written per
-// element), bound by HBM.  One 256-thread workgroup owns a 128 x 128 tile of
-// x: thread t loads float4 number t of each of the tile's 16 strips of 8 rows
-// (32 lanes cover one 512-byte row segment, fully coalesced), keeps its 64
-// values in registers, and writes its codes after the tile's amax is known, so
-// every input byte is read from HBM once.  The three layouts differ in the
-// reduction:
-//   * 1x128: amax per row -- the 32 lanes of a row reduce by lane shuffles;
-//   * 128x128: amax over the tile -- wave shuffles, then 4 waves through LDS;
-//   * 1x128 transposed (x [T, F] -> q [F, T], s [F, T/128], the token-
-//     contiguous operands of the weight-gradient GEMM): amax per column over
-//     the tile's 128 rows -- in-thread, lane l with l + 32, then 4 waves
-//     through LDS; the codes are transposed through an LDS byte tile so each
-//     store writes 16 consecutive tokens of one feature.
+// element), bound by HBM; every input byte is read from HBM once, and each
+// thread keeps its values in registers until its group's amax is known.
+//   * 1x128 (x [M, K]): the groups are consecutive 512-byte runs of the flat
+//     array, so each wave streams 16 consecutive groups (8 KB) per step and
+//     the 32 lanes of a group reduce its amax by lane shuffles;
+//   * 128x128 and 1x128 transposed: one 512-thread workgroup owns a 128 x 128
+//     tile; thread t loads float4 number t of each of the tile's 8 strips of
+//     16 rows (32 lanes cover one 512-byte row segment).  128x128: amax over
+//     the tile (wave shuffles, then 8 waves through LDS).  Transposed (x [T, F]
+//     -> q [F, T], s [F, T/128], the token-contiguous operands of the weight-
+//     gradient GEMM): amax per column over the tile's 128 rows (in-thread, lane
+//     l with l + 32, then 8 waves through LDS), and the codes are transposed
+//     through an LDS byte tile so each store writes 16 consecutive tokens of
+//     one feature.
+// The quotient x / s is computed without a full division per element (see
+// quotient()): one division per group for RN(1/s), then multiplies and FMAs
+// that reproduce the IEEE quotient bit for bit.
 #include "dg_kernel.h"
 
 namespace dg {
 namespace {
 
 constexpr int kQ = 128;          // group / tile edge
-constexpr int kQThreads = 256;   // 4 waves
-constexpr int kQStrips = 16;     // float4 loads per thread: 128 rows x 32 float4 / 256
+constexpr int kQThreads = 512;   // 8 waves
+constexpr int kQStrips = 8;      // float4 loads per thread: 128 rows x 32 float4 / 512
 constexpr float kE4m3Max = 448.0f;
 
 enum QuantMode : int { Q_ROWS = 0, Q_BLOCKS = 1, Q_TRANSPOSED = 2 };
 
 __device__ __forceinline__ float scale_of(float amax) { return amax == 0.0f ? 1.0f : amax / kE4m3Max; }
 
+// x / s, equal to the IEEE fp32 quotient: y0 = x * RN(1/s), then two
+// residual corrections y += RN(1/s) * (x - y*s) with the residual exact in an
+// FMA (Markstein's scheme).  A group whose scale is below 2^-60 is first
+// rescaled by 2^64 (x and s alike, exactly) so the residuals stay in the
+// normal range; the sign is copied from x so that -0 stays -0.
 __device__ __forceinline__ float quotient(float x, float s) {
-  return fminf(fmaxf(x / s, -kE4m3Max), kE4m3Max);
+  const float k = s < 0x1p-60f ? 0x1p64f : 1.0f;
+  x *= k;
+  s *= k;
+  const float r = 1.0f / s;
+  float y = x * r;
+  float e = __builtin_fmaf(-y, s, x);
+  y = __builtin_fmaf(e, r, y);
+  e = __builtin_fmaf(-y, s, x);
+  y = __builtin_copysignf(__builtin_fmaf(e, r, y), x);
+  return fminf(fmaxf(y, -kE4m3Max), kE4m3Max);
 }
 
 // Four values (already within +-448) -> four e4m3fn codes, round to nearest
@@ -53,17 +71,18 @@ __device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d) 
 
 __device__ __forceinline__ float max_xor(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
 
+// 128 x 128 tiles: MODE is Q_BLOCKS or Q_TRANSPOSED
 template <int MODE>
 __global__ __launch_bounds__(kQThreads) void quant_kernel(const float* __restrict__ x, uint8_t* __restrict__ q,
                                                           float* __restrict__ s, int rows, int cols, int64_t tiles,
                                                           int col_tiles) {
   // Q_BLOCKS / Q_TRANSPOSED: per-wave partial maxima; Q_TRANSPOSED: byte tile
-  __shared__ float sMax[4][kQ];
+  __shared__ float sMax[8][kQ];
   __shared__ __attribute__((aligned(16))) uint8_t sT[MODE == Q_TRANSPOSED ? kQ : 1][kQ + 16];
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int c4 = t & 31;       // float4 column of the thread in the tile
-  const int rsub = t >> 5;     // row of the thread within each 8-row strip
+  const int rsub = t >> 5;     // row of the thread within each 16-row strip
 
   for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
     const int64_t tr = tile / col_tiles;
@@ -71,35 +90,17 @@ __global__ __launch_bounds__(kQThreads) void quant_kernel(const float* __restric
     const int64_t r0 = tr * kQ;
     const int c0 = tc * kQ;
     const int col = c0 + 4 * c4;
-    // load: strip i covers tile rows 8i .. 8i+7
+    // load: strip i covers tile rows 16i .. 16i+15
     float4 v[kQStrips];
 #pragma unroll
     for (int i = 0; i < kQStrips; ++i) {
-      const int64_t r = r0 + 8 * i + rsub;
+      const int64_t r = r0 + 16 * i + rsub;
       const bool ok = r < rows && (MODE != Q_TRANSPOSED || col < cols);
       v[i] = ok ? *reinterpret_cast<const float4*>(x + r * cols + col) : float4{0.f, 0.f, 0.f, 0.f};
     }
     auto amax4 = [](const float4& a) { return fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))); };
 
-    if constexpr (MODE == Q_ROWS) {
-      const int kg = cols / kQ;
-#pragma unroll
-      for (int i = 0; i < kQStrips; ++i) {
-        float m = amax4(v[i]);
-        m = max_xor(m, 16);
-        m = max_xor(m, 8);
-        m = max_xor(m, 4);
-        m = max_xor(m, 2);
-        m = max_xor(m, 1);
-        const float sc = scale_of(m);
-        const int64_t r = r0 + 8 * i + rsub;
-        if (r < rows) {
-          if (c4 == 0) s[r * kg + tc] = sc;
-          *reinterpret_cast<uint32_t*>(q + r * cols + col) =
-              encode4(quotient(v[i].x, sc), quotient(v[i].y, sc), quotient(v[i].z, sc), quotient(v[i].w, sc));
-        }
-      }
-    } else if constexpr (MODE == Q_BLOCKS) {
+    if constexpr (MODE == Q_BLOCKS) {
       float m = 0.f;
 #pragma unroll
       for (int i = 0; i < kQStrips; ++i) m = fmaxf(m, amax4(v[i]));
@@ -112,11 +113,14 @@ __global__ __launch_bounds__(kQThreads) void quant_kernel(const float* __restric
       __syncthreads();  // the previous tile's readers of sMax are done
       if (lane == 0) sMax[wave][0] = m;
       __syncthreads();
-      const float sc = scale_of(fmaxf(fmaxf(sMax[0][0], sMax[1][0]), fmaxf(sMax[2][0], sMax[3][0])));
+      float mm = sMax[0][0];
+#pragma unroll
+      for (int w = 1; w < 8; ++w) mm = fmaxf(mm, sMax[w][0]);
+      const float sc = scale_of(mm);
       if (t == 0) s[tr * col_tiles + tc] = sc;
 #pragma unroll
       for (int i = 0; i < kQStrips; ++i) {
-        const int64_t r = r0 + 8 * i + rsub;
+        const int64_t r = r0 + 16 * i + rsub;
         if (r < rows)
           *reinterpret_cast<uint32_t*>(q + r * cols + col) =
               encode4(quotient(v[i].x, sc), quotient(v[i].y, sc), quotient(v[i].z, sc), quotient(v[i].w, sc));
@@ -138,14 +142,16 @@ __global__ __launch_bounds__(kQThreads) void quant_kernel(const float* __restric
       __syncthreads();  // the previous tile's readers of sMax and sT are done
       if (lane < 32) *reinterpret_cast<float4*>(&sMax[wave][4 * c4]) = m;
       __syncthreads();
-      const float4 a0 = *reinterpret_cast<const float4*>(&sMax[0][4 * c4]);
-      const float4 a1 = *reinterpret_cast<const float4*>(&sMax[1][4 * c4]);
-      const float4 a2 = *reinterpret_cast<const float4*>(&sMax[2][4 * c4]);
-      const float4 a3 = *reinterpret_cast<const float4*>(&sMax[3][4 * c4]);
-      const float sx = scale_of(fmaxf(fmaxf(a0.x, a1.x), fmaxf(a2.x, a3.x)));
-      const float sy = scale_of(fmaxf(fmaxf(a0.y, a1.y), fmaxf(a2.y, a3.y)));
-      const float sz = scale_of(fmaxf(fmaxf(a0.z, a1.z), fmaxf(a2.z, a3.z)));
-      const float sw = scale_of(fmaxf(fmaxf(a0.w, a1.w), fmaxf(a2.w, a3.w)));
+      float4 a = *reinterpret_cast<const float4*>(&sMax[0][4 * c4]);
+#pragma unroll
+      for (int w = 1; w < 8; ++w) {
+        const float4 b = *reinterpret_cast<const float4*>(&sMax[w][4 * c4]);
+        a.x = fmaxf(a.x, b.x);
+        a.y = fmaxf(a.y, b.y);
+        a.z = fmaxf(a.z, b.z);
+        a.w = fmaxf(a.w, b.w);
+      }
+      const float sx = scale_of(a.x), sy = scale_of(a.y), sz = scale_of(a.z), sw = scale_of(a.w);
       const int kg = rows / kQ;  // token groups per feature
       if (t < 32) {
         const float sv[4] = {sx, sy, sz, sw};
@@ -158,7 +164,7 @@ __global__ __launch_bounds__(kQThreads) void quant_kernel(const float* __restric
       for (int i = 0; i < kQStrips; ++i) {
         const uint32_t w = encode4(quotient(v[i].x, sx), quotient(v[i].y, sy), quotient(v[i].z, sz),
                                    quotient(v[i].w, sw));
-        const int tok = 8 * i + rsub;
+        const int tok = 16 * i + rsub;
         sT[4 * c4 + 0][tok] = (uint8_t)(w & 0xffu);
         sT[4 * c4 + 1][tok] = (uint8_t)((w >> 8) & 0xffu);
         sT[4 * c4 + 2][tok] = (uint8_t)((w >> 16) & 0xffu);
@@ -167,12 +173,48 @@ __global__ __launch_bounds__(kQThreads) void quant_kernel(const float* __restric
       __syncthreads();
       // 8 lanes write one feature's 128 tokens (a whole 128-byte line)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int f = 32 * k + (t >> 3);
+      for (int k = 0; k < 2; ++k) {
+        const int f = 64 * k + (t >> 3);
         const int ch = t & 7;
         if (c0 + f < cols)
           *reinterpret_cast<uint4*>(q + (int64_t)(c0 + f) * rows + r0 + 16 * ch) =
               *reinterpret_cast<const uint4*>(&sT[f][16 * ch]);
+      }
+    }
+  }
+}
+
+// 1x128 groups of a row-major [M, K] array (K % 128 == 0) are consecutive
+// 512-byte runs of the flat array: each wave streams 16 consecutive groups
+// (8 KB) per step, lane l holding float4 number l + 64j (group 2j + l/32).
+__global__ __launch_bounds__(kQThreads) void quant_rows_kernel(const float* __restrict__ x, uint8_t* __restrict__ q,
+                                                               float* __restrict__ s, int64_t groups) {
+  const int lane = threadIdx.x & 63;
+  const int64_t waves = (int64_t)gridDim.x * (kQThreads / 64);
+  const int64_t chunks = (groups + 15) / 16;
+  for (int64_t c = (int64_t)blockIdx.x * (kQThreads / 64) + (threadIdx.x >> 6); c < chunks; c += waves) {
+    const int64_t g0 = c * 16;
+    float4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t g = g0 + 2 * j + (lane >> 5);
+      v[j] = g < groups ? *reinterpret_cast<const float4*>(x + g0 * kQ + 256 * j + 4 * lane)
+                        : float4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float m = fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w)));
+      m = max_xor(m, 16);
+      m = max_xor(m, 8);
+      m = max_xor(m, 4);
+      m = max_xor(m, 2);
+      m = max_xor(m, 1);
+      const float sc = scale_of(m);
+      const int64_t g = g0 + 2 * j + (lane >> 5);
+      if (g < groups) {
+        if ((lane & 31) == 0) s[g] = sc;
+        *reinterpret_cast<uint32_t*>(q + g0 * kQ + 256 * j + 4 * lane) =
+            encode4(quotient(v[j].x, sc), quotient(v[j].y, sc), quotient(v[j].z, sc), quotient(v[j].w, sc));
       }
     }
   }
@@ -191,10 +233,13 @@ hipError_t launch_quantize(int mode, const float* x, uint8_t* q, float* s, int r
   const int grid = (int)(tiles < cap ? tiles : cap);
   if (grid <= 0) return hipSuccess;
   switch (mode) {
-    case Q_ROWS:
-      hipLaunchKernelGGL(quant_kernel<Q_ROWS>, dim3(grid), dim3(kQThreads), 0, stream, x, q, s, rows, cols, tiles,
-                         col_tiles);
+    case Q_ROWS: {
+      const int64_t groups = (int64_t)rows * (cols / kQ);
+      const int64_t wgs = (groups + 16 * (kQThreads / 64) - 1) / (16 * (kQThreads / 64));
+      const int g2 = (int)(wgs < cap ? wgs : cap);
+      hipLaunchKernelGGL(quant_rows_kernel, dim3(g2), dim3(kQThreads), 0, stream, x, q, s, groups);
       break;
+    }
     case Q_BLOCKS:
       hipLaunchKernelGGL(quant_kernel<Q_BLOCKS>, dim3(grid), dim3(kQThreads), 0, stream, x, q, s, rows, cols, tiles,
                          col_tiles);

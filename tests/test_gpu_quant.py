@@ -90,6 +90,38 @@ def test_1x128_transposed_small(dg, t, f):
     check(got, oracle.quantize_1x128_transposed(x), f"transposed {t}x{f}")
 
 
+@pytest.mark.parametrize("mode", ["1x128", "128x128", "transposed"])
+def test_extreme_magnitudes(dg, mode):
+    """Group maxima from 2^-130 to 2^120 (scales below 2^-60 take the
+    quotient's rescaled path), fp32 subnormal inputs inside normal groups,
+    negative zeros: still bit-exact."""
+    say(f"quantize extreme magnitudes {mode}")
+    rng = np.random.default_rng(4242)
+    rows, cols = 256, 1024
+    x = rng.standard_normal((rows, cols)).astype(np.float64)
+    if mode == "transposed":
+        e = rng.integers(-130, 120, size=(rows // 128, cols))
+        x = x * np.repeat(2.0 ** e, 128, axis=0)
+    else:
+        e = rng.integers(-130, 120, size=(rows, cols // 128))
+        x = x * np.repeat(2.0 ** e, 128, axis=1)
+    x = x.astype(np.float32)
+    x[5, 3:40] = np.float32(1e-41)       # subnormal values in a normal group
+    x[7, 9] = np.float32(-0.0)
+    amax = np.abs(x).max()
+    assert np.isfinite(amax)
+    if mode == "1x128":
+        got = run(dg.dg_quantize_fp8_1x128, x, (rows, cols), (rows, cols // 128))
+        ref = oracle.quantize_1x128(x)
+    elif mode == "128x128":
+        got = run(dg.dg_quantize_fp8_128x128, x, (rows, cols), (rows // 128, cols // 128))
+        ref = oracle.quantize_128x128(x)
+    else:
+        got = run(dg.dg_quantize_fp8_1x128_transposed, x, (cols, rows), (cols, rows // 128))
+        ref = oracle.quantize_1x128_transposed(x)
+    check(got, ref, f"extreme magnitudes {mode}")
+
+
 @pytest.mark.parametrize("what,rows,cols", [
     ("activations 1x128", 4096, 7168),     # the pages' usage example LHS, [4096, 7168] with [4096, 56] scales
     ("weights 128x128", 2112, 7168),       # its RHS, [2112, 7168] with [17, 56] scales
