@@ -13,8 +13,9 @@ launch stream (the per-shape table); the one with the largest time is the
 "dominant kernel", which is also bracketed by events inside the timed steps,
 and whose roofline fraction is reported from those.  The CPU oracle is
 timed on a bounded sample of the same workload's outputs (`cpu_baseline`).
-Other workloads (contiguous, masked, wgrad, k_grouped_wgrad, small) print a
-line of the same form.  Exactly one JSON line goes to stdout.
+Other workloads (contiguous, masked, wgrad, k_grouped_wgrad, small,
+dense_ue8m0 -- the sweep with power-of-two scales -- and quantize, the FP8
+quantiser in GB/s) print a line of the same form.  Exactly one JSON line goes to stdout.
 
 Before the W warmup steps the step runs untimed for at least half a second so
 the GPU clock has settled when timing starts.  `roofline.traffic` is the
@@ -114,7 +115,9 @@ def _sample_idx(rng, count, *highs):
 
 # ------------------------------------------------------------- workloads ---
 
-def build_dense(small=False):
+def build_dense(small=False, pow2=False):
+    """The dense sweep; pow2: power-of-two (UE8M0) scales through
+    dg_gemm_fp8_nt_ue8m0 (scales applied by the block-scaled MFMA)."""
     import torch
     import moe_grouped_gemm_x128_amd as dg
     from harness import inputs, workloads
@@ -126,17 +129,18 @@ def build_dense(small=False):
         m, n, k = s["m"], s["n"], s["k"]
         mmax = max(x["m"] for x in shapes if x["k"] == k)
         if k not in a_by_k:
-            a, sa = inputs.quantize_1x128(inputs._normal(inputs._rng(seed + k, 0), (mmax, k)))
+            a, sa = inputs.quantize_1x128(inputs._normal(inputs._rng(seed + k, 0), (mmax, k)), pow2)
             a_by_k[k] = (a, sa, _dev(a), _dev(sa))
         if (n, k) not in b_by_nk:
-            b, sb = inputs.quantize_128x128(inputs._normal(inputs._rng(seed + n * 7 + k, 1), (n, k)))
+            b, sb = inputs.quantize_128x128(inputs._normal(inputs._rng(seed + n * 7 + k, 1), (n, k)), pow2)
             b_by_nk[(n, k)] = (b, sb, _dev(b), _dev(sb))
         a, sa, da, dsa = a_by_k[k]
         b, sb, db, dsb = b_by_nk[(n, k)]
         da_m, dsa_m = da[:m], dsa[:m]
         out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
-        fn = (lambda da_m=da_m, dsa_m=dsa_m, db=db, dsb=dsb, out=out:
-              dg.dg_gemm_fp8_nt(da_m, dsa_m, db, dsb, out))
+        gemm = dg.dg_gemm_fp8_nt_ue8m0 if pow2 else dg.dg_gemm_fp8_nt
+        fn = (lambda da_m=da_m, dsa_m=dsa_m, db=db, dsb=dsb, out=out, gemm=gemm:
+              gemm(da_m, dsa_m, db, dsb, out))
         nbytes = m * k + m * (k // 128) * 4 + n * k + ((n + 127) // 128) * (k // 128) * 4 + m * n * 2
 
         def sample(rng, count, a=a[:m], sa=sa[:m], b=b, sb=sb, m=m, n=n):
@@ -144,11 +148,12 @@ def build_dense(small=False):
             r, c = _sample_idx(rng, count, m, n)
             return oracle.gemm_fp8_nt_at(a, sa, b, sb, r, c)
 
-        calls.append(Call(s["name"], 2.0 * m * n * k, nbytes, fn, (sample, k)))
+        calls.append(Call(s["name"] + ("_ue8m0" if pow2 else ""), 2.0 * m * n * k, nbytes, fn, (sample, k)))
     desc = ("dense FP8 NT GEMM sweep: M in {64,128,4096} x (N,K) in {(2112,7168),(24576,1536),"
             "(32768,512),(7168,16384),(4096,7168),(7168,2048)}" if not small else "dense M=128 N=256 K=512")
-    return calls, {"workload": "dense_sweep" if not small else "dense_small", "description": desc,
-                   "shapes": len(calls), "scales": "A 1x128, B 128x128, fp32", "out": "bf16"}
+    name = "dense_small" if small else ("dense_sweep_ue8m0" if pow2 else "dense_sweep")
+    scales = "A 1x128, B 128x128, " + ("power-of-two (UE8M0) values in fp32" if pow2 else "fp32")
+    return calls, {"workload": name, "description": desc, "shapes": len(calls), "scales": scales, "out": "bf16"}
 
 
 def build_contiguous():
@@ -393,7 +398,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="dense",
-                    choices=["dense", "small", "contiguous", "masked", "wgrad", "k_grouped_wgrad", "quantize"])
+                    choices=["dense", "small", "contiguous", "masked", "wgrad", "k_grouped_wgrad", "quantize",
+                             "dense_ue8m0"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--settle-seconds", type=float, default=0.5, help="untimed run before the warmup steps")
@@ -413,7 +419,7 @@ def main():
     builders = {"dense": build_dense, "small": lambda: build_dense(small=True),
                 "contiguous": build_contiguous, "masked": build_masked,
                 "wgrad": build_wgrad, "k_grouped_wgrad": lambda: build_wgrad(kgrouped=True),
-                "quantize": build_quantize}
+                "quantize": build_quantize, "dense_ue8m0": lambda: build_dense(pow2=True)}
     if args.copy_calibration:
         copy_calibration()
         return

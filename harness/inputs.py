@@ -40,11 +40,18 @@ def _encode_e4m3(y: np.ndarray) -> np.ndarray:
     return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
-def quantize_1x128(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+def _pow2_ceil(s: np.ndarray) -> np.ndarray:
+    """The smallest power of two >= s (s > 0, fp32): UE8M0-representable scales."""
+    m, e = np.frexp(s.astype(np.float64))
+    return np.ldexp(1.0, np.where(m == 0.5, e - 1, e)).astype(np.float32)
+
+
+def quantize_1x128(x: np.ndarray, pow2: bool = False) -> tuple[np.ndarray, np.ndarray]:
     """x fp32 [R, K] (K % 128 == 0) -> (q uint8 [R, K], s fp32 [R, K/128]).
 
     One scale per row and 128-wide K group, as the activation operand of the
-    pages' usage example ([M, K] with [M, K//128] scales).
+    pages' usage example ([M, K] with [M, K//128] scales).  pow2: the scale is
+    rounded up to a power of two (UE8M0 scales).
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
     r, k = x.shape
@@ -53,11 +60,13 @@ def quantize_1x128(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     amax = np.abs(g).max(axis=2)
     s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
     s[amax == 0] = np.float32(1.0)
+    if pow2:
+        s = _pow2_ceil(s)
     y = np.clip(g / s[:, :, None], -E4M3_MAX, E4M3_MAX).astype(np.float32)
     return _encode_e4m3(y.reshape(r, k)), s
 
 
-def quantize_128x128(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+def quantize_128x128(x: np.ndarray, pow2: bool = False) -> tuple[np.ndarray, np.ndarray]:
     """x fp32 [N, K] -> (q uint8 [N, K], s fp32 [ceil(N/128), K/128]).
 
     One scale per 128x128 block, the last row block clipped to the rows that
@@ -75,6 +84,8 @@ def quantize_128x128(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
         amax = np.abs(blk).max(axis=(0, 2))
         si = (amax / np.float32(E4M3_MAX)).astype(np.float32)
         si[amax == 0] = np.float32(1.0)
+        if pow2:
+            si = _pow2_ceil(si)
         s[i] = si
         y = np.clip(blk / si[None, :, None], -E4M3_MAX, E4M3_MAX).astype(np.float32)
         q[i * BLOCK_K:(i + 1) * BLOCK_K] = _encode_e4m3(y.reshape(-1, k))
@@ -97,9 +108,9 @@ class Dense:
     sb: np.ndarray
 
 
-def make_dense(m: int, n: int, k: int, seed: int) -> Dense:
-    a, sa = quantize_1x128(_normal(_rng(seed, 0), (m, k)))
-    b, sb = quantize_128x128(_normal(_rng(seed, 1), (n, k)))
+def make_dense(m: int, n: int, k: int, seed: int, pow2: bool = False) -> Dense:
+    a, sa = quantize_1x128(_normal(_rng(seed, 0), (m, k)), pow2)
+    b, sb = quantize_128x128(_normal(_rng(seed, 1), (n, k)), pow2)
     return Dense(m, n, k, a, sa, b, sb)
 
 

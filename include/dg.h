@@ -61,6 +61,17 @@ typedef enum {
 dg_status dg_gemm_fp8_nt(const void* a, const float* sa, const void* b, const float* sb,
                          void* c, int m, int n, int k, hipStream_t stream);
 
+/* Dense FP8 NT GEMM with power-of-two (UE8M0) scales (DeepGEMM pages,
+ * aikraft.ru support table: the newer architecture's scale format is packed
+ * UE8M0, i.e. an 8-bit exponent).  Same operands, layouts and result as
+ * dg_gemm_fp8_nt, but every scale in sa and sb must be an exact power of two
+ * 2^e with -127 <= e <= 127 (stored as fp32): the block-scaled MFMA then
+ * applies sa*sb inside the matrix unit and accumulates in fp32, with no
+ * vector-unit promotion.  Only the exponent field of each scale is read; a
+ * scale that is not such a power of two gives wrong results (no error). */
+dg_status dg_gemm_fp8_nt_ue8m0(const void* a, const float* sa, const void* b, const float* sb,
+                               void* c, int m, int n, int k, hipStream_t stream);
+
 /* MoE grouped GEMM, contiguous layout (DeepGEMM pages, "分组 GEMM": training
  * forward and inference prefill; "使用示例": m_indices gives each LHS row its
  * group).  The rows of all experts are stacked into one LHS:
@@ -153,7 +164,8 @@ typedef enum {
   DG_KIND_CONTIGUOUS = 1,
   DG_KIND_MASKED = 2,
   DG_KIND_WGRAD = 3,
-  DG_KIND_K_GROUPED_WGRAD = 4
+  DG_KIND_K_GROUPED_WGRAD = 4,
+  DG_KIND_DENSE_POW2 = 5      /* dg_gemm_fp8_nt_ue8m0 */
 } dg_kind;
 
 /* Tile configuration the per-shape heuristic picks (DeepGEMM pages: block

@@ -34,11 +34,12 @@ _lib.dg_grouped_fp8_contiguous.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _
 _lib.dg_grouped_fp8_masked.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]
 _lib.dg_wgrad_fp8_nt.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]
 _lib.dg_k_grouped_wgrad_fp8_nt.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]
+_lib.dg_gemm_fp8_nt_ue8m0.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]
 _lib.dg_quantize_fp8_1x128.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
 _lib.dg_quantize_fp8_128x128.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
 _lib.dg_quantize_fp8_1x128_transposed.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
 for _f in ("dg_gemm_fp8_nt", "dg_grouped_fp8_contiguous", "dg_grouped_fp8_masked",
-           "dg_wgrad_fp8_nt", "dg_k_grouped_wgrad_fp8_nt", "dg_quantize_fp8_1x128",
+           "dg_wgrad_fp8_nt", "dg_k_grouped_wgrad_fp8_nt", "dg_gemm_fp8_nt_ue8m0", "dg_quantize_fp8_1x128",
            "dg_quantize_fp8_128x128", "dg_quantize_fp8_1x128_transposed"):
     getattr(_lib, _f).restype = ctypes.c_int
 _lib.dg_status_string.argtypes = [ctypes.c_int]
@@ -55,7 +56,7 @@ class TileConfig(ctypes.Structure):
 _lib.dg_select_config.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(TileConfig)]
 _lib.dg_select_config.restype = ctypes.c_int
 
-KIND_DENSE, KIND_CONTIGUOUS, KIND_MASKED, KIND_WGRAD, KIND_K_GROUPED_WGRAD = range(5)
+KIND_DENSE, KIND_CONTIGUOUS, KIND_MASKED, KIND_WGRAD, KIND_K_GROUPED_WGRAD, KIND_DENSE_POW2 = range(6)
 FP8 = torch.float8_e4m3fn
 
 
@@ -131,6 +132,22 @@ def dg_gemm_fp8_nt(a, sa, b, sb, c):
     _dev(a, sa, b, sb, c)
     _check(_lib.dg_gemm_fp8_nt(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(c), m, n, k, _stream(c)),
            "dg_gemm_fp8_nt")
+    return c
+
+
+def dg_gemm_fp8_nt_ue8m0(a, sa, b, sb, c):
+    """dg_gemm_fp8_nt with power-of-two (UE8M0) scales applied by the
+    block-scaled MFMA (see include/dg.h); sa, sb must be powers of two."""
+    _fp8(a, "a"); _fp8(b, "b"); _f32(sa, "sa"); _f32(sb, "sb")
+    m, k = a.shape
+    n = b.shape[0]
+    _shape(b, (n, k), "b"); _shape(sa, (m, k // 128), "sa"); _shape(sb, ((n + 127) // 128, k // 128), "sb")
+    _shape(c, (m, n), "c")
+    if c.dtype != torch.bfloat16:
+        raise TypeError("c must be bfloat16")
+    _dev(a, sa, b, sb, c)
+    _check(_lib.dg_gemm_fp8_nt_ue8m0(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(c), m, n, k, _stream(c)),
+           "dg_gemm_fp8_nt_ue8m0")
     return c
 
 
@@ -233,6 +250,10 @@ def dg_quantize_fp8_1x128_transposed(x, q, s):
 
 def gemm_fp8_fp8_bf16_nt(lhs, rhs, out):
     return dg_gemm_fp8_nt(lhs[0], lhs[1], rhs[0], rhs[1], out)
+
+
+def gemm_fp8_fp8_bf16_nt_ue8m0(lhs, rhs, out):
+    return dg_gemm_fp8_nt_ue8m0(lhs[0], lhs[1], rhs[0], rhs[1], out)
 
 
 def m_grouped_gemm_fp8_fp8_bf16_nt_contiguous(lhs, rhs, out, m_indices):

@@ -68,7 +68,7 @@ constexpr int kSplitMinBlocks = 12;
 constexpr size_t kMaxWorkspaceBytes = size_t(256) << 20;  // split-K partials per stream
 
 int choose_splits(int kind, int rows, long tiles, int num_cus, int kbs) {
-  if (kind != DG_KIND_DENSE && kind != DG_KIND_MASKED) return 1;
+  if (kind != DG_KIND_DENSE && kind != DG_KIND_MASKED && kind != DG_KIND_DENSE_POW2) return 1;
   if (rows > 256) return 1;  // large M: the extra pass costs more than the idle CUs (measured)
   if (tiles * 10 >= num_cus * 7L) return 1;  // enough tiles already
   long s = (num_cus + tiles - 1) / tiles;
@@ -111,7 +111,8 @@ dg::TileShape heuristic(int kind, int rows, int n, int k, int groups, int num_cu
     const dg::TileShape wide = bm == 64 ? dg::TileShape{64, 128, 1, 4} : dg::TileShape{128, 128, 2, 2};
     const dg::TileShape mid = bm == 64 ? dg::TileShape{64, 64, 1, 4} : dg::TileShape{128, 64, 2, 2};
     const dg::TileShape cands[5] = {wide, mid, {64, 128, 1, 4}, {64, 64, 1, 4}, {64, 32, 2, 2}};
-    const long need = long_k && (kind == DG_KIND_DENSE) ? (num_cus * 7L) / (10L * kSplitTarget)
+    const long need = long_k && (kind == DG_KIND_DENSE || kind == DG_KIND_DENSE_POW2)
+                          ? (num_cus * 7L) / (10L * kSplitTarget)
                                                          : (num_cus * 7L) / 10L;
     for (const auto& c : cands) {
       if (!dg::has_instance(kind, c)) continue;
@@ -186,7 +187,8 @@ dg_status plan(int kind, int rows, int n, int k, int groups, int num_cus, bool a
   const int kbs = k / 128;
   int splits = allow_split ? choose_splits(kind, rows, tiles, num_cus, kbs) : 1;
   if (const char* e = std::getenv("DG_FORCE_SPLITS"))
-    if (allow_split && (kind == DG_KIND_DENSE || kind == DG_KIND_MASKED)) splits = std::atoi(e);
+    if (allow_split && (kind == DG_KIND_DENSE || kind == DG_KIND_MASKED || kind == DG_KIND_DENSE_POW2))
+      splits = std::atoi(e);
   if (splits < 1) splits = 1;
   if (splits > kMaxSplits) splits = kMaxSplits;
   if (splits > kbs) splits = kbs;
@@ -282,7 +284,8 @@ dg_status run(int kind, dg::Params& p, int rows, int n, int k, int groups, hipSt
   int cus = 0;
   if (device_cus(&cus) != 0) return DG_ERROR_LAUNCH;
   (void)hipGetLastError();  // clear a stale error from unrelated work
-  const bool may_split = (kind == DG_KIND_DENSE || kind == DG_KIND_MASKED) && !stream_capturing(stream);
+  const bool may_split = (kind == DG_KIND_DENSE || kind == DG_KIND_MASKED || kind == DG_KIND_DENSE_POW2) &&
+                         !stream_capturing(stream);
   Launch l;
   dg_status st = plan(kind, rows, n, k, groups, cus, may_split, p, l);
   if (st != DG_SUCCESS) return st;
@@ -341,6 +344,28 @@ dg_status dg_gemm_fp8_nt(const void* a, const float* sa, const void* b, const fl
   p.groups = 1;
   p.vec_out = (n % 4 == 0) && aligned(c, 8);
   return run(dg::KIND_DENSE, p, m, n, k, 1, stream);
+}
+
+dg_status dg_gemm_fp8_nt_ue8m0(const void* a, const float* sa, const void* b, const float* sb, void* c,
+                               int m, int n, int k, hipStream_t stream) {
+  if (!a || !sa || !b || !sb || !c) return DG_ERROR_INVALID_VALUE;
+  if (m <= 0 || n <= 0 || k <= 0) return DG_ERROR_INVALID_VALUE;
+  if (k % 128 != 0) return DG_ERROR_UNSUPPORTED;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(sa, 4) || !aligned(sb, 4) || !aligned(c, 2))
+    return DG_ERROR_UNSUPPORTED;
+  dg::Params p = base_params();
+  p.a = static_cast<const uint8_t*>(a);
+  p.sa = sa;
+  p.b = static_cast<const uint8_t*>(b);
+  p.sb = sb;
+  p.out = c;
+  p.m = m;
+  p.n = n;
+  p.lda = k;
+  p.kbs = k / 128;
+  p.groups = 1;
+  p.vec_out = (n % 4 == 0) && aligned(c, 8);
+  return run(dg::KIND_DENSE_POW2, p, m, n, k, 1, stream);
 }
 
 dg_status dg_grouped_fp8_contiguous(const void* a, const float* sa, const void* b, const float* sb,
@@ -464,7 +489,7 @@ const char* dg_status_string(dg_status s) {
 dg_status dg_select_config(int kind, int m, int n, int k, int num_groups, int num_cus,
                            dg_tile_config* out) {
   if (!out) return DG_ERROR_INVALID_VALUE;
-  if (kind < DG_KIND_DENSE || kind > DG_KIND_K_GROUPED_WGRAD) return DG_ERROR_INVALID_VALUE;
+  if (kind < DG_KIND_DENSE || kind > DG_KIND_DENSE_POW2) return DG_ERROR_INVALID_VALUE;
   if (m <= 0 || n <= 0 || k <= 0 || num_groups <= 0 || num_cus <= 0) return DG_ERROR_INVALID_VALUE;
   dg::Params p = base_params();
   Launch l;

@@ -14,6 +14,7 @@ enum Kind : int {
   KIND_MASKED = 2,      // C bf16 [G,Mx,N];   rows < masked_m[g]
   KIND_WGRAD = 3,       // D fp32 [M,N] +=;   B scales per row
   KIND_KGROUPED = 4,    // D fp32 [G,M,N] +=; per-group K ranges
+  KIND_DENSE_POW2 = 5,  // C bf16 [M,N]; power-of-two scales applied by the block-scaled MFMA
 };
 
 constexpr int kMaxKGroups = 256;

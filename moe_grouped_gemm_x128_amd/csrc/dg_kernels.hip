@@ -153,6 +153,19 @@ __device__ __forceinline__ v8i load_frag(const uint8_t* frag_base, uint32_t lo, 
   return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
 }
 
+// Power-of-two scales (UE8M0): the block-scaled MFMA multiplies each 32-wide
+// K chunk of an operand row by 2^(E - 127), E being the 8-bit scale byte the
+// lane holding that chunk supplies (byte 0 of its scale operand), and adds
+// srcC: acc + sb * sa * (block sum), with the scaling applied inside the matrix
+// unit and no vector-unit promotion.  A positive power-of-two fp32 scale
+// 2^(E-127) has E as its exponent field: bits >> 23.
+__device__ __forceinline__ int ue8m0_of(float s) { return (int)(__builtin_bit_cast(uint32_t, s) >> 23); }
+
+__device__ __forceinline__ v4f mfma_block_scaled(const v8i& b_rows, const v8i& a_rows, const v4f& acc, int sb_e,
+                                                 int sa_e) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b_rows, a_rows, acc, 0, 0, 0, sb_e, 0, sa_e);
+}
+
 __device__ __forceinline__ v4f mfma_block(const v8i& b_rows, const v8i& a_rows) {
   // D[n][m] = sum over the 128 k of the block; both operands use the same
   // (lane, byte) -> k assignment, so the sum covers exactly the block.
@@ -168,6 +181,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   constexpr int FM = WTM / 16;   // 16-row fragments per wave
   constexpr int FN = WTN / 16;   // 16-column fragments per wave
   constexpr bool kRowScaleB = (KIND == KIND_WGRAD || KIND == KIND_KGROUPED);
+  constexpr bool kPow2 = (KIND == KIND_DENSE_POW2);  // scales applied by the MFMA
   constexpr bool kFp32Out = kRowScaleB;
   // the columns of one wave tile sit inside one 128-block: one sb per wave
   constexpr bool kWaveUniformSb = !kRowScaleB && (kBK % WTN == 0) && (BN % WTN == 0);
@@ -235,7 +249,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     }
   }
   // split-K: `splits` consecutive work items share one output tile
-  constexpr bool kCanSplit = (KIND == KIND_DENSE || KIND == KIND_MASKED);
+  constexpr bool kCanSplit = (KIND == KIND_DENSE || KIND == KIND_MASKED || KIND == KIND_DENSE_POW2);
   const int splits = kCanSplit ? p.splits : 1;
   const int TS = T * splits;
   const int per_xcd = (TS + 7) >> 3;
@@ -678,12 +692,20 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
           }
   #pragma unroll
           for (int r = 0; r < NR; ++r) {
-            part[r] = kStreamM ? mfma_block(res[r], cur) : mfma_block(cur, res[r]);
-            if (r + 1 < NR) {
-              if (o > 0)
-                promote(o - 1, r + 1, true);
-              else
-                promote_pending(r + 1);
+            if constexpr (kPow2) {
+              // B fragment i carries sb, A fragment j carries its rows' sa
+              const int j = kStreamM ? o : r, i = kStreamM ? r : o;
+              const float sa = kStreamM ? sa_cur : sav[kStreamM ? 0 : j];
+              acc_at(o, r) = kStreamM ? mfma_block_scaled(res[r], cur, acc_at(o, r), ue8m0_of(sbv[i]), ue8m0_of(sa))
+                                      : mfma_block_scaled(cur, res[r], acc_at(o, r), ue8m0_of(sbv[i]), ue8m0_of(sa));
+            } else {
+              part[r] = kStreamM ? mfma_block(res[r], cur) : mfma_block(cur, res[r]);
+              if (r + 1 < NR) {
+                if (o > 0)
+                  promote(o - 1, r + 1, true);
+                else
+                  promote_pending(r + 1);
+              }
             }
           }
           // this group's share of the next block's DMAs (spread over the first
@@ -691,7 +713,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
           constexpr int kSpread = NOV / 2 > 0 ? NOV / 2 : 1;
           if (o < kSpread)
             issue_ahead(rel, (o * ND) / kSpread, ((o + 1) * ND) / kSpread);
-          promote(o, 0, false);
+          if constexpr (!kPow2) promote(o, 0, false);
           sa_prev = sa_cur;
           cur = nxt;
           // keep each group's loads, MFMAs and FMAs together: no fragment
@@ -700,7 +722,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
         }
         // the rest of the last group is promoted during the next block
   #pragma unroll
-        for (int r = 0; r < NR && NOV > 0; ++r) {
+        for (int r = 0; r < NR && NOV > 0 && !kPow2; ++r) {
           const int j = kStreamM ? NOV - 1 : r, i = kStreamM ? r : NOV - 1;
           const float sa = kStreamM ? sa_prev : sav[kStreamM ? 0 : j];
           if constexpr (kRowScaleB) {
@@ -712,7 +734,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
         }
       }
   #pragma unroll
-      for (int r = 1; r < NR && NOV > 0; ++r) {
+      for (int r = 1; r < NR && NOV > 0 && !kPow2; ++r) {
         if constexpr (kRowScaleB)
           fma4q(acc_at(NOV - 1, r), pend[r], pendq[r], part[r]);
         else
@@ -910,6 +932,9 @@ hipError_t launch_shape(int kind, const Params& p, int grid, hipStream_t stream)
       break;
     case KIND_KGROUPED:
       launch_kind<BM, BN, WM, WN, S, KIND_KGROUPED>(g, b, stream, p);
+      break;
+    case KIND_DENSE_POW2:
+      launch_kind<BM, BN, WM, WN, S, KIND_DENSE_POW2>(g, b, stream, p);
       break;
     default:
       return hipErrorInvalidValue;
@@ -1245,7 +1270,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const Params p, int 
 }  // namespace
 
 bool has_instance(int kind, const TileShape& s) {
-  if (kind < KIND_DENSE || kind > KIND_KGROUPED) return false;
+  if (kind < KIND_DENSE || kind > KIND_DENSE_POW2) return false;
 #define X(BM, BN, WM, WN, S) \
   if (s.bm == BM && s.bn == BN && s.wm == WM && s.wn == WN) return !excluded(BM, BN, WM, kind);
   DG_SHAPES(X)
@@ -1273,7 +1298,7 @@ hipError_t launch_masked_bdirect(const Params& p, int grid, hipStream_t stream) 
 }
 
 hipError_t launch_splitk_reduce(int kind, const Params& p, hipStream_t stream) {
-  if (kind != KIND_DENSE && kind != KIND_MASKED) return hipErrorInvalidValue;
+  if (kind != KIND_DENSE && kind != KIND_MASKED && kind != KIND_DENSE_POW2) return hipErrorInvalidValue;
   const int64_t items = (int64_t)p.groups * p.m * ((p.n + 3) / 4);
   const int64_t blocks = (items + 255) / 256;
   const int grid = (int)(blocks < 4096 ? (blocks > 0 ? blocks : 1) : 4096);

@@ -102,6 +102,17 @@ def test_grouped_argument_errors(lib):
     assert m(A16, A16, A16, A16, A16, A16, 2, 256, 8, 200, None) == UNSUPPORTED
 
 
+def test_ue8m0_argument_errors(lib):
+    f = lib.dg_gemm_fp8_nt_ue8m0
+    f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 3 + [ctypes.c_void_p]
+    assert f(None, A16, A16, A16, A16, 1, 1, 128, None) == INVALID
+    assert f(A16, A16, A16, A16, None, 1, 1, 128, None) == INVALID
+    assert f(A16, A16, A16, A16, A16, 0, 1, 128, None) == INVALID
+    assert f(A16, A16, A16, A16, A16, 1, 1, 100, None) == UNSUPPORTED   # K % 128
+    assert f(MIS, A16, A16, A16, A16, 1, 1, 128, None) == UNSUPPORTED   # a alignment
+    assert f(A16, A16 + 2, A16, A16, A16, 1, 1, 128, None) == UNSUPPORTED
+
+
 def test_quantizer_argument_errors(lib):
     vp, i = ctypes.c_void_p, ctypes.c_int
     for name in ("dg_quantize_fp8_1x128", "dg_quantize_fp8_128x128", "dg_quantize_fp8_1x128_transposed"):
