@@ -304,3 +304,28 @@ def quantize_1x128_transposed(x: np.ndarray):
     _check(lib().dgo_quantize_1x128_transposed(_p(x), _I(t), _I(f), _p(q), _p(s)),
            "quantize_1x128_transposed")
     return q, s
+
+
+# ---- BF16 NT GEMM (dg_oracle.c) ----
+
+def gemm_bf16_nt(a, b):
+    """A [M,K], B [N,K] bf16 bit patterns (uint16) -> (C bf16 bits [M,N], exact-sum fp64 [M,N])."""
+    a, b = _c(a, np.uint16), _c(b, np.uint16)
+    m, k = a.shape
+    n = b.shape[0]
+    c = np.empty((m, n), np.uint16)
+    x = np.empty((m, n), np.float64)
+    _check(lib().dgo_gemm_bf16_nt(_p(a), _p(b), _I(m), _I(n), _I(k), _p(c), _p(x)), "gemm_bf16_nt")
+    return c, x
+
+
+def gemm_bf16_nt_at(a, b, rows, cols):
+    """Unrounded fp64 values of the sampled outputs (rows[i], cols[i])."""
+    a, b = _c(a, np.uint16), _c(b, np.uint16)
+    rows, cols = _c(rows, np.int64), _c(cols, np.int64)
+    m, k = a.shape
+    n = b.shape[0]
+    out = np.empty(rows.shape, np.float64)
+    _check(lib().dgo_gemm_bf16_nt_at(_p(a), _p(b), _I(m), _I(n), _I(k), _p(rows), _p(cols), _I(rows.size),
+                                     _p(out)), "gemm_bf16_nt_at")
+    return out

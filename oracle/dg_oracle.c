@@ -419,3 +419,51 @@ int dgo_k_grouped_wgrad_at(const uint8_t* a, const float* sa, const uint8_t* b,
   free(kb_start);
   return 0;
 }
+
+/* ---- BF16 NT GEMM ---------------------------------------------------------
+ * The pages list BF16 GEMM beside FP8 (aikraft.ru, support table: formats FP8,
+ * FP4, BF16; DeepSeek DeepGEMM 中文讲解, "未来计划": BF16 support).  Same NT
+ * layouts, no scales:
+ *
+ *   C[m,n] = bf16( sum_k A[m,k] * B[n,k] ),  A [M,K], B [N,K] bf16, C [M,N] bf16
+ *
+ * A bf16 value is the fp32 value whose upper 16 bits it holds, exact in fp64;
+ * each product (8 x 8 significant bits) is exact in fp64; the K products are
+ * added in ascending k in fp64 (rounding error below k * 2^-53 * sum|terms|,
+ * far below half a bf16 step except within that distance of a tie); one
+ * rounding to bf16 (round to nearest even). */
+static double bf16_value(uint16_t h) {
+  const uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+static double bf16_element(const uint16_t* arow, const uint16_t* brow, int64_t k) {
+  double acc = 0.0;
+  for (int64_t t = 0; t < k; ++t) acc += bf16_value(arow[t]) * bf16_value(brow[t]);
+  return acc;
+}
+
+int dgo_gemm_bf16_nt(const uint16_t* a, const uint16_t* b, int64_t m, int64_t n, int64_t k, uint16_t* c,
+                     double* c_exact) {
+  if (m < 0 || n < 0 || k < 0) return -1;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < m; ++i)
+    for (int64_t j = 0; j < n; ++j) {
+      const double v = bf16_element(a + i * k, b + j * k, k);
+      if (c_exact) c_exact[i * n + j] = v;
+      c[i * n + j] = round_bf16(v);
+    }
+  return 0;
+}
+
+/* the elements (rows[i], cols[i]) only, unrounded */
+int dgo_gemm_bf16_nt_at(const uint16_t* a, const uint16_t* b, int64_t m, int64_t n, int64_t k,
+                        const int64_t* rows, const int64_t* cols, int64_t count, double* out) {
+  for (int64_t i = 0; i < count; ++i)
+    if (rows[i] < 0 || rows[i] >= m || cols[i] < 0 || cols[i] >= n) return -1;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < count; ++i) out[i] = bf16_element(a + rows[i] * k, b + cols[i] * k, k);
+  return 0;
+}
