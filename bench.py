@@ -14,8 +14,9 @@ launch stream (the per-shape table); the one with the largest time is the
 and whose roofline fraction is reported from those.  The CPU oracle is
 timed on a bounded sample of the same workload's outputs (`cpu_baseline`).
 Other workloads (contiguous, masked, wgrad, k_grouped_wgrad, small,
-dense_ue8m0 -- the sweep with power-of-two scales -- and quantize, the FP8
-quantiser in GB/s) print a line of the same form.  Exactly one JSON line goes to stdout.
+dense_ue8m0 -- the sweep with power-of-two scales --, bf16 -- the sweep's
+shapes in BF16 against the bf16 peak -- and quantize, the FP8 quantiser in
+GB/s) print a line of the same form.  Exactly one JSON line goes to stdout.
 
 Before the W warmup steps the step runs untimed for at least half a second so
 the GPU clock has settled when timing starts.  `roofline.traffic` is the
@@ -42,8 +43,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "FP8 block-scaled GEMM TFLOPS (dense/grouped) and % of MI355X FP8 or HBM peak"
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
-RIDGE = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 
 
 def log(msg):
@@ -96,12 +97,13 @@ def copy_calibration():
 class Call:
     """One GEMM launch of the step plus its algorithmic work."""
 
-    def __init__(self, name, flops, nbytes, fn, sample=None):
+    def __init__(self, name, flops, nbytes, fn, sample=None, peak=PEAK_FP8_TFLOPS):
         self.name, self.flops, self.bytes, self.fn, self.sample = name, flops, nbytes, fn, sample
+        self.peak = peak  # dense MFMA peak of the launch's arithmetic type, TFLOP/s
 
     @property
     def bound(self):
-        return "mfma" if self.flops / self.bytes >= RIDGE else "hbm"
+        return "mfma" if self.flops / self.bytes >= self.peak * 1e12 / (PEAK_HBM_GBS * 1e9) else "hbm"
 
 
 def _dev(x):
@@ -216,6 +218,43 @@ def build_wgrad(kgrouped=False):
     calls = [Call(s["name"], 2.0 * w.m * w.n * t, nbytes, fn, None)]
     return calls, {"workload": s["name"], "description":
                    f"weight gradient D[{w.m},{w.n}] += over tokens {w.ks}, 1x128 scales on both operands, fp32 D"}
+
+
+def build_bf16():
+    """The dense sweep's shapes in BF16 (dg_gemm_bf16_nt): N(0,1) operands
+    rounded to bf16, no scales; roofline against the bf16 dense peak."""
+    import torch
+    import moe_grouped_gemm_x128_amd as dg
+    from harness import inputs, workloads
+
+    shapes = workloads.dense_sweep()
+    seed = shapes[0]["seed"]
+    a_by_k, b_by_nk, calls = {}, {}, []
+    to_dev = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+    for s in shapes:
+        m, n, k = s["m"], s["n"], s["k"]
+        mmax = max(x["m"] for x in shapes if x["k"] == k)
+        if k not in a_by_k:
+            a = inputs._to_bf16_bits(inputs._normal(inputs._rng(seed + k, 0), (mmax, k)))
+            a_by_k[k] = (a, to_dev(a))
+        if (n, k) not in b_by_nk:
+            b = inputs._to_bf16_bits(inputs._normal(inputs._rng(seed + n * 7 + k, 1), (n, k)))
+            b_by_nk[(n, k)] = (b, to_dev(b))
+        a, da = a_by_k[k]
+        b, db = b_by_nk[(n, k)]
+        da_m = da[:m]
+        out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        fn = lambda da_m=da_m, db=db, out=out: dg.dg_gemm_bf16_nt(da_m, db, out)
+        nbytes = 2 * (m * k + n * k + m * n)
+
+        def sample(rng, count, a=a[:m], b=b, m=m, n=n):
+            import oracle
+            r, c = _sample_idx(rng, count, m, n)
+            return oracle.gemm_bf16_nt_at(a, b, r, c)
+
+        calls.append(Call(s["name"] + "_bf16", 2.0 * m * n * k, nbytes, fn, (sample, k), peak=PEAK_BF16_TFLOPS))
+    return calls, {"workload": "dense_sweep_bf16", "description": "the dense sweep's 18 shapes in BF16",
+                   "shapes": len(calls), "scales": "none", "out": "bf16"}
 
 
 QUANT_METRIC = "FP8 quantiser GB/s (absmax/448 fp32 scales) and % of MI355X HBM peak"
@@ -399,7 +438,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="dense",
                     choices=["dense", "small", "contiguous", "masked", "wgrad", "k_grouped_wgrad", "quantize",
-                             "dense_ue8m0"])
+                             "dense_ue8m0", "bf16"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--settle-seconds", type=float, default=0.5, help="untimed run before the warmup steps")
@@ -419,7 +458,7 @@ def main():
     builders = {"dense": build_dense, "small": lambda: build_dense(small=True),
                 "contiguous": build_contiguous, "masked": build_masked,
                 "wgrad": build_wgrad, "k_grouped_wgrad": lambda: build_wgrad(kgrouped=True),
-                "quantize": build_quantize, "dense_ue8m0": lambda: build_dense(pow2=True)}
+                "quantize": build_quantize, "dense_ue8m0": lambda: build_dense(pow2=True), "bf16": build_bf16}
     if args.copy_calibration:
         copy_calibration()
         return
@@ -438,13 +477,13 @@ def main():
     for c, ms in zip(calls, per_ms):
         tf = c.flops / (ms * 1e-3) / 1e12
         gbs = c.bytes / (ms * 1e-3) / 1e9
-        frac = tf / PEAK_FP8_TFLOPS if c.bound == "mfma" else gbs / PEAK_HBM_GBS
+        frac = tf / c.peak if c.bound == "mfma" else gbs / PEAK_HBM_GBS
         shapes.append({"name": c.name, "us": round(ms * 1e3, 2), "tflops": round(tf, 1),
                        "gbs": round(gbs, 1), "bound": c.bound, "frac": round(frac, 4)})
         log(f"{c.name:52s} {ms * 1e3:9.1f} us {tf:8.1f} TFLOP/s {gbs:8.1f} GB/s {c.bound} {frac:.3f}")
     dc = calls[dom]
     if dc.bound == "mfma":
-        achieved, peak, unit = dc.flops / (dms * 1e-3) / 1e12, PEAK_FP8_TFLOPS, "TFLOP/s"
+        achieved, peak, unit = dc.flops / (dms * 1e-3) / 1e12, dc.peak, "TFLOP/s"
     else:
         achieved, peak, unit = dc.bytes / (dms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
     roofline = {"bound": dc.bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
@@ -462,8 +501,10 @@ def main():
             QUANT_METRIC, "f32"
         data = "synthetic (seeded N(0,1) fp32)"
     else:
-        value, unit, metric, dtype = step_flops / (ms_per_step * 1e-3) / 1e12, "TFLOP/s", METRIC, "fp8"
-        data = "synthetic (seeded N(0,1), e4m3-quantised)"
+        bf16 = args.workload == "bf16"
+        value, unit, metric, dtype = step_flops / (ms_per_step * 1e-3) / 1e12, "TFLOP/s", METRIC, \
+            "bf16" if bf16 else "fp8"
+        data = "synthetic (seeded N(0,1), bf16)" if bf16 else "synthetic (seeded N(0,1), e4m3-quantised)"
     line = {"metric": metric, "value": round(value, 2),
             "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",

@@ -114,6 +114,28 @@ def make_dense(m: int, n: int, k: int, seed: int, pow2: bool = False) -> Dense:
     return Dense(m, n, k, a, sa, b, sb)
 
 
+@dataclass
+class DenseBf16:
+    """Dense BF16 NT problem: A [M,K], B [N,K] as bf16 bit patterns (uint16)."""
+    m: int
+    n: int
+    k: int
+    a: np.ndarray
+    b: np.ndarray
+
+
+def _to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns via torch's CPU cast (round to nearest even)."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def make_dense_bf16(m: int, n: int, k: int, seed: int) -> DenseBf16:
+    """N(0,1) operands rounded to bf16 (the same seeded streams as make_dense)."""
+    return DenseBf16(m, n, k, _to_bf16_bits(_normal(_rng(seed, 0), (m, k))),
+                     _to_bf16_bits(_normal(_rng(seed, 1), (n, k))))
+
+
 def _grouped_rhs(g: int, n: int, k: int, seed: int) -> tuple[np.ndarray, np.ndarray]:
     nb = (n + BLOCK_K - 1) // BLOCK_K
     b = np.empty((g, n, k), dtype=np.uint8)

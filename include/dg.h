@@ -72,6 +72,16 @@ dg_status dg_gemm_fp8_nt(const void* a, const float* sa, const void* b, const fl
 dg_status dg_gemm_fp8_nt_ue8m0(const void* a, const float* sa, const void* b, const float* sb,
                                void* c, int m, int n, int k, hipStream_t stream);
 
+/* Dense BF16 NT GEMM (DeepGEMM pages: aikraft.ru lists BF16 GEMM beside FP8
+ * in its support table; DeepSeek DeepGEMM 中文讲解, "未来计划": BF16 support).
+ * The same scheduler, operand staging and layouts as the FP8 path, with bf16
+ * MFMAs accumulating in fp32 and no scales:
+ *   a [M,K] bf16, b [N,K] bf16, c [M,N] bf16 = round-to-nearest-even(sum_k a*b),
+ *   every element written.
+ * M, N >= 1; K >= 64, K % 64 == 0 and K <= 2^22. */
+dg_status dg_gemm_bf16_nt(const void* a, const void* b, void* c, int m, int n, int k,
+                          hipStream_t stream);
+
 /* MoE grouped GEMM, contiguous layout (DeepGEMM pages, "分组 GEMM": training
  * forward and inference prefill; "使用示例": m_indices gives each LHS row its
  * group).  The rows of all experts are stacked into one LHS:

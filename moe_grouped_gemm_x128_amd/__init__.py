@@ -35,11 +35,12 @@ _lib.dg_grouped_fp8_masked.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
 _lib.dg_wgrad_fp8_nt.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]
 _lib.dg_k_grouped_wgrad_fp8_nt.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]
 _lib.dg_gemm_fp8_nt_ue8m0.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]
+_lib.dg_gemm_bf16_nt.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _vp]
 _lib.dg_quantize_fp8_1x128.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
 _lib.dg_quantize_fp8_128x128.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
 _lib.dg_quantize_fp8_1x128_transposed.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
 for _f in ("dg_gemm_fp8_nt", "dg_grouped_fp8_contiguous", "dg_grouped_fp8_masked",
-           "dg_wgrad_fp8_nt", "dg_k_grouped_wgrad_fp8_nt", "dg_gemm_fp8_nt_ue8m0", "dg_quantize_fp8_1x128",
+           "dg_wgrad_fp8_nt", "dg_k_grouped_wgrad_fp8_nt", "dg_gemm_fp8_nt_ue8m0", "dg_gemm_bf16_nt", "dg_quantize_fp8_1x128",
            "dg_quantize_fp8_128x128", "dg_quantize_fp8_1x128_transposed"):
     getattr(_lib, _f).restype = ctypes.c_int
 _lib.dg_status_string.argtypes = [ctypes.c_int]
@@ -151,6 +152,19 @@ def dg_gemm_fp8_nt_ue8m0(a, sa, b, sb, c):
     return c
 
 
+def dg_gemm_bf16_nt(a, b, c):
+    """C[M,N] bf16 = A[M,K] bf16 . B[N,K]^T bf16, fp32 accumulation (see include/dg.h)."""
+    for t, name in ((a, "a"), (b, "b"), (c, "c")):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    m, k = a.shape
+    n = b.shape[0]
+    _shape(b, (n, k), "b"); _shape(c, (m, n), "c")
+    _dev(a, b, c)
+    _check(_lib.dg_gemm_bf16_nt(_ptr(a), _ptr(b), _ptr(c), m, n, k, _stream(c)), "dg_gemm_bf16_nt")
+    return c
+
+
 def dg_grouped_fp8_contiguous(a, sa, b, sb, c, m_indices):
     _fp8(a, "a"); _fp8(b, "b"); _f32(sa, "sa"); _f32(sb, "sb")
     m_total, k = a.shape
@@ -254,6 +268,10 @@ def gemm_fp8_fp8_bf16_nt(lhs, rhs, out):
 
 def gemm_fp8_fp8_bf16_nt_ue8m0(lhs, rhs, out):
     return dg_gemm_fp8_nt_ue8m0(lhs[0], lhs[1], rhs[0], rhs[1], out)
+
+
+def gemm_bf16_bf16_bf16_nt(lhs, rhs, out):
+    return dg_gemm_bf16_nt(lhs, rhs, out)
 
 
 def m_grouped_gemm_fp8_fp8_bf16_nt_contiguous(lhs, rhs, out, m_indices):

@@ -49,6 +49,12 @@ int occupancy(int kind, const dg::TileShape& s) {
   return occ < 1 ? 1 : occ;
 }
 
+// Dense kinds (C [M,N] bf16, one group, K may be split): FP8 with fp32 or
+// power-of-two scales, and BF16.
+bool dense_like(int kind) {
+  return kind == DG_KIND_DENSE || kind == DG_KIND_DENSE_POW2 || kind == dg::KIND_BF16;
+}
+
 bool parse_forced(dg::TileShape* s) {
   const char* e = std::getenv("DG_FORCE_TILE");
   if (!e || !*e) return false;
@@ -68,7 +74,7 @@ constexpr int kSplitMinBlocks = 12;
 constexpr size_t kMaxWorkspaceBytes = size_t(256) << 20;  // split-K partials per stream
 
 int choose_splits(int kind, int rows, long tiles, int num_cus, int kbs) {
-  if (kind != DG_KIND_DENSE && kind != DG_KIND_MASKED && kind != DG_KIND_DENSE_POW2) return 1;
+  if (kind != DG_KIND_DENSE && kind != DG_KIND_MASKED && !dense_like(kind)) return 1;
   if (rows > 256) return 1;  // large M: the extra pass costs more than the idle CUs (measured)
   if (tiles * 10 >= num_cus * 7L) return 1;  // enough tiles already
   long s = (num_cus + tiles - 1) / tiles;
@@ -111,7 +117,7 @@ dg::TileShape heuristic(int kind, int rows, int n, int k, int groups, int num_cu
     const dg::TileShape wide = bm == 64 ? dg::TileShape{64, 128, 1, 4} : dg::TileShape{128, 128, 2, 2};
     const dg::TileShape mid = bm == 64 ? dg::TileShape{64, 64, 1, 4} : dg::TileShape{128, 64, 2, 2};
     const dg::TileShape cands[5] = {wide, mid, {64, 128, 1, 4}, {64, 64, 1, 4}, {64, 32, 2, 2}};
-    const long need = long_k && (kind == DG_KIND_DENSE || kind == DG_KIND_DENSE_POW2)
+    const long need = long_k && dense_like(kind)
                           ? (num_cus * 7L) / (10L * kSplitTarget)
                                                          : (num_cus * 7L) / 10L;
     for (const auto& c : cands) {
@@ -187,7 +193,7 @@ dg_status plan(int kind, int rows, int n, int k, int groups, int num_cus, bool a
   const int kbs = k / 128;
   int splits = allow_split ? choose_splits(kind, rows, tiles, num_cus, kbs) : 1;
   if (const char* e = std::getenv("DG_FORCE_SPLITS"))
-    if (allow_split && (kind == DG_KIND_DENSE || kind == DG_KIND_MASKED || kind == DG_KIND_DENSE_POW2))
+    if (allow_split && (dense_like(kind) || kind == DG_KIND_MASKED))
       splits = std::atoi(e);
   if (splits < 1) splits = 1;
   if (splits > kMaxSplits) splits = kMaxSplits;
@@ -284,7 +290,7 @@ dg_status run(int kind, dg::Params& p, int rows, int n, int k, int groups, hipSt
   int cus = 0;
   if (device_cus(&cus) != 0) return DG_ERROR_LAUNCH;
   (void)hipGetLastError();  // clear a stale error from unrelated work
-  const bool may_split = (kind == DG_KIND_DENSE || kind == DG_KIND_MASKED || kind == DG_KIND_DENSE_POW2) &&
+  const bool may_split = (dense_like(kind) || kind == DG_KIND_MASKED) &&
                          !stream_capturing(stream);
   Launch l;
   dg_status st = plan(kind, rows, n, k, groups, cus, may_split, p, l);
@@ -366,6 +372,25 @@ dg_status dg_gemm_fp8_nt_ue8m0(const void* a, const float* sa, const void* b, co
   p.groups = 1;
   p.vec_out = (n % 4 == 0) && aligned(c, 8);
   return run(dg::KIND_DENSE_POW2, p, m, n, k, 1, stream);
+}
+
+dg_status dg_gemm_bf16_nt(const void* a, const void* b, void* c, int m, int n, int k, hipStream_t stream) {
+  if (!a || !b || !c) return DG_ERROR_INVALID_VALUE;
+  if (m <= 0 || n <= 0 || k <= 0) return DG_ERROR_INVALID_VALUE;
+  if (k % 64 != 0 || k > (1 << 22)) return DG_ERROR_UNSUPPORTED;  // 32-bit byte ranges per tile
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, 2)) return DG_ERROR_UNSUPPORTED;
+  dg::Params p = base_params();
+  p.a = static_cast<const uint8_t*>(a);
+  p.b = static_cast<const uint8_t*>(b);
+  p.out = c;
+  p.m = m;
+  p.n = n;
+  p.lda = 2 * k;    // bytes per row
+  p.kbs = k / 64;   // 128-byte K blocks
+  p.groups = 1;
+  p.vec_out = (n % 4 == 0) && aligned(c, 8);
+  // the planner counts K in bytes / 128: pass the row length in bytes
+  return run(dg::KIND_BF16, p, m, n, 2 * k, 1, stream);
 }
 
 dg_status dg_grouped_fp8_contiguous(const void* a, const float* sa, const void* b, const float* sb,

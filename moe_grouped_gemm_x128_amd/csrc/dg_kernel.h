@@ -15,6 +15,8 @@ enum Kind : int {
   KIND_WGRAD = 3,       // D fp32 [M,N] +=;   B scales per row
   KIND_KGROUPED = 4,    // D fp32 [G,M,N] +=; per-group K ranges
   KIND_DENSE_POW2 = 5,  // C bf16 [M,N]; power-of-two scales applied by the block-scaled MFMA
+  KIND_BF16 = 6,        // C bf16 [M,N] = A bf16 [M,K] . B bf16 [N,K]^T; no scales; a "K block" is
+                        // 128 bytes = 64 values (lda = 2K bytes, kbs = K/64)
 };
 
 constexpr int kMaxKGroups = 256;

@@ -82,13 +82,14 @@ __device__ __forceinline__ Rsrc buffer_rsrc(const void* base, uint32_t num_bytes
               (uint32_t)__builtin_amdgcn_readfirstlane(num_bytes), 0x00020000u};
 }
 
-// The resource moved `bytes` further along (bytes <= num), with its range cut
-// to zero unless `live`: the range check still ends where the original one
-// did, and a dead resource reads zeros without touching memory.
+// The resource moved `bytes` further along, with its range cut to zero unless
+// `live` and bytes < num: the range check still ends where the original one
+// did, and a dead or exhausted resource reads zeros without touching memory
+// (the range never wraps below zero).
 __device__ __forceinline__ v4i at(const Rsrc& r, uint32_t bytes, bool live) {
   const uint64_t b = (((uint64_t)r.hi << 32) | r.lo) + bytes;
-  return v4i{(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xffffu), (int)(live ? r.num - bytes : 0u),
-             (int)r.flags};
+  const uint32_t num = __builtin_amdgcn_readfirstlane(live && bytes < r.num ? r.num - bytes : 0u);  // wave-uniform
+  return v4i{(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xffffu), (int)num, (int)r.flags};
 }
 
 #pragma clang diagnostic push
@@ -166,6 +167,21 @@ __device__ __forceinline__ v4f mfma_block_scaled(const v8i& b_rows, const v8i& a
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b_rows, a_rows, acc, 0, 0, 0, sb_e, 0, sa_e);
 }
 
+// BF16: a lane's 32 fragment bytes are 16 bf16 values of its row; the two
+// halves feed two 16x16x32 bf16 MFMAs that accumulate into `acc` (both
+// operands use the same lane -> k assignment, so the pair covers the 64 values
+// of the 128-byte K block).
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ v4f mfma_block_bf16(const v8i& b_rows, const v8i& a_rows, const v4f& acc) {
+  const v8bf b0 = __builtin_bit_cast(v8bf, v4i{b_rows[0], b_rows[1], b_rows[2], b_rows[3]});
+  const v8bf b1 = __builtin_bit_cast(v8bf, v4i{b_rows[4], b_rows[5], b_rows[6], b_rows[7]});
+  const v8bf a0 = __builtin_bit_cast(v8bf, v4i{a_rows[0], a_rows[1], a_rows[2], a_rows[3]});
+  const v8bf a1 = __builtin_bit_cast(v8bf, v4i{a_rows[4], a_rows[5], a_rows[6], a_rows[7]});
+  const v4f d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0, a0, acc, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1, a1, d, 0, 0, 0);
+}
+
 __device__ __forceinline__ v4f mfma_block(const v8i& b_rows, const v8i& a_rows) {
   // D[n][m] = sum over the 128 k of the block; both operands use the same
   // (lane, byte) -> k assignment, so the sum covers exactly the block.
@@ -182,6 +198,8 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   constexpr int FN = WTN / 16;   // 16-column fragments per wave
   constexpr bool kRowScaleB = (KIND == KIND_WGRAD || KIND == KIND_KGROUPED);
   constexpr bool kPow2 = (KIND == KIND_DENSE_POW2);  // scales applied by the MFMA
+  constexpr bool kBf16 = (KIND == KIND_BF16);         // no scales at all
+  constexpr bool kDirectAcc = kPow2 || kBf16;         // MFMAs accumulate into acc: no promotion
   constexpr bool kFp32Out = kRowScaleB;
   // the columns of one wave tile sit inside one 128-block: one sb per wave
   constexpr bool kWaveUniformSb = !kRowScaleB && (kBK % WTN == 0) && (BN % WTN == 0);
@@ -249,7 +267,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     }
   }
   // split-K: `splits` consecutive work items share one output tile
-  constexpr bool kCanSplit = (KIND == KIND_DENSE || KIND == KIND_MASKED || KIND == KIND_DENSE_POW2);
+  constexpr bool kCanSplit = (KIND == KIND_DENSE || KIND == KIND_MASKED || KIND == KIND_DENSE_POW2 || kBf16);
   const int splits = kCanSplit ? p.splits : 1;
   const int TS = T * splits;
   const int per_xcd = (TS + 7) >> 3;
@@ -387,17 +405,18 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     const int bg = (KIND == KIND_KGROUPED) ? 0 : x.g;  // K-grouped: one B [N,T]
     const int bcols = max(0, min(BN, p.n - x.n0));      // valid B rows (output columns)
     const uint32_t on = x.live ? 1u : 0u;
+    const uint32_t son = kBf16 ? 0u : on;  // BF16: the scale pieces read nothing
     Res r;
     r.a = buffer_rsrc(p.a + x.a_row0 * (int64_t)p.lda, on * (uint32_t)x.rows * p.lda);
     r.b = buffer_rsrc(p.b + ((int64_t)bg * p.n + x.n0) * (int64_t)p.lda, on * (uint32_t)bcols * p.lda);
-    r.sa = buffer_rsrc(p.sa + x.a_row0 * (int64_t)p.kbs, on * (uint32_t)x.rows * p.kbs * 4);
+    r.sa = buffer_rsrc(p.sa + x.a_row0 * (int64_t)p.kbs, son * (uint32_t)x.rows * p.kbs * 4);
     if constexpr (kRowScaleB) {
       r.sb = buffer_rsrc(p.sb + (int64_t)x.n0 * p.kbs, on * (uint32_t)bcols * p.kbs * 4);
     } else {
       // only the 128-column blocks the tile touches
       const int nb0 = x.n0 / kBK;
       const int nbt = min(nb_rows - nb0, (x.n0 - nb0 * kBK + BN + kBK - 1) / kBK);  // a tile may straddle blocks
-      r.sb = buffer_rsrc(p.sb + ((int64_t)x.g * nb_rows + nb0) * p.kbs, on * (uint32_t)max(nbt, 0) * p.kbs * 4);
+      r.sb = buffer_rsrc(p.sb + ((int64_t)x.g * nb_rows + nb0) * p.kbs, son * (uint32_t)max(nbt, 0) * p.kbs * 4);
     }
     r.kb0 = x.kb0;
     r.nkb = x.live ? x.nkb : 0;
@@ -489,7 +508,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
       for (int q = 0; q < QS; ++q) {
         if (QA + QB + q < lo || QA + QB + q >= hi) continue;
         const int sp = wave + NW * q;  // scale piece: sa rows 64*sp.., then sb
-        const bool is_a = sp < PSA, real = sp < PS && live;
+        const bool is_a = sp < PSA, real = sp < PS && live && !kBf16;  // BF16 has no scales
         // select the sa or sb resource arithmetically (a select here is lowered
         // to an indexed stack array)
         const uint32_t f = (uint32_t)__builtin_amdgcn_readfirstlane(is_a ? 1 : 0);
@@ -692,7 +711,10 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
           }
   #pragma unroll
           for (int r = 0; r < NR; ++r) {
-            if constexpr (kPow2) {
+            if constexpr (kBf16) {
+              acc_at(o, r) = kStreamM ? mfma_block_bf16(res[r], cur, acc_at(o, r))
+                                      : mfma_block_bf16(cur, res[r], acc_at(o, r));
+            } else if constexpr (kPow2) {
               // B fragment i carries sb, A fragment j carries its rows' sa
               const int j = kStreamM ? o : r, i = kStreamM ? r : o;
               const float sa = kStreamM ? sa_cur : sav[kStreamM ? 0 : j];
@@ -713,7 +735,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
           constexpr int kSpread = NOV / 2 > 0 ? NOV / 2 : 1;
           if (o < kSpread)
             issue_ahead(rel, (o * ND) / kSpread, ((o + 1) * ND) / kSpread);
-          if constexpr (!kPow2) promote(o, 0, false);
+          if constexpr (!kDirectAcc) promote(o, 0, false);
           sa_prev = sa_cur;
           cur = nxt;
           // keep each group's loads, MFMAs and FMAs together: no fragment
@@ -722,7 +744,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
         }
         // the rest of the last group is promoted during the next block
   #pragma unroll
-        for (int r = 0; r < NR && NOV > 0 && !kPow2; ++r) {
+        for (int r = 0; r < NR && NOV > 0 && !kDirectAcc; ++r) {
           const int j = kStreamM ? NOV - 1 : r, i = kStreamM ? r : NOV - 1;
           const float sa = kStreamM ? sa_prev : sav[kStreamM ? 0 : j];
           if constexpr (kRowScaleB) {
@@ -734,7 +756,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
         }
       }
   #pragma unroll
-      for (int r = 1; r < NR && NOV > 0 && !kPow2; ++r) {
+      for (int r = 1; r < NR && NOV > 0 && !kDirectAcc; ++r) {
         if constexpr (kRowScaleB)
           fma4q(acc_at(NOV - 1, r), pend[r], pendq[r], part[r]);
         else
@@ -936,6 +958,9 @@ hipError_t launch_shape(int kind, const Params& p, int grid, hipStream_t stream)
     case KIND_DENSE_POW2:
       launch_kind<BM, BN, WM, WN, S, KIND_DENSE_POW2>(g, b, stream, p);
       break;
+    case KIND_BF16:
+      launch_kind<BM, BN, WM, WN, S, KIND_BF16>(g, b, stream, p);
+      break;
     default:
       return hipErrorInvalidValue;
   }
@@ -1066,7 +1091,8 @@ __global__ __launch_bounds__(512) void masked_bdirect_kernel(const Params p) {
       const bool live = rel < nkb;
       const uint32_t koff = __builtin_amdgcn_readfirstlane((kb0 + rel) * kBK);
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)((((uint64_t)rsB.hi << 32) | rsB.lo) + koff), (short)0, (int)(live ? rsB.num - koff : 0u),
+          (void*)((((uint64_t)rsB.hi << 32) | rsB.lo) + koff), (short)0,
+          (int)(live && koff < rsB.num ? rsB.num - koff : 0u),  // a wave past N reads nothing
           (int)rsB.flags);
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
@@ -1270,7 +1296,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const Params p, int 
 }  // namespace
 
 bool has_instance(int kind, const TileShape& s) {
-  if (kind < KIND_DENSE || kind > KIND_DENSE_POW2) return false;
+  if (kind < KIND_DENSE || kind > KIND_BF16) return false;
 #define X(BM, BN, WM, WN, S) \
   if (s.bm == BM && s.bn == BN && s.wm == WM && s.wn == WN) return !excluded(BM, BN, WM, kind);
   DG_SHAPES(X)
@@ -1298,7 +1324,8 @@ hipError_t launch_masked_bdirect(const Params& p, int grid, hipStream_t stream) 
 }
 
 hipError_t launch_splitk_reduce(int kind, const Params& p, hipStream_t stream) {
-  if (kind != KIND_DENSE && kind != KIND_MASKED && kind != KIND_DENSE_POW2) return hipErrorInvalidValue;
+  if (kind != KIND_DENSE && kind != KIND_MASKED && kind != KIND_DENSE_POW2 && kind != KIND_BF16)
+    return hipErrorInvalidValue;
   const int64_t items = (int64_t)p.groups * p.m * ((p.n + 3) / 4);
   const int64_t blocks = (items + 255) / 256;
   const int grid = (int)(blocks < 4096 ? (blocks > 0 ? blocks : 1) : 4096);

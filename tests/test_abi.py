@@ -102,6 +102,18 @@ def test_grouped_argument_errors(lib):
     assert m(A16, A16, A16, A16, A16, A16, 2, 256, 8, 200, None) == UNSUPPORTED
 
 
+def test_bf16_argument_errors(lib):
+    f = lib.dg_gemm_bf16_nt
+    f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 3 + [ctypes.c_void_p]
+    assert f(None, A16, A16, 1, 1, 64, None) == INVALID
+    assert f(A16, A16, None, 1, 1, 64, None) == INVALID
+    assert f(A16, A16, A16, 1, 0, 64, None) == INVALID
+    assert f(A16, A16, A16, 1, 1, 96, None) == UNSUPPORTED    # K % 64
+    assert f(A16, A16, A16, 1, 1, 1 << 23, None) == UNSUPPORTED
+    assert f(MIS, A16, A16, 1, 1, 64, None) == UNSUPPORTED    # a alignment
+    assert f(A16, A16, MIS, 1, 1, 64, None) == UNSUPPORTED    # c alignment
+
+
 def test_ue8m0_argument_errors(lib):
     f = lib.dg_gemm_fp8_nt_ue8m0
     f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 3 + [ctypes.c_void_p]
