@@ -26,6 +26,8 @@ known size), stored in profiles/; it is reported only while the kernel sources
 hash to the version the counters were taken on, else null.
 
     python bench.py --only NAME[,NAME]   time only the named GEMMs (for counters)
+    python bench.py --cold               per-launch table with cold caches (512 MB
+                                         flush before each call, outside its events)
     python bench.py --copy-calibration   run a plain 1 GiB device-to-device copy
 """
 from __future__ import annotations
@@ -340,17 +342,22 @@ def cpu_baseline_quantize(calls, seconds):
 
 # --------------------------------------------------------------- timing ---
 
-def per_call_times(calls, steps):
+def per_call_times(calls, steps, cold=False):
     """Mean duration (ms) of each GEMM: HIP events around every call on the
     launch stream, over `steps` passes.  Used for the per-shape table and to
     find the dominant GEMM; not the timed steps (each event record takes GPU
-    time between kernels that a real caller would not spend)."""
+    time between kernels that a real caller would not spend).  cold: a 512 MB
+    buffer (more than the 256 MB MALL plus the L2s) is overwritten before each
+    call, outside its event pair, so every call starts with cold caches."""
     import torch
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if cold else None
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
           for _ in range(steps)]
     torch.cuda.synchronize()
     for s in range(steps):
         for i, c in enumerate(calls):
+            if cold:
+                flush.fill_(s & 0xff)
             ev[s][i][0].record()
             c.fn()
             ev[s][i][1].record()
@@ -359,7 +366,7 @@ def per_call_times(calls, steps):
     return per.mean(axis=0)
 
 
-def time_steps(calls, steps, warmup, settle_s=0.5):
+def time_steps(calls, steps, warmup, settle_s=0.5, cold=False):
     """Returns (total ms of the K timed steps, per-call mean ms, index of the
     dominant call, its mean ms inside the timed steps).
 
@@ -375,7 +382,7 @@ def time_steps(calls, steps, warmup, settle_s=0.5):
         for c in calls:
             c.fn()
         torch.cuda.synchronize()
-    per_ms = per_call_times(calls, steps)
+    per_ms = per_call_times(calls, steps, cold)
     dom = int(np.argmax(per_ms))
     for _ in range(warmup):
         for c in calls:
@@ -444,6 +451,8 @@ def main():
     ap.add_argument("--settle-seconds", type=float, default=0.5, help="untimed run before the warmup steps")
     ap.add_argument("--only", default="", help="comma-separated GEMM names to time (others skipped)")
     ap.add_argument("--copy-calibration", action="store_true", help="run the counter-calibration copy and exit")
+    ap.add_argument("--cold", action="store_true",
+                    help="per-launch table with a 512 MB cache flush before each call (the timed steps are unchanged)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -469,7 +478,9 @@ def main():
         assert calls, f"--only matched none of the workload's GEMMs"
         config = dict(config, only=sorted(keep))
     log(f"{len(calls)} GEMMs per step; timing {args.steps} steps after {args.warmup} warmup")
-    total_ms, per_ms, dom, dms = time_steps(calls, args.steps, args.warmup, args.settle_seconds)
+    total_ms, per_ms, dom, dms = time_steps(calls, args.steps, args.warmup, args.settle_seconds, args.cold)
+    if args.cold:
+        config = dict(config, per_launch="cold caches (512 MB flush before each call)")
     ms_per_step = total_ms / args.steps
     step_flops = sum(c.flops for c in calls)
 
