@@ -98,6 +98,12 @@ __device__ __forceinline__ void dma16(uint32_t lds, v4i rsrc, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :: "s"(lds), "v"(voff), "s"(rsrc) : "memory", "m0");
 }
+// The same with the nontemporal (streaming) cache policy, for operands read
+// once per output tile row or column (see kStreamB).
+__device__ __forceinline__ void dma16_nt(uint32_t lds, v4i rsrc, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
 __device__ __forceinline__ void dma4(uint32_t lds, v4i rsrc, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                :: "s"(lds), "v"(voff), "s"(rsrc) : "memory", "m0");
@@ -199,6 +205,16 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   constexpr bool kRowScaleB = (KIND == KIND_WGRAD || KIND == KIND_KGROUPED);
   constexpr bool kPow2 = (KIND == KIND_DENSE_POW2);  // scales applied by the MFMA
   constexpr bool kBf16 = (KIND == KIND_BF16);         // no scales at all
+  // B loaded with the streaming (nontemporal) cache policy by the instances
+  // whose launches read each B tile with one row of tiles: the dense tiles of
+  // at most 128 rows (the heuristic's choice for M <= 128) and the masked
+  // layout's tall tiles (one tile covers a group's rows).  Measured faster
+  // there (dense M=64 x 7168 x 16384 +60%, masked decode +17-24%) and slower
+  // where several row tiles re-read the same B (large-M dense -5 to -13%,
+  // contiguous -4%).  Decided per instance at compile time: a runtime choice
+  // in the DMA loop cost the 256x256 instances registers (spills in the loop).
+  constexpr bool kStreamB =
+      ((KIND == KIND_DENSE || KIND == KIND_DENSE_POW2 || kBf16) && BM <= 128) || KIND == KIND_MASKED;
   constexpr bool kDirectAcc = kPow2 || kBf16;         // MFMAs accumulate into acc: no promotion
   constexpr bool kFp32Out = kRowScaleB;
   // the columns of one wave tile sit inside one 128-block: one sb per wave
@@ -494,7 +510,10 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
         if (QA + q < lo || QA + q >= hi) continue;
         const int pi = wave + NW * q;
         if constexpr (PB % NW == 0) {
-          dma16(base + OFF_B + pi * 1024, rb, voff0 + q * step);
+          if constexpr (kStreamB)
+            dma16_nt(base + OFF_B + pi * 1024, rb, voff0 + q * step);
+          else
+            dma16(base + OFF_B + pi * 1024, rb, voff0 + q * step);
         } else {
           // past the last B piece: read nothing into the sink
           const bool real = pi < PB;
@@ -1097,8 +1116,9 @@ __global__ __launch_bounds__(512) void masked_bdirect_kernel(const Params p) {
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
         const uint32_t off = bvoff + (uint32_t)(16 * f) * p.lda;
-        const v4i lo = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-        const v4i hi = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
+        // (cache policy 2 = nontemporal: each expert's B is streamed once)
+        const v4i lo = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
+        const v4i hi = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 2));
         dst[f] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
     };
