@@ -36,6 +36,7 @@ namespace dg {
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float f4nt __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kBK = 128;      // K block = scale granularity
@@ -581,7 +582,11 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
           const int n = n0 + wn * WTN + 16 * i + 4 * lq;
           if (n >= p.n) continue;
           if (p.vec_out && n + 3 < p.n) {
-            const float4 v = *reinterpret_cast<const float4*>(d + n);
+            // D is read once and written once per tile: streaming (nontemporal)
+            // accesses keep it from displacing the operands (weight gradient +6%,
+            // K-grouped +10%; the same for bf16 C stores made other kinds slower)
+            const f4nt t = __builtin_nontemporal_load(reinterpret_cast<const f4nt*>(d + n));
+            const float4 v = float4{t[0], t[1], t[2], t[3]};
             acc[i][j] = v4f{v.x, v.y, v.z, v.w};
           } else {
 #pragma unroll
@@ -908,7 +913,8 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
         if constexpr (kFp32Out) {
           float* d = static_cast<float*>(p.out) + orow * p.n + n;
           if (p.vec_out && n + 3 < p.n) {
-            *reinterpret_cast<float4*>(d) = float4{acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+            __builtin_nontemporal_store(f4nt{acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]},
+                                        reinterpret_cast<f4nt*>(d));
           } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
