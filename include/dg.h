@@ -175,7 +175,8 @@ typedef enum {
   DG_KIND_MASKED = 2,
   DG_KIND_WGRAD = 3,
   DG_KIND_K_GROUPED_WGRAD = 4,
-  DG_KIND_DENSE_POW2 = 5      /* dg_gemm_fp8_nt_ue8m0 */
+  DG_KIND_DENSE_POW2 = 5,     /* dg_gemm_fp8_nt_ue8m0 */
+  DG_KIND_BF16 = 6            /* dg_gemm_bf16_nt (k counts bf16 values) */
 } dg_kind;
 
 /* Tile configuration the per-shape heuristic picks (DeepGEMM pages: block

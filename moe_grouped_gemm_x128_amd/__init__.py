@@ -57,7 +57,7 @@ class TileConfig(ctypes.Structure):
 _lib.dg_select_config.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(TileConfig)]
 _lib.dg_select_config.restype = ctypes.c_int
 
-KIND_DENSE, KIND_CONTIGUOUS, KIND_MASKED, KIND_WGRAD, KIND_K_GROUPED_WGRAD, KIND_DENSE_POW2 = range(6)
+KIND_DENSE, KIND_CONTIGUOUS, KIND_MASKED, KIND_WGRAD, KIND_K_GROUPED_WGRAD, KIND_DENSE_POW2, KIND_BF16 = range(7)
 FP8 = torch.float8_e4m3fn
 
 

@@ -52,7 +52,7 @@ int occupancy(int kind, const dg::TileShape& s) {
 // Dense kinds (C [M,N] bf16, one group, K may be split): FP8 with fp32 or
 // power-of-two scales, and BF16.
 bool dense_like(int kind) {
-  return kind == DG_KIND_DENSE || kind == DG_KIND_DENSE_POW2 || kind == dg::KIND_BF16;
+  return kind == DG_KIND_DENSE || kind == DG_KIND_DENSE_POW2 || kind == DG_KIND_BF16;
 }
 
 bool parse_forced(dg::TileShape* s) {
@@ -514,12 +514,14 @@ const char* dg_status_string(dg_status s) {
 dg_status dg_select_config(int kind, int m, int n, int k, int num_groups, int num_cus,
                            dg_tile_config* out) {
   if (!out) return DG_ERROR_INVALID_VALUE;
-  if (kind < DG_KIND_DENSE || kind > DG_KIND_DENSE_POW2) return DG_ERROR_INVALID_VALUE;
+  if (kind < DG_KIND_DENSE || kind > DG_KIND_BF16) return DG_ERROR_INVALID_VALUE;
   if (m <= 0 || n <= 0 || k <= 0 || num_groups <= 0 || num_cus <= 0) return DG_ERROR_INVALID_VALUE;
+  if (kind == DG_KIND_BF16 && k > (1 << 22)) return DG_ERROR_UNSUPPORTED;
   dg::Params p = base_params();
   Launch l;
   const int groups = (kind == DG_KIND_MASKED || kind == DG_KIND_K_GROUPED_WGRAD) ? num_groups : 1;
-  dg_status st = plan(kind, m, n, k, groups, num_cus, true, p, l);
+  // the planner counts K in 128-byte blocks: BF16 rows are 2K bytes long
+  dg_status st = plan(kind, m, n, kind == DG_KIND_BF16 ? 2 * k : k, groups, num_cus, true, p, l);
   if (st != DG_SUCCESS) return st;
   out->block_m = l.shape.bm;
   out->block_n = l.shape.bn;

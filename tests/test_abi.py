@@ -183,6 +183,7 @@ SHAPES = [(0, m, n, k, 1) for m in (1, 64, 128, 4096)
           for (n, k) in [(2112, 7168), (24576, 1536), (32768, 512), (7168, 16384), (4096, 7168), (7168, 2048)]]
 SHAPES += [(1, 32768, 4096, 7168, 4), (1, 65536, 7168, 2048, 8), (2, 256, 4096, 7168, 1),
            (2, 256, 7168, 2048, 16), (3, 7168, 2048, 4096, 1), (4, 7168, 2048, 10240, 4)]
+SHAPES += [(5, m, 7168, 16384, 1) for m in (64, 4096)] + [(6, m, 7168, 8192, 1) for m in (64, 4096)]
 
 
 @pytest.mark.parametrize("kind,m,n,k,g", SHAPES)
@@ -195,9 +196,9 @@ def test_heuristic_invariants(lib, kind, m, n, k, g):
     assert c["tiles"] == tiles
     s = c["k_splits"]
     assert 1 <= s <= 16
-    if kind not in (0, 2):
+    if kind not in (0, 2, 5, 6):
         assert s == 1  # split K only for the bf16-output dense and masked layouts
-    kbs = k // 128
+    kbs = k // 64 if kind == 6 else k // 128  # BF16: K blocks of 64 values (128 bytes)
     if s > 1:
         chunk = -(-kbs // s)
         assert -(-kbs // chunk) == s, "a split would be empty"
@@ -229,6 +230,7 @@ def test_heuristic_rejects_bad_queries(lib):
     out = c()
     lib.dg_select_config.argtypes = [ctypes.c_int] * 6 + [ctypes.c_void_p]
     assert lib.dg_select_config(9, 1, 1, 128, 1, 256, ctypes.addressof(out)) == INVALID
+    assert lib.dg_select_config(7, 1, 1, 128, 1, 256, ctypes.addressof(out)) == INVALID
     assert lib.dg_select_config(0, 0, 1, 128, 1, 256, ctypes.addressof(out)) == INVALID
     assert lib.dg_select_config(0, 1, 1, 128, 1, 256, None) == INVALID
 
