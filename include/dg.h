@@ -35,6 +35,12 @@
  *   - device-resident control data (m_indices, masked_m) cannot be checked on
  *     the host; out-of-range values mean "skip": a row whose expert id is not
  *     in [0, G) is left untouched, masked_m[g] is clamped to [0, M_max].
+ *   - environment overrides for tests and tuning, read at each call:
+ *     DG_FORCE_TILE=BMxBNxWMxWN forces a tile instance (UNSUPPORTED if the kind
+ *     has none), DG_FORCE_SPLITS=s forces s K splits where splitting is
+ *     allowed, DG_MASKED_BDIRECT=0|1 forces the masked layout off / onto the
+ *     decode kernel that streams B into registers, DG_LOG=1 prints each plan
+ *     to stderr.  Results stay within the same accuracy bound either way.
  */
 #ifndef DG_MI355X_H
 #define DG_MI355X_H
