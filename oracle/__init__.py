@@ -329,3 +329,18 @@ def gemm_bf16_nt_at(a, b, rows, cols):
     _check(lib().dgo_gemm_bf16_nt_at(_p(a), _p(b), _I(m), _I(n), _I(k), _p(rows), _p(cols), _I(rows.size),
                                      _p(out)), "gemm_bf16_nt_at")
     return out
+
+
+# ---- SwiGLU then 1x128 quantise (dg_quant_oracle.c) ----
+
+def swiglu_quantize_1x128(c: np.ndarray):
+    """c bf16 bits (uint16) [M, 2I], gate = c[:, :I], up = c[:, I:] ->
+    (q uint8 [M, I], s fp32 [M, I/128], h fp64 [M, I] before its fp32 rounding)."""
+    c = _c(c, np.uint16)
+    m, i2 = c.shape
+    i = i2 // 2
+    q = np.empty((m, i), np.uint8)
+    s = np.empty((m, i // 128), np.float32)
+    h = np.empty((m, i), np.float64)
+    _check(lib().dgo_swiglu_quantize_1x128(_p(c), _I(m), _I(i), _p(q), _p(s), _p(h)), "swiglu_quantize_1x128")
+    return q, s, h

@@ -34,6 +34,7 @@
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
+#include <string.h>
 
 #define QG 128
 #define E4M3_LARGEST 448.0f
@@ -123,5 +124,50 @@ int dgo_quantize_1x128_transposed(const float* x, int64_t t, int64_t f, uint8_t*
     for (int64_t j = 0; j < f; ++j) xt[j * t + i] = x[i * f + j];
   const int rc = dgo_quantize_1x128(xt, f, t, q, s);
   free(xt);
+  return rc;
+}
+
+/* ---- SwiGLU on the first linear's output, then the 1x128 rule ----------
+ *
+ * DeepGEMM pages (the Russian overview "DeepSeek выложила в открытый доступ
+ * библиотеку…", section "Ключевые функции: Mega MoE и индексация": Mega MoE
+ * runs an expert's first linear layer, the SwiGLU activation and the second
+ * linear layer in one kernel).  Between the two FP8 GEMMs the
+ * activation's output must be re-quantised, since the second GEMM takes FP8
+ * operands with 1x128 scales.  Reading taken (the pages give no layout):
+ *
+ *   c [M, 2I] bf16, the first GEMM's output; gate g = c[:, 0:I],
+ *   up u = c[:, I:2I] (the two halves of the stacked projection);
+ *   h = silu(g) * u,  silu(x) = x / (1 + e^-x)   evaluated in fp64,
+ *   rounded once to fp32, then the 1x128 rule above on h [M, I]:
+ *   q [M, I] e4m3, s [M, I/128] fp32.
+ *
+ * h_exact (optional, [M, I] fp64) receives h before the fp32 rounding. */
+static double bf16_to_double(uint16_t bits) {
+  const uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+static double silu(double x) { return x / (1.0 + exp(-x)); }
+
+int dgo_swiglu_quantize_1x128(const uint16_t* c, int64_t m, int64_t i, uint8_t* q, float* s,
+                              double* h_exact) {
+  if (m < 0 || i < 0 || i % QG) return -1;
+  float* h = (float*)malloc(sizeof(float) * (size_t)(m * i > 0 ? m * i : 1));
+  if (!h) return -2;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < m; ++r) {
+    const uint16_t* gate = c + r * 2 * i;
+    const uint16_t* up = gate + i;
+    for (int64_t j = 0; j < i; ++j) {
+      const double v = silu(bf16_to_double(gate[j])) * bf16_to_double(up[j]);
+      if (h_exact) h_exact[r * i + j] = v;
+      h[r * i + j] = (float)v;
+    }
+  }
+  const int rc = dgo_quantize_1x128(h, m, i, q, s);
+  free(h);
   return rc;
 }
