@@ -170,6 +170,26 @@ dg_status dg_quantize_fp8_128x128(const float* x, void* q, float* s, int n, int 
 dg_status dg_quantize_fp8_1x128_transposed(const float* x, void* q, float* s, int t, int f,
                                            hipStream_t stream);
 
+/* ---- SwiGLU + FP8 re-quantise between an expert's two linear layers -----
+ * DeepGEMM pages (the Russian overview, "Ключевые функции: Mega MoE и
+ * индексация": Mega MoE fuses an expert's first linear layer, SwiGLU and the
+ * second linear layer; the second FP8 GEMM needs its input re-quantised with
+ * 1x128 scales).  The column layout is a reading, the pages give none:
+ *   c [M, 2I] bf16, the first GEMM's output: gate = c[:, 0:I], up = c[:, I:2I]
+ *   h = silu(gate) * up = gate / (1 + e^-gate) * up, in fp32
+ *   q [M, I] fp8 e4m3, s [M, I/128] fp32: the 1x128 rule of
+ *   dg_quantize_fp8_1x128 applied to h (amax / 448, s = 1 for a zero group).
+ * h carries a few fp32 ulp of the exponential's error and the quotient is
+ * h * RN(1/s), so a code can differ from exact evaluation where h / s lies
+ * within about 2^-20 (relative) of the midpoint between two e4m3 values; the
+ * scales match exact evaluation to within the same relative margin.
+ * Every row is independent (grouped layouts pass their whole row range;
+ * padding rows get codes of whatever they hold).  Inputs must keep h finite
+ * in fp32.  c 16-byte aligned, q 8-byte, s 4-byte.  M >= 1; I >= 128,
+ * I % 128 == 0, 2I fits an int.  Every output element is written. */
+dg_status dg_swiglu_quantize_fp8_1x128(const void* c, void* q, float* s, int m, int i,
+                                       hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* dg_status_string(dg_status s);
 

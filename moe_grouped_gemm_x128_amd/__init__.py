@@ -39,9 +39,10 @@ _lib.dg_gemm_bf16_nt.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _vp]
 _lib.dg_quantize_fp8_1x128.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
 _lib.dg_quantize_fp8_128x128.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
 _lib.dg_quantize_fp8_1x128_transposed.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
+_lib.dg_swiglu_quantize_fp8_1x128.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
 for _f in ("dg_gemm_fp8_nt", "dg_grouped_fp8_contiguous", "dg_grouped_fp8_masked",
            "dg_wgrad_fp8_nt", "dg_k_grouped_wgrad_fp8_nt", "dg_gemm_fp8_nt_ue8m0", "dg_gemm_bf16_nt", "dg_quantize_fp8_1x128",
-           "dg_quantize_fp8_128x128", "dg_quantize_fp8_1x128_transposed"):
+           "dg_quantize_fp8_128x128", "dg_quantize_fp8_1x128_transposed", "dg_swiglu_quantize_fp8_1x128"):
     getattr(_lib, _f).restype = ctypes.c_int
 _lib.dg_status_string.argtypes = [ctypes.c_int]
 _lib.dg_status_string.restype = ctypes.c_char_p
@@ -100,6 +101,11 @@ def _fp8(t, name):
 def _f32(t, name):
     if t.dtype != torch.float32:
         raise TypeError(f"{name} must be float32, got {t.dtype}")
+
+
+def _bf16(t, name):
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
 
 
 def _shape(t, shape, name):
@@ -260,6 +266,19 @@ def dg_quantize_fp8_1x128_transposed(x, q, s):
     return q, s
 
 
+def dg_swiglu_quantize_fp8_1x128(c, q, s):
+    """c bf16 [M,2I] (gate | up) -> q fp8 [M,I], s fp32 [M,I/128]: SwiGLU then
+    the 1x128 quantise (see include/dg.h)."""
+    _bf16(c, "c"); _fp8(q, "q"); _f32(s, "s")
+    _dev(c, q, s)
+    m, i2 = c.shape
+    i = i2 // 2
+    _shape(q, (m, i), "q"); _shape(s, (m, i // 128), "s")
+    _check(_lib.dg_swiglu_quantize_fp8_1x128(_ptr(c), _ptr(q), _ptr(s), m, i, _stream(c)),
+           "dg_swiglu_quantize_fp8_1x128")
+    return q, s
+
+
 # ------------------------------------------------------ page-style names ---
 
 def gemm_fp8_fp8_bf16_nt(lhs, rhs, out):
@@ -309,3 +328,12 @@ def quantize_fp8_1x128_transposed(x):
     t, f = x.shape
     return dg_quantize_fp8_1x128_transposed(x, torch.empty((f, t), dtype=FP8, device=x.device),
                                             torch.empty((f, t // 128), dtype=torch.float32, device=x.device))
+
+
+def swiglu_quantize_fp8_1x128(c):
+    """Second-GEMM operand from the first GEMM's bf16 output c [M,2I]:
+    (fp8 silu(gate)*up [M,I], fp32 scales [M,I/128])."""
+    m, i2 = c.shape
+    i = i2 // 2
+    return dg_swiglu_quantize_fp8_1x128(c, torch.empty((m, i), dtype=FP8, device=c.device),
+                                        torch.empty((m, i // 128), dtype=torch.float32, device=c.device))

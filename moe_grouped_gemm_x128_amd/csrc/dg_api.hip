@@ -2,6 +2,7 @@
 // tile heuristic and kernel dispatch.  Validation runs before any HIP call, so
 // every error path can be exercised on a machine without a GPU.
 #include <atomic>
+#include <climits>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -557,6 +558,20 @@ dg_status dg_quantize_fp8_1x128_transposed(const float* x, void* q, float* s, in
   if (t % 128 != 0 || f % 4 != 0) return DG_ERROR_UNSUPPORTED;
   if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4)) return DG_ERROR_UNSUPPORTED;
   return quantize(2, x, q, s, t, f, stream);
+}
+
+dg_status dg_swiglu_quantize_fp8_1x128(const void* c, void* q, float* s, int m, int i, hipStream_t stream) {
+  if (!c || !q || !s) return DG_ERROR_INVALID_VALUE;
+  if (m <= 0 || i <= 0) return DG_ERROR_INVALID_VALUE;
+  if (i % 128 != 0 || i > INT_MAX / 2) return DG_ERROR_UNSUPPORTED;
+  if (!aligned(c, 16) || !aligned(q, 8) || !aligned(s, 4)) return DG_ERROR_UNSUPPORTED;
+  int cus = 0;
+  if (device_cus(&cus) != 0) return DG_ERROR_LAUNCH;
+  (void)hipGetLastError();  // clear a stale error from unrelated work
+  if (dg::launch_swiglu_quantize(static_cast<const uint16_t*>(c), static_cast<uint8_t*>(q), s, m, i, cus, stream) !=
+      hipSuccess)
+    return DG_ERROR_LAUNCH;
+  return DG_SUCCESS;
 }
 
 int dg_version(void) { return 100; }

@@ -75,6 +75,7 @@ __device__ __forceinline__ float max_xor(float v, int mask) { return fmaxf(v, __
 // (measured: 15% faster on [65536, 7168], 40% on [4096, 7168]).
 typedef float f4nt __attribute__((ext_vector_type(4)));
 typedef unsigned u4nt __attribute__((ext_vector_type(4)));
+typedef unsigned u2nt __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float4 load_nt(const float* p) {
   const f4nt t = __builtin_nontemporal_load(reinterpret_cast<const f4nt*>(p));
@@ -231,7 +232,98 @@ __global__ __launch_bounds__(kQThreads) void quant_rows_kernel(const float* __re
   }
 }
 
+// ---- SwiGLU on the first linear's output, then the 1x128 rule ----------
+// c [M, 2I] bf16 holds the gate projection in columns [0, I) and the up
+// projection in [I, 2I); h = silu(gate) * up [M, I] is quantised in 1x128
+// groups, which are consecutive 128-byte runs of the flat q [M, I].  16 lanes
+// share a group, each with 8 gate and 8 up values (one 16-byte load of each),
+// so a wave covers 4 groups per pass and 16 per step (16 KB in flight).
+// Per element the work is about 18 VALU cycles (two of them transcendental
+// at quarter rate), close to the ~24 per element that HBM speed allows.
+// h carries the exp unit's error (a few fp32 ulp), so the quotient is
+// h * RN(1/s) instead of the exact division of the plain quantiser: codes
+// differ from exact evaluation only where h / s lies within a few ulp of a
+// rounding midpoint between two e4m3 values.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// silu(g) = g / (1 + e^-g): e^-g = 2^(-g log2 e) on the exp unit, then one
+// reciprocal.  Large negative g gives e = inf and silu = -0; large positive
+// g gives e = 0 and silu = g.
+__device__ __forceinline__ float silu(float g) {
+  const float e = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);
+  return g * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+__global__ __launch_bounds__(kQThreads) void swiglu_quant_kernel(const uint16_t* __restrict__ c,
+                                                                 uint8_t* __restrict__ q, float* __restrict__ s,
+                                                                 int64_t groups, int64_t groups_per_row) {
+  const int lane = threadIdx.x & 63;
+  const int sub = lane & 15;
+  const int64_t half = groups_per_row * kQ;  // I, in elements
+  const int64_t waves = (int64_t)gridDim.x * (kQThreads / 64);
+  const int64_t chunks = (groups + 15) / 16;
+  for (int64_t ch = (int64_t)blockIdx.x * (kQThreads / 64) + (threadIdx.x >> 6); ch < chunks; ch += waves) {
+    u4nt gv[4], uv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t g = ch * 16 + 4 * j + (lane >> 4);
+      if (g < groups) {
+        // row r's gate group gi starts at r * 2I + gi * 128 = (g + r * I/128) * 128
+        const uint16_t* p = c + (g + g / groups_per_row * groups_per_row) * kQ + sub * 8;
+        gv[j] = __builtin_nontemporal_load(reinterpret_cast<const u4nt*>(p));
+        uv[j] = __builtin_nontemporal_load(reinterpret_cast<const u4nt*>(p + half));
+      } else {
+        gv[j] = u4nt{0u, 0u, 0u, 0u};
+        uv[j] = u4nt{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float h[8];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        h[2 * t] = silu(bf16_lo(gv[j][t])) * bf16_lo(uv[j][t]);
+        h[2 * t + 1] = silu(bf16_hi(gv[j][t])) * bf16_hi(uv[j][t]);
+      }
+      float m = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) m = fmaxf(m, fabsf(h[t]));
+      m = max_xor(m, 8);
+      m = max_xor(m, 4);
+      m = max_xor(m, 2);
+      m = max_xor(m, 1);
+      const float sc = scale_of(m);
+      // a scale below 2^-60 is raised by 2^64 (h alike, exactly) so that
+      // 1/s stays finite
+      const float k = sc < 0x1p-60f ? 0x1p64f : 1.0f;
+      const float r = 1.0f / (sc * k);
+      float y[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) y[t] = fminf(fmaxf(h[t] * k * r, -kE4m3Max), kE4m3Max);
+      const int64_t g = ch * 16 + 4 * j + (lane >> 4);
+      if (g < groups) {
+        if (sub == 0) s[g] = sc;
+        const u2nt w = {encode4(y[0], y[1], y[2], y[3]), encode4(y[4], y[5], y[6], y[7])};
+        __builtin_nontemporal_store(w, reinterpret_cast<u2nt*>(q + g * kQ + sub * 8));
+      }
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_swiglu_quantize(const uint16_t* c, uint8_t* q, float* s, int rows, int half_cols, int num_cus,
+                                  hipStream_t stream) {
+  const int64_t gpr = half_cols / kQ;
+  const int64_t groups = (int64_t)rows * gpr;
+  if (groups <= 0) return hipSuccess;
+  const int64_t wgs = (groups + 16 * (kQThreads / 64) - 1) / (16 * (kQThreads / 64));
+  const int64_t cap = (int64_t)(num_cus > 0 ? num_cus : 256) * 8;
+  const int grid = (int)(wgs < cap ? wgs : cap);
+  hipLaunchKernelGGL(swiglu_quant_kernel, dim3(grid), dim3(kQThreads), 0, stream, c, q, s, groups, gpr);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize(int mode, const float* x, uint8_t* q, float* s, int rows, int cols, int num_cus,
                            hipStream_t stream) {

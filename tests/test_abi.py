@@ -148,6 +148,22 @@ def test_quantizer_argument_errors(lib):
     assert qt(A16, A16 + 4, A16, 128, 128, None) == UNSUPPORTED           # q 16-byte alignment
 
 
+def test_swiglu_quantizer_argument_errors(lib):
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    f = lib.dg_swiglu_quantize_fp8_1x128
+    f.argtypes = [vp, vp, vp, i, i, vp]
+    assert f(None, A16, A16, 4, 128, None) == INVALID
+    assert f(A16, None, A16, 4, 128, None) == INVALID
+    assert f(A16, A16, None, 4, 128, None) == INVALID
+    assert f(A16, A16, A16, 0, 128, None) == INVALID
+    assert f(A16, A16, A16, 4, 0, None) == INVALID
+    assert f(A16, A16, A16, 4, 192, None) == UNSUPPORTED                 # I % 128
+    assert f(A16, A16, A16, 4, (1 << 30) + 128, None) == UNSUPPORTED     # 2I overflows an int
+    assert f(A16 + 8, A16, A16, 4, 128, None) == UNSUPPORTED             # c 16-byte alignment
+    assert f(A16, A16 + 4, A16, 4, 128, None) == UNSUPPORTED             # q 8-byte alignment
+    assert f(A16, A16, A16 + 2, 4, 128, None) == UNSUPPORTED             # s alignment
+
+
 def test_wgrad_argument_errors(lib):
     w = lib.dg_wgrad_fp8_nt
     assert w(A16, A16, A16, A16, None, 4, 4, 128, None) == INVALID
