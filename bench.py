@@ -311,6 +311,47 @@ def build_quantize():
                    "scales": "absmax/448 fp32", "in": "fp32", "out": "e4m3"}
 
 
+SWIGLU_METRIC = "SwiGLU + FP8 1x128 re-quantise GB/s (bf16 in, e4m3 + fp32 scales out) and % of MI355X HBM peak"
+
+
+def build_swiglu():
+    """SwiGLU + 1x128 quantise of the first linear's bf16 output [M, 2I] for
+    the MoE workloads: the contiguous layout's G=8 x 8192 rows with N = 2I of
+    4096 and of 7168, and a masked decode batch of 16 groups x 256 rows
+    (N = 4096).  Inputs are seeded N(0,1) bf16 drawn on the device;
+    algorithmic bytes = 4 read + 1 written per output element + the scales."""
+    import torch
+    import moe_grouped_gemm_x128_amd as dg
+    from harness import inputs
+
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(inputs.SEED_BASE + 6)
+    specs = [("swiglu_quant_m65536_n4096", 65536, 2048), ("swiglu_quant_m65536_n7168", 65536, 3584),
+             ("swiglu_quant_m4096_n4096", 4096, 2048)]
+    calls = []
+    for name, m, i in specs:
+        c = torch.randn((m, 2 * i), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        q = torch.empty((m, i), dtype=torch.uint8, device="cuda")
+        sc = torch.empty((m, i // 128), dtype=torch.float32, device="cuda")
+        fn = lambda c=c, q=q, sc=sc: dg.dg_swiglu_quantize_fp8_1x128(c, q, sc)
+        nbytes = m * i * 5 + sc.numel() * 4
+
+        def sample(rng, rows, c=c, i=i):
+            """The oracle on the first `rows` rows; returns the algorithmic
+            bytes covered."""
+            import oracle
+            rows = min(rows, c.shape[0])
+            bits = c[:rows].view(torch.int16).cpu().numpy().view(np.uint16)
+            oracle.swiglu_quantize_1x128(bits)
+            return rows * i * 5 + rows * (i // 128) * 4
+
+        calls.append(Call(name, 0.0, nbytes, fn, (sample, i)))
+    return calls, {"workload": "swiglu_quantize", "description":
+                   "SwiGLU (gate | up halves) + FP8 1x128 quantise of the first linear's bf16 output: "
+                   "[65536, 4096], [65536, 7168] (G=8 x 8192 rows) and [4096, 4096] (16 x 256 decode rows)",
+                   "scales": "absmax/448 fp32", "in": "bf16", "out": "e4m3"}
+
+
 def cpu_baseline_quantize(calls, seconds):
     """Time the oracle quantiser on the first rows of each input (GB/s of
     algorithmic traffic), sized to about `seconds` of CPU work."""
@@ -445,7 +486,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="dense",
                     choices=["dense", "small", "contiguous", "masked", "wgrad", "k_grouped_wgrad", "quantize",
-                             "dense_ue8m0", "bf16"])
+                             "dense_ue8m0", "bf16", "swiglu_quantize"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--settle-seconds", type=float, default=0.5, help="untimed run before the warmup steps")
@@ -467,7 +508,8 @@ def main():
     builders = {"dense": build_dense, "small": lambda: build_dense(small=True),
                 "contiguous": build_contiguous, "masked": build_masked,
                 "wgrad": build_wgrad, "k_grouped_wgrad": lambda: build_wgrad(kgrouped=True),
-                "quantize": build_quantize, "dense_ue8m0": lambda: build_dense(pow2=True), "bf16": build_bf16}
+                "quantize": build_quantize, "dense_ue8m0": lambda: build_dense(pow2=True), "bf16": build_bf16,
+                "swiglu_quantize": build_swiglu}
     if args.copy_calibration:
         copy_calibration()
         return
@@ -501,16 +543,17 @@ def main():
                 "frac": round(achieved / peak, 4), "traffic": measured_traffic(dc.name), "kernel": dc.name,
                 "flops_per_launch": dc.flops, "bytes_per_launch": dc.bytes, "avg_us": round(dms * 1e3, 2)}
 
-    quant = args.workload == "quantize"
+    quant = args.workload in ("quantize", "swiglu_quantize")
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         cpu = cpu_baseline_quantize(calls, args.cpu_seconds) if quant else cpu_baseline(calls, args.cpu_seconds)
 
     if quant:  # a stream, not a contraction: whole-step algorithmic bytes per second
+        swiglu = args.workload == "swiglu_quantize"
         value, unit, metric, dtype = sum(c.bytes for c in calls) / (ms_per_step * 1e-3) / 1e9, "GB/s", \
-            QUANT_METRIC, "f32"
-        data = "synthetic (seeded N(0,1) fp32)"
+            SWIGLU_METRIC if swiglu else QUANT_METRIC, "f32"
+        data = "synthetic (seeded N(0,1) bf16)" if swiglu else "synthetic (seeded N(0,1) fp32)"
     else:
         bf16 = args.workload == "bf16"
         value, unit, metric, dtype = step_flops / (ms_per_step * 1e-3) / 1e12, "TFLOP/s", METRIC, \
