@@ -179,10 +179,10 @@ dg_status dg_quantize_fp8_1x128_transposed(const float* x, void* q, float* s, in
  *   h = silu(gate) * up = gate / (1 + e^-gate) * up, in fp32
  *   q [M, I] fp8 e4m3, s [M, I/128] fp32: the 1x128 rule of
  *   dg_quantize_fp8_1x128 applied to h (amax / 448, s = 1 for a zero group).
- * h carries a few fp32 ulp of the exponential's error and the quotient is
- * h * RN(1/s), so a code can differ from exact evaluation where h / s lies
- * within about 2^-20 (relative) of the midpoint between two e4m3 values; the
- * scales match exact evaluation to within the same relative margin.
+ * h is within a few fp32 ulp of exact for every gate and the quotient is
+ * h * RN(1/s), so a code can differ from exact evaluation only where h / s
+ * lies within about 2^-20 (relative) of the midpoint between two e4m3 values;
+ * the scales match exact evaluation to within the same relative margin.
  * Every row is independent (grouped layouts pass their whole row range;
  * padding rows get codes of whatever they hold).  Inputs must keep h finite
  * in fp32.  c 16-byte aligned, q 8-byte, s 4-byte.  M >= 1; I >= 128,

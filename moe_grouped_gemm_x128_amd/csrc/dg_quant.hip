@@ -238,7 +238,7 @@ __global__ __launch_bounds__(kQThreads) void quant_rows_kernel(const float* __re
 // groups, which are consecutive 128-byte runs of the flat q [M, I].  16 lanes
 // share a group, each with 8 gate and 8 up values (one 16-byte load of each),
 // so a wave covers 4 groups per pass and 16 per step (16 KB in flight).
-// Per element the work is about 18 VALU cycles (two of them transcendental
+// Per element the work is about 20 VALU cycles (two of them transcendental
 // at quarter rate), close to the ~24 per element that HBM speed allows.
 // h carries the exp unit's error (a few fp32 ulp), so the quotient is
 // h * RN(1/s) instead of the exact division of the plain quantiser: codes
@@ -247,11 +247,18 @@ __global__ __launch_bounds__(kQThreads) void quant_rows_kernel(const float* __re
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// silu(g) = g / (1 + e^-g): e^-g = 2^(-g log2 e) on the exp unit, then one
-// reciprocal.  Large negative g gives e = inf and silu = -0; large positive
-// g gives e = 0 and silu = g.
+// silu(g) = g / (1 + e^-g) for a bf16 gate g.  e^-g = 2^(-g log2 e) with
+// log2 e split into a 15-bit head, whose product with g (8 significant bits)
+// is exact in fp32, and a tail t = log2 e - head applied as the factor
+// 2^(-g t) ~= 1 - g t ln 2 (|g t ln 2| < 4.4e-4 wherever e is finite, so the
+// dropped second-order term is under 2 ulp).  The exp unit then sees an exact
+// argument, and h stays within a few fp32 ulp of exact for every gate instead
+// of losing |g| * 2^-24 to the rounding of g * log2 e.  Large negative g gives
+// e = inf and silu = -0; large positive g gives e = 0 and silu = g.
 __device__ __forceinline__ float silu(float g) {
-  const float e = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);
+  constexpr float kLog2eHead = 1.44268798828125f;     // 15 significant bits
+  constexpr float kTailLn2 = -4.888495368504664e-06f;  // -(log2 e - head) * ln 2
+  const float e = __builtin_amdgcn_exp2f(g * -kLog2eHead) * __builtin_fmaf(g, kTailLn2, 1.0f);
   return g * __builtin_amdgcn_rcpf(1.0f + e);
 }
 

@@ -7,7 +7,7 @@ exactly, so the bar is stated on the oracle's exact values: every scale within
 where the oracle's exact quotient h / s lies within 2^-18 (relative) of the
 midpoint between two e4m3 values; there the code must be one of the two, and
 such elements must be rare (< 1e-3) on random inputs.  The GPU's h is within a few fp32 ulp of
-exact for |gate| < 32 (the inputs here), far inside that margin."""
+exact for every gate (the exponential's argument is exact), far inside that margin."""
 from __future__ import annotations
 
 import numpy as np
@@ -82,7 +82,9 @@ def test_swiglu_quant_ragged(dg, m, i):
 def test_swiglu_quant_special_rows(dg):
     """Zero gate or up halves (a zero group: codes +-0 with the sign of h,
     scale 1), saturated gates (+-100: silu = gate, and silu = -0), tiny
-    products (scale below 2^-60) and large ones (2^100)."""
+    products (scale below 2^-60) and large ones (2^100), and gates in
+    [-80, -20] (h = gate * e^gate * up down to 1e-33, where a rounded
+    exponential argument would cost |gate| * 2^-24 of relative error)."""
     i = 256
     rng = np.random.default_rng(7)
     rows = []
@@ -93,6 +95,7 @@ def test_swiglu_quant_special_rows(dg):
     rows.append(np.concatenate([g, u * 2.0 ** -110]))
     rows.append(np.concatenate([g, u * 2.0 ** 100]))
     rows.append(np.concatenate([np.concatenate([g[:128] * 8, g[128:] / 8]), u]))
+    rows.append(np.concatenate([-20.0 - 60.0 * rng.random(i), u]))
     c = bf16_bits(np.stack(rows).astype(np.float32))
     say("swiglu quantise special rows")
     q, s = run(dg, c)
