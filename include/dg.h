@@ -38,8 +38,9 @@
  *   - environment overrides for tests and tuning, read at each call:
  *     DG_FORCE_TILE=BMxBNxWMxWN forces a tile instance (UNSUPPORTED if the kind
  *     has none), DG_FORCE_SPLITS=s forces s K splits where splitting is
- *     allowed, DG_MASKED_BDIRECT=0|1 forces the masked layout off / onto the
- *     decode kernel that streams B into registers, DG_LOG=1 prints each plan
+ *     allowed, DG_MASKED_BDIRECT=1 runs the masked layout on the decode
+ *     kernel that streams B into registers (by default the general kernel
+ *     serves it), DG_LOG=1 prints each plan
  *     to stderr.  Results stay within the same accuracy bound either way.
  */
 #ifndef DG_MI355X_H

@@ -72,15 +72,22 @@ bool parse_forced(dg::TileShape* s) {
 constexpr int kMaxSplits = 16;
 constexpr int kSplitTarget = 4;
 constexpr int kSplitMinBlocks = 12;
+// The masked layout's tall tiles read each B column block once per group, so
+// a few-group decode has few tiles: up to 8 splits of at least 6 K blocks
+// (G=1, N=4096, K=7168: 26 us at 8 splits against 31 us at 4, cold).
+constexpr int kMaskedSplitTarget = 8;
+constexpr int kMaskedSplitMinBlocks = 6;
 constexpr size_t kMaxWorkspaceBytes = size_t(256) << 20;  // split-K partials per stream
 
 int choose_splits(int kind, int rows, long tiles, int num_cus, int kbs) {
   if (kind != DG_KIND_DENSE && kind != DG_KIND_MASKED && !dense_like(kind)) return 1;
   if (rows > 256) return 1;  // large M: the extra pass costs more than the idle CUs (measured)
   if (tiles * 10 >= num_cus * 7L) return 1;  // enough tiles already
+  const bool masked = kind == DG_KIND_MASKED;
   long s = (num_cus + tiles - 1) / tiles;
-  if (s > kSplitTarget) s = kSplitTarget;
-  if (s > kbs / kSplitMinBlocks) s = kbs / kSplitMinBlocks;
+  if (s > (masked ? kMaskedSplitTarget : kSplitTarget)) s = masked ? kMaskedSplitTarget : kSplitTarget;
+  if (masked && kbs < 3 * kSplitMinBlocks) return 1;  // short K: the reduction pass costs more (measured)
+  if (s > kbs / (masked ? kMaskedSplitMinBlocks : kSplitMinBlocks)) s = kbs / (masked ? kMaskedSplitMinBlocks : kSplitMinBlocks);
   return s < 2 ? 1 : (int)s;
 }
 
@@ -96,7 +103,9 @@ struct Candidate {
 // over workgroups (choose_splits).  Thresholds are from measured sweeps on
 // MI355X:
 //   * masked layout: tall 256-row tiles (B read once per group, the waves
-//     skip the row quarters past masked_m), as wide as the group count allows;
+//     skip the row quarters past masked_m): 256 columns when the groups give
+//     1.5 tiles per CU, else 128 columns on 4 waves (long K split to fill the
+//     CUs), or 64 when even those are too few for a short K;
 //   * few rows (<= 128 per group): the largest tile that still leaves enough
 //     tiles -- about 0.7 of the CUs, or a quarter of that when a long K is
 //     split four ways -- since such shapes stream B from HBM;
@@ -107,10 +116,10 @@ dg::TileShape heuristic(int kind, int rows, int n, int k, int groups, int num_cu
   const int kbs = k / 128;
   const bool long_k = allow_split && kbs >= 3 * kSplitMinBlocks;
   if (kind == DG_KIND_MASKED && rows <= 256) {
-    const dg::TileShape tall256{256, 256, 1, 8}, tall128{256, 128, 1, 8}, tall64{256, 64, 1, 4};
+    const dg::TileShape tall256{256, 256, 1, 8}, tall128{256, 128, 1, 4}, tall64{256, 64, 1, 4};
     const long cols128 = (long)groups * ceil_div(n, 128);
     if (cols128 * 2 >= 3L * num_cus) return tall256;   // enough tiles at 256 columns
-    if (long_k) return cols128 >= num_cus / 4 ? tall128 : tall64;
+    if (long_k) return tall128;
     return cols128 * 4 >= 3L * num_cus ? tall128 : tall64;
   }
   if (rows <= 128 || kind == DG_KIND_MASKED) {
@@ -160,18 +169,15 @@ struct Launch {
 };
 
 // Masked layout: the decode kernel that streams B into registers (256x256
-// tiles, 8 waves, K blocks in pairs).  Measured faster than the general
-// kernel when its work items fill the CUs (G=16: 118 vs 138 us for N=4096,
-// K=7168; G=4 with four K splits: 47 vs 50 us), slower when they cannot.
-// DG_MASKED_BDIRECT=0/1 overrides the choice.
-int choose_splits(int kind, int rows, long tiles, int num_cus, int kbs);
-bool use_bdirect(int kind, bool forced_tile, int rows, int n, int k, int groups, int num_cus, bool allow_split) {
+// tiles, 8 waves, K blocks in pairs), taken only when DG_MASKED_BDIRECT=1.
+// It was faster than the general kernel until the general kernel's B loads
+// took the streaming cache policy; since then the general kernel wins on
+// every decode shape of the page workloads (cold: G=16, N=7168, K=2048 82 vs
+// 92 us; G=16, N=4096, K=7168 144 vs 148 us; G=4 54 vs 62 us).
+bool use_bdirect(int kind, int k) {
   if (kind != DG_KIND_MASKED || (k / 128) % 2 != 0) return false;
-  if (const char* e = std::getenv("DG_MASKED_BDIRECT")) return e[0] == '1';
-  if (forced_tile) return false;
-  const long tiles = (long)groups * ceil_div(rows, 256) * ceil_div(n, 256);
-  const int splits = allow_split ? choose_splits(kind, rows, tiles, num_cus, k / 128) : 1;
-  return tiles * splits * 10 >= 9L * num_cus;
+  const char* e = std::getenv("DG_MASKED_BDIRECT");
+  return e && e[0] == '1';
 }
 
 // `allow_split`: split-K needs a temporary workspace, so it is planned only
@@ -182,7 +188,7 @@ dg_status plan(int kind, int rows, int n, int k, int groups, int num_cus, bool a
   const bool forced = parse_forced(&s);
   if (!forced) s = heuristic(kind, rows, n, k, groups, num_cus, allow_split);
   // (the decode kernel takes K blocks in pairs: an even count per work item)
-  l.bdirect = use_bdirect(kind, forced, rows, n, k, groups, num_cus, allow_split);
+  l.bdirect = use_bdirect(kind, k);
   if (l.bdirect) s = dg::TileShape{256, 256, 1, 8};
   if (!dg::has_instance(kind, s)) return DG_ERROR_UNSUPPORTED;
   p.tiles_m = ceil_div(rows, s.bm);
