@@ -229,6 +229,25 @@ def test_heuristic_invariants(lib, kind, m, n, k, g):
     assert _cfg(lib, kind, m, n, k, g) == c  # deterministic
 
 
+def test_masked_plan(lib, monkeypatch):
+    """Masked decode: the general kernel's tall tiles serve every page shape,
+    long K is split until the CUs are covered, short K is not split, and the
+    register-streaming decode kernel runs only when asked for."""
+    monkeypatch.delenv("DG_MASKED_BDIRECT", raising=False)
+    for g in (1, 2, 4, 16):
+        for n, k in ((4096, 7168), (7168, 2048)):
+            c = _cfg(lib, 2, 256, n, k, g)
+            assert c["kernel"] == 0 and c["block_m"] == 256
+            if k == 2048:
+                assert c["k_splits"] == 1
+            elif c["tiles"] < 180:
+                assert c["tiles"] * c["k_splits"] >= 256 and (k // 128) // c["k_splits"] >= 6
+    assert _cfg(lib, 2, 256, 4096, 7168, 16)["block_n"] == 256
+    monkeypatch.setenv("DG_MASKED_BDIRECT", "1")
+    c = _cfg(lib, 2, 256, 4096, 7168, 16)
+    assert c["kernel"] == 1 and (c["block_m"], c["block_n"]) == (256, 256)
+
+
 def test_split_k_planning(lib):
     """Few output tiles and a long K: split K to give every CU work; many
     tiles: no split."""
