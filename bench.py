@@ -15,8 +15,9 @@ and whose roofline fraction is reported from those.  The CPU oracle is
 timed on a bounded sample of the same workload's outputs (`cpu_baseline`).
 Other workloads (contiguous, masked, wgrad, k_grouped_wgrad, small,
 dense_ue8m0 -- the sweep with power-of-two scales --, bf16 -- the sweep's
-shapes in BF16 against the bf16 peak -- and quantize, the FP8 quantiser in
-GB/s) print a line of the same form.  Exactly one JSON line goes to stdout.
+shapes in BF16 against the bf16 peak --, quantize, the FP8 quantiser in
+GB/s, and swiglu_quantize, the SwiGLU + FP8 re-quantise step between an
+expert's two GEMMs in GB/s) print a line of the same form.  Exactly one JSON line goes to stdout.
 
 Before the W warmup steps the step runs untimed for at least half a second so
 the GPU clock has settled when timing starts.  `roofline.traffic` is the
