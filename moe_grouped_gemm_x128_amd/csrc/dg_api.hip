@@ -84,10 +84,12 @@ int choose_splits(int kind, int rows, long tiles, int num_cus, int kbs) {
   if (rows > 256) return 1;  // large M: the extra pass costs more than the idle CUs (measured)
   if (tiles * 10 >= num_cus * 7L) return 1;  // enough tiles already
   const bool masked = kind == DG_KIND_MASKED;
-  long s = (num_cus + tiles - 1) / tiles;
-  if (s > (masked ? kMaskedSplitTarget : kSplitTarget)) s = masked ? kMaskedSplitTarget : kSplitTarget;
   if (masked && kbs < 3 * kSplitMinBlocks) return 1;  // short K: the reduction pass costs more (measured)
-  if (s > kbs / (masked ? kMaskedSplitMinBlocks : kSplitMinBlocks)) s = kbs / (masked ? kMaskedSplitMinBlocks : kSplitMinBlocks);
+  const long target = masked ? kMaskedSplitTarget : kSplitTarget;
+  const long most = kbs / (masked ? kMaskedSplitMinBlocks : kSplitMinBlocks);
+  long s = (num_cus + tiles - 1) / tiles;
+  if (s > target) s = target;
+  if (s > most) s = most;
   return s < 2 ? 1 : (int)s;
 }
 
