@@ -118,7 +118,8 @@ dg::TileShape heuristic(int kind, int rows, int n, int k, int groups, int num_cu
   const int kbs = k / 128;
   const bool long_k = allow_split && kbs >= 3 * kSplitMinBlocks;
   if (kind == DG_KIND_MASKED && rows <= 256) {
-    const dg::TileShape tall256{256, 256, 1, 8}, tall128{256, 128, 1, 4}, tall64{256, 64, 1, 4};
+    // 256 columns on 2x4 waves: 3-4% faster than 1x8 for 16 groups (cold)
+    const dg::TileShape tall256{256, 256, 2, 4}, tall128{256, 128, 1, 4}, tall64{256, 64, 1, 4};
     const long cols128 = (long)groups * ceil_div(n, 128);
     if (cols128 * 2 >= 3L * num_cus) return tall256;   // enough tiles at 256 columns
     if (long_k) return tall128;
