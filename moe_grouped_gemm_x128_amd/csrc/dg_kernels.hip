@@ -252,10 +252,6 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   static_assert(BN % 16 == 0, "whole 16-column fragments");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE + 1024];  // + padding-DMA sink
-  // contiguous: rows of a tile that carry its expert, double-buffered by tile
-  // parity (the next tile is looked up while the current one is computed)
-  __shared__ int sRowOk[2][KIND == KIND_CONTIGUOUS ? BM : 1];
-  __shared__ int sExpert[2][2];  // per parity: experts of the tile's two 128-row blocks
   // bf16 epilogue staging: a wave's 16-row fragment row goes through LDS so
   // that each store covers whole (64 columns) or half (32 columns) 128-byte
   // lines; rows padded by 16 bytes against bank conflicts
@@ -295,13 +291,17 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   // of items) is one (output tile, K split) pair.  decode() gives its Tile;
   // live == 0: no work (past the end, an empty K range, or -- contiguous -- a
   // block of padding rows).
+  // contiguous: bit i of rmask[i / 64] says whether row wm * WTM + i of the
+  // tile carries the tile's expert (this wave's rows only)
+  constexpr int RMW = KIND == KIND_CONTIGUOUS ? (WTM + 63) / 64 : 1;
   struct Tile {
     int live, g, m0, n0, rows, kb0, nkb, split;
     int64_t a_row0, out_row0;
+    uint64_t rmask[RMW];
   };
   const int t_end = per_xcd * 8;
   auto decode = [&](int t) -> Tile {
-    Tile x{0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    Tile x{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, {}};
     const int LS = (t & 7) * per_xcd + (t >> 3);
     if (t >= t_end || LS >= TS) return x;
     const int L = splits > 1 ? LS / splits : LS;
@@ -354,36 +354,44 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     x.live = x.nkb > 0;
     return x;
   };
-  // contiguous: which of the tile's rows carry expert `e`, into parity
-  // buffer `par`.  All waves call this together (it synchronises the
-  // workgroup); the first barrier waits for the epilogue that last read `par`.
-  // Only rows of a block whose expert is `e` qualify (lo / hi: the first /
-  // second 128-row block), so a stray id of another expert inside a block is
-  // skipped whatever the tile height.
-  auto mark_rows = [&](const Tile& x, int par, int e, bool lo, bool hi) {
-    barrier();
-    for (int r = tid; r < BM; r += NW * 64)
-      sRowOk[par][r] = r < x.rows && (r < 128 ? lo : hi) && p.ctrl[x.m0 + r] == e;
-  };
   // contiguous: the expert of each 128-aligned row block of the tile (the
-  // single valid id in it).  A 256-row tile whose two blocks belong to
-  // different experts is computed twice, once per expert (the second pass is
-  // queued in `pend`); each pass stores only its expert's rows.
-  int pend_t = -1, pend_g = -1;  // item and expert of a queued second pass
-  auto find_expert = [&](Tile& x, int t, int par) {
-    barrier();  // every wave is done with the epilogue that last read `par`
-    if (tid < 2) sExpert[par][tid] = -1;
-    barrier();
-    for (int r = tid; r < x.rows; r += NW * 64) {
-      const int id = p.ctrl[x.m0 + r];
-      if (id >= 0 && id < p.groups) atomicMax(&sExpert[par][r >= 128 ? 1 : 0], id);
+  // largest id in [0, G) in it: a block holds one expert, the rest is -1
+  // padding).  Every wave reads the ids itself (no LDS, no barrier) and keeps
+  // the rows of its own that carry the tile's expert as bit masks.  A
+  // 256-row tile whose two blocks belong to different experts is computed
+  // twice, once per expert (the second pass is queued in `pend`); each pass
+  // stores only its expert's rows.
+  auto wave_max = [](int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+  auto row_id = [&](const Tile& x, int r) { return r < x.rows ? p.ctrl[x.m0 + r] : -1; };
+  // rows of this wave with id `e` in a block whose expert is `e` (blocks
+  // 0 and 1 qualify per lo / hi)
+  auto mark_rows = [&](Tile& x, int e, bool lo, bool hi) {
+#pragma unroll
+    for (int c = 0; c < RMW; ++c) {
+      const int r = wm * WTM + 64 * c + lane;
+      const bool in = lane < WTM - 64 * c;
+      const bool ok = in && (r < 128 ? lo : hi) && row_id(x, r) == e;
+      x.rmask[c] = __ballot(ok);
     }
-    barrier();
-    // (read from LDS: made wave-uniform so the loop that depends on it stays scalar)
-    const int e0 = __builtin_amdgcn_readfirstlane(sExpert[par][0]);
-    const int e1 = __builtin_amdgcn_readfirstlane(sExpert[par][1]);
+  };
+  int pend_t = -1, pend_g = -1;  // item and expert of a queued second pass
+  auto find_expert = [&](Tile& x, int t) {
+    int m0v = -1, m1v = -1;
+#pragma unroll
+    for (int i = 0; i < BM / 64; ++i) {
+      const int r = 64 * i + lane;
+      const int id = row_id(x, r);
+      const int v = (id >= 0 && id < p.groups) ? id : -1;
+      if (r < 128) m0v = max(m0v, v); else m1v = max(m1v, v);
+    }
+    const int e0 = wave_max(m0v);
+    const int e1 = BM > 128 ? wave_max(m1v) : -1;
     const int e = e0 >= 0 ? e0 : e1;
-    mark_rows(x, par, e, e0 == e, e1 == e);
+    mark_rows(x, e, e0 == e, e1 == e);
     x.g = e;
     x.live = e >= 0;
     if (e0 >= 0 && e1 >= 0 && e1 != e0) {
@@ -393,13 +401,13 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   };
   // the first live item at or after `t` (or a queued second pass); `t`
   // moves past it
-  auto next_live = [&](int& t, int par) -> Tile {
+  auto next_live = [&](int& t) -> Tile {
     if constexpr (KIND == KIND_CONTIGUOUS) {
       if (pend_t >= 0) {
         Tile x = decode(pend_t);
         x.g = pend_g;
         pend_t = -1;
-        mark_rows(x, par, x.g, false, true);  // the second block's expert
+        mark_rows(x, x.g, false, true);  // the second block's expert
         return x;
       }
     }
@@ -407,16 +415,29 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     while (t < t_end) {
       x = decode(t);
       if constexpr (KIND == KIND_CONTIGUOUS)
-        if (x.live) find_expert(x, t, par);
+        if (x.live) find_expert(x, t);
       t += gridDim.x;
       if (x.live) break;
     }
     return x;
   };
-  // DMA resources of a tile (a dead tile's read nothing)
+  // DMA sources of a tile at its first K block (a dead tile's read nothing):
+  // the operand resources (the same on every wave) and the resource of each
+  // of this wave's scale pieces -- sa rows or sb rows (row-scaled B) / 128-column
+  // blocks, moved to the piece's first row, or empty -- so that a K block
+  // only moves the bases.
   struct Res {
-    Rsrc a, b, sa, sb;
+    Rsrc a, b;
+    Rsrc s[QS];
     int kb0, nkb;
+  };
+  // r advanced by `bytes` with its range cut where it ended (empty if that is
+  // past the end or !on); wave-uniform
+  auto moved = [](const Rsrc& r, uint32_t bytes, bool on) {
+    const uint64_t b = (((uint64_t)r.hi << 32) | r.lo) + bytes;
+    return Rsrc{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b),
+                (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xffffu),
+                (uint32_t)__builtin_amdgcn_readfirstlane(on && bytes < r.num ? r.num - bytes : 0u), r.flags};
   };
   auto make_res = [&](const Tile& x) -> Res {
     const int bg = (KIND == KIND_KGROUPED) ? 0 : x.g;  // K-grouped: one B [N,T]
@@ -426,14 +447,24 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     Res r;
     r.a = buffer_rsrc(p.a + x.a_row0 * (int64_t)p.lda, on * (uint32_t)x.rows * p.lda);
     r.b = buffer_rsrc(p.b + ((int64_t)bg * p.n + x.n0) * (int64_t)p.lda, on * (uint32_t)bcols * p.lda);
-    r.sa = buffer_rsrc(p.sa + x.a_row0 * (int64_t)p.kbs, son * (uint32_t)x.rows * p.kbs * 4);
+    const Rsrc sa = buffer_rsrc(p.sa + x.a_row0 * (int64_t)p.kbs, son * (uint32_t)x.rows * p.kbs * 4);
+    Rsrc sb;
     if constexpr (kRowScaleB) {
-      r.sb = buffer_rsrc(p.sb + (int64_t)x.n0 * p.kbs, on * (uint32_t)bcols * p.kbs * 4);
+      sb = buffer_rsrc(p.sb + (int64_t)x.n0 * p.kbs, on * (uint32_t)bcols * p.kbs * 4);
     } else {
       // only the 128-column blocks the tile touches
       const int nb0 = x.n0 / kBK;
       const int nbt = min(nb_rows - nb0, (x.n0 - nb0 * kBK + BN + kBK - 1) / kBK);  // a tile may straddle blocks
-      r.sb = buffer_rsrc(p.sb + ((int64_t)x.g * nb_rows + nb0) * p.kbs, son * (uint32_t)max(nbt, 0) * p.kbs * 4);
+      sb = buffer_rsrc(p.sb + ((int64_t)x.g * nb_rows + nb0) * p.kbs, son * (uint32_t)max(nbt, 0) * p.kbs * 4);
+    }
+    const uint32_t prow = 64u * p.kbs * 4;  // bytes of 64 scale rows
+#pragma unroll
+    for (int q = 0; q < QS; ++q) {
+      const int sp = wave + NW * q;  // scale piece: sa rows 64*sp.., then sb
+      const bool is_a = sp < PSA;
+      const uint32_t rowoff = (uint32_t)(is_a ? sp : sp - PSA) * prow;
+      const Rsrc src{is_a ? sa.lo : sb.lo, is_a ? sa.hi : sb.hi, is_a ? sa.num : sb.num, sa.flags};
+      r.s[q] = moved(src, rowoff, sp < PS);
     }
     r.kb0 = x.kb0;
     r.nkb = x.live ? x.nkb : 0;
@@ -465,15 +496,15 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   bool stores_pending = false;  // the previous tile's epilogue stores may be in flight
 
   int t_next = blockIdx.x;
-  int par = 0;
-  Tile cur = next_live(t_next, par);
+  Tile cur = next_live(t_next);
   int qbase = 0;        // ring stage of the current tile's first K block
   bool first = true;
   while (cur.live) {
+    // the next tile: looked up (with cross-tile prefetch) only before the
+    // current tile's last S-1 K blocks, so its state is not live in the main
+    // part of the K loop (registers)
     Tile nxt = decode(t_end);
-    if (xfer) nxt = next_live(t_next, par ^ 1);
     const Res rc = make_res(cur);
-    const Res rn = make_res(nxt);
     const int n0 = cur.n0, rows = cur.rows, nkb = cur.nkb, split = cur.split;
     const int64_t out_row0 = cur.out_row0;
 
@@ -485,84 +516,69 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     const uint32_t step = (uint32_t)(NW * 8) * p.lda;  // bytes between a wave's pieces
     // scale pieces: 64 rows (or columns / 128-blocks) each, one float per lane
     const uint32_t svoff = (uint32_t)lane * p.kbs * 4;
-    const uint32_t sstep = 64u * p.kbs * 4;
 
-    // this wave's DMAs for K block r.kb0 + rel of a tile into ring stage
-    // `st`; only the pieces with index in [lo, hi) (A pieces first, then B,
-    // then scales), so a block's DMAs can be spread over the fragment groups
-    // of the previous block instead of stalling every wave at the same point.
-    // Branch-free: a block past the tile's K range (or of a dead tile) reads
-    // nothing -- its resources have an empty range, read zeros and touch no
-    // memory -- into a stage no live block of the ring needs.
-    constexpr int ND = QA + QB + QS;
-    auto issue = [&](const Res& r, int rel, int st, int lo, int hi) {
+    // The DMAs of one K block: each source moved to the block (empty past
+    // the tile's K range or for a dead tile: such a block reads zeros and
+    // touches no memory, into a stage no live block of the ring needs) and
+    // the ring stage it lands in.  Built once per block; `issue` then only
+    // sends pieces [lo, hi) of it (A pieces first, then B, then scales), so a
+    // block's DMAs can be spread over the fragment groups of the previous
+    // block instead of stalling every wave at the same point.
+    struct Blk {
+      v4i a, b, s[QS];
+      uint32_t base;
+    };
+    // A source moved to K byte offset `koff` of its rows (scalar arithmetic):
+    // a non-empty range holds at least one row, which is longer than any K
+    // offset, so the range stays positive; a dead block or source reads
+    // nothing.
+    auto at_k = [](const Rsrc& r, uint32_t koff, bool live) {
+      const uint64_t b = (((uint64_t)r.hi << 32) | r.lo) + koff;
+      return v4i{(int)__builtin_amdgcn_readfirstlane((uint32_t)b),
+                 (int)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xffffu),
+                 (int)__builtin_amdgcn_readfirstlane((live && r.num != 0u) ? r.num - koff : 0u), (int)r.flags};
+    };
+    auto blk_of = [&](const Res& r, int rel, int st) -> Blk {
       const bool live = rel < r.nkb;
-      const int kb = r.kb0 + rel;
-      const uint32_t base = smem_lds + st * STAGE;
-      const uint32_t koff = __builtin_amdgcn_readfirstlane(kb * kBK);
-      const uint32_t skoff = __builtin_amdgcn_readfirstlane(kb * 4);
-      const v4i ra = at(r.a, koff, live);
-      const v4i rb = at(r.b, koff, live);
+      const uint32_t kb = (uint32_t)(r.kb0 + rel);
+      Blk d;
+      d.a = at_k(r.a, kb * kBK, live);
+      d.b = at_k(r.b, kb * kBK, live);
+#pragma unroll
+      for (int q = 0; q < QS; ++q) d.s[q] = at_k(r.s[q], kb * 4, live);
+      d.base = __builtin_amdgcn_readfirstlane(smem_lds + st * STAGE);
+      return d;
+    };
+    constexpr int ND = QA + QB + QS;
+    auto issue = [&](const Blk& d, int lo, int hi) {
 #pragma unroll
       for (int q = 0; q < QA; ++q)
-        if (q >= lo && q < hi) dma16(base + OFF_A + (wave + NW * q) * 1024, ra, voff0 + q * step);
+        if (q >= lo && q < hi) dma16(d.base + OFF_A + (wave + NW * q) * 1024, d.a, voff0 + q * step);
 #pragma unroll
       for (int q = 0; q < QB; ++q) {
         if (QA + q < lo || QA + q >= hi) continue;
         const int pi = wave + NW * q;
         if constexpr (PB % NW == 0) {
           if constexpr (kStreamB)
-            dma16_nt(base + OFF_B + pi * 1024, rb, voff0 + q * step);
+            dma16_nt(d.base + OFF_B + pi * 1024, d.b, voff0 + q * step);
           else
-            dma16(base + OFF_B + pi * 1024, rb, voff0 + q * step);
+            dma16(d.base + OFF_B + pi * 1024, d.b, voff0 + q * step);
         } else {
           // past the last B piece: read nothing into the sink
           const bool real = pi < PB;
-          v4i rq = rb;
-          rq[2] = real ? rb[2] : 0;
-          dma16(__builtin_amdgcn_readfirstlane(real ? base + OFF_B + pi * 1024 : smem_lds + S * STAGE), rq,
-                voff0 + q * step);
+          v4i rq = d.b;
+          rq[2] = real ? d.b[2] : 0;
+          dma16(real ? d.base + OFF_B + pi * 1024 : smem_lds + S * STAGE, rq, voff0 + q * step);
         }
       }
 #pragma unroll
       for (int q = 0; q < QS; ++q) {
         if (QA + QB + q < lo || QA + QB + q >= hi) continue;
-        const int sp = wave + NW * q;  // scale piece: sa rows 64*sp.., then sb
-        const bool is_a = sp < PSA, real = sp < PS && live && !kBf16;  // BF16 has no scales
-        // select the sa or sb resource arithmetically (a select here is lowered
-        // to an indexed stack array)
-        const uint32_t f = (uint32_t)__builtin_amdgcn_readfirstlane(is_a ? 1 : 0);
-        Rsrc sel;
-        sel.lo = r.sb.lo + (r.sa.lo - r.sb.lo) * f;
-        sel.hi = r.sb.hi + (r.sa.hi - r.sb.hi) * f;
-        sel.num = r.sb.num + (r.sa.num - r.sb.num) * f;
-        sel.flags = r.sa.flags;
-        const v4i r4 = at(sel, skoff, real);
-        const v4i rs = v4i{(int)__builtin_amdgcn_readfirstlane(r4[0]), (int)__builtin_amdgcn_readfirstlane(r4[1]),
-                           (int)__builtin_amdgcn_readfirstlane(r4[2]), (int)__builtin_amdgcn_readfirstlane(r4[3])};
-        const uint32_t lds = __builtin_amdgcn_readfirstlane(sp < PS ? base + OFF_SA + sp * 256 : smem_lds + S * STAGE);
-        dma4(lds, rs, svoff + (uint32_t)(is_a ? sp : sp - PSA) * sstep);
+        const int sp = wave + NW * q;
+        dma4(sp < PS ? d.base + OFF_SA + sp * 256 : smem_lds + S * STAGE, d.s[q], svoff);
       }
     };
-    // the block S-1 ahead of the current tile's block `rel`: this tile's own,
-    // else (cross-tile prefetch) the next tile's, else a dead block
-    const int qs = __builtin_amdgcn_readfirstlane(qbase % S);  // uniform: keep the ring stage scalar
-    auto sel = [](uint32_t c, const Rsrc& x, const Rsrc& y) {  // c ? x : y, scalar arithmetic
-      return Rsrc{y.lo + (x.lo - y.lo) * c, y.hi + (x.hi - y.hi) * c, y.num + (x.num - y.num) * c, x.flags};
-    };
-    auto issue_ahead = [&](int rel, int lo, int hi) {
-      const int q = rel + S - 1;
-      const int st = (qs + q) % S;
-      const uint32_t c = (uint32_t)__builtin_amdgcn_readfirstlane(q < nkb ? 1 : 0);
-      Res r;
-      r.a = sel(c, rc.a, rn.a);
-      r.b = sel(c, rc.b, rn.b);
-      r.sa = sel(c, rc.sa, rn.sa);
-      r.sb = sel(c, rc.sb, rn.sb);
-      r.kb0 = c ? rc.kb0 : rn.kb0;
-      r.nkb = c ? rc.nkb : rn.nkb;
-      issue(r, c ? q : q - nkb, st, lo, hi);
-    };
+    const int qs = qbase % S;
 
     v4f acc[FN][FM];
 #pragma unroll
@@ -640,11 +656,11 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
       if (first || !xfer) {
   #pragma unroll
         for (int s = 0; s < S - 1; ++s)
-          if (s < nkb) issue(rc, s, (qs + s) % S, 0, ND);
+          if (s < nkb) issue(blk_of(rc, s, (qs + s) % S), 0, ND);
       }
 
-  #pragma unroll 1
-      for (int rel = 0; rel < nkb; ++rel) {
+      // one K block; `dma` is the block issued during it (S-1 ahead)
+      auto block = [&](int rel, const Blk& dma) {
         const int st = (qs + rel) % S;
         // this wave's DMAs for block `rel` are done once at most
         // (blocks issued after it) x DMIN of its operations remain in flight;
@@ -723,7 +739,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
           else
             fma4(acc_at(NOV - 1, r), pend[r], part[r]);
         };
-        if constexpr (NOV == 0) issue_ahead(rel, 0, ND);  // no groups to spread over
+        if constexpr (NOV == 0) issue(dma, 0, ND);  // no groups to spread over
 
   #pragma unroll
         for (int o = 0; o < NOV; ++o) {
@@ -758,7 +774,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
           // half of the groups so they still land in time)
           constexpr int kSpread = NOV / 2 > 0 ? NOV / 2 : 1;
           if (o < kSpread)
-            issue_ahead(rel, (o * ND) / kSpread, ((o + 1) * ND) / kSpread);
+            issue(dma, (o * ND) / kSpread, ((o + 1) * ND) / kSpread);
           if constexpr (!kDirectAcc) promote(o, 0, false);
           sa_prev = sa_cur;
           cur = nxt;
@@ -778,7 +794,17 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
             pend[r] = sa * sbv[i];
           }
         }
-      }
+      };
+      // main part: the DMAs are this tile's own blocks
+      const int tail = max(0, nkb - (S - 1));
+  #pragma unroll 1
+      for (int rel = 0; rel < tail; ++rel) block(rel, blk_of(rc, rel + S - 1, (qs + rel + S - 1) % S));
+      // last S-1 blocks: the DMAs are the next tile's first blocks (cross-tile
+      // prefetch), else dead blocks
+      if (xfer) nxt = next_live(t_next);
+      const Res rn = make_res(nxt);
+  #pragma unroll 1
+      for (int rel = tail; rel < nkb; ++rel) block(rel, blk_of(rn, rel + S - 1 - nkb, (qs + rel + S - 1) % S));
   #pragma unroll
       for (int r = 1; r < NR && NOV > 0 && !kDirectAcc; ++r) {
         if constexpr (kRowScaleB)
@@ -805,6 +831,11 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     }
 
     // ---- epilogue ----
+    // contiguous: does row 16*j + r of this wave's rows carry the tile's expert
+    // (j a compile-time fragment row, r < 16)
+    auto rbit = [&](int j, int r) -> bool {
+      return ((cur.rmask[((16 * j) / 64) % RMW] >> (uint32_t)(16 * (j % 4) + r)) & 1u) != 0;
+    };
     if (kStage && staged) {
       // fragment row j: lanes write their 4 bf16 per column fragment into the
       // wave's LDS rows, then read 16 contiguous bytes each along the rows
@@ -831,7 +862,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
           const int ml = wm * WTM + 16 * j + r;
           bool row_ok;
           if constexpr (KIND == KIND_CONTIGUOUS)
-            row_ok = sRowOk[par][ml] != 0;
+            row_ok = rbit(j, r);
           else
             row_ok = ml < rows;
           const int n = n0 + wn * WTN + cb / 2;  // 8 columns, all valid or none (N % 8 == 0)
@@ -860,7 +891,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
         const int ml = wm * WTM + 16 * j + l16;
         bool row_ok;
         if constexpr (KIND == KIND_CONTIGUOUS)
-          row_ok = sRowOk[par][ml] != 0;
+          row_ok = rbit(j, l16);
         else
           row_ok = ml < rows;
 #pragma unroll
@@ -884,7 +915,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
       const int ml = wm * WTM + 16 * j + l16;
       bool row_ok;
       if constexpr (KIND == KIND_CONTIGUOUS)
-        row_ok = sRowOk[par][ml] != 0;
+        row_ok = rbit(j, l16);
       else
         row_ok = ml < rows;
       if (!row_ok) continue;
@@ -938,10 +969,9 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     stores_pending = xfer && exact_stores;
 
     // ---- next tile ----
-    if (!xfer) nxt = next_live(t_next, par ^ 1);
+    if (!xfer) nxt = next_live(t_next);
     qbase += nkb;
     cur = nxt;
-    par ^= 1;
     first = false;
   }
   wait_vm<0>();  // no DMA (dead blocks included) outlives the workgroup
