@@ -18,12 +18,15 @@
  *   - split K: for shapes with too few output tiles to occupy every compute
  *     unit (few rows, long K), the dense and masked calls split K over several
  *     workgroups and add the fp32 partials in a second kernel, in a fixed
- *     order (results are deterministic).  The partials live in a temporary
- *     workspace (splits * rows * N * 4 bytes) taken from a memory pool the
- *     library owns per device, allocated and returned in stream order; the
- *     pool keeps freed blocks for reuse until the process ends.  A call made
- *     while `stream` is being captured into a HIP graph never splits, so it
- *     allocates nothing and records only the GEMM kernel;
+ *     order (results are deterministic).  The partials (splits * rows * N * 4
+ *     bytes, at most 256 MB) live in a buffer taken from a memory pool the
+ *     library owns per device, allocated before the two kernels and freed
+ *     after them in the order of `stream`, so the buffer is never seen by
+ *     another stream and does not outlive the call; the pool keeps freed
+ *     blocks for reuse until the process ends.  If no buffer can be had the
+ *     call runs without a split instead.  A call made while `stream` is being
+ *     captured into a HIP graph never splits, so it allocates nothing and
+ *     records only the GEMM kernel;
  *   - tensors are row-major with the last dimension contiguous;
  *   - fp8 = OCP E4M3FN bytes (what torch calls float8_e4m3fn); scales fp32;
  *   - K_b = K/128, NB = ceil(N/128);
@@ -57,7 +60,9 @@ typedef enum {
   DG_SUCCESS = 0,
   DG_ERROR_INVALID_VALUE = 1, /* null pointer, a size <= 0, G <= 0           */
   DG_ERROR_UNSUPPORTED = 2,   /* K % 128 != 0, misalignment, layout limits   */
-  DG_ERROR_LAUNCH = 3         /* the HIP runtime reported a launch failure   */
+  DG_ERROR_LAUNCH = 3,        /* the HIP runtime reported a launch failure   */
+  DG_ERROR_WORKSPACE = 4      /* a call's split-K partials exceed the fixed
+                                 scratch of an allocation-free entry point   */
 } dg_status;
 
 /* Dense FP8 NT GEMM (DeepGEMM pages, "使用示例": the normal FP8 GEMM call).

@@ -189,6 +189,10 @@ def dg_grouped_fp8_contiguous(a, sa, b, sb, c, m_indices):
 
 
 def dg_grouped_fp8_masked(a, sa, b, sb, c, masked_m):
+    return _grouped_masked(_lib.dg_grouped_fp8_masked, "dg_grouped_fp8_masked", a, sa, b, sb, c, masked_m)
+
+
+def _grouped_masked(fn, name, a, sa, b, sb, c, masked_m):
     _fp8(a, "a"); _fp8(b, "b"); _f32(sa, "sa"); _f32(sb, "sb")
     g, m_max, k = a.shape
     n = b.shape[1]
@@ -200,8 +204,7 @@ def dg_grouped_fp8_masked(a, sa, b, sb, c, masked_m):
     if c.dtype != torch.bfloat16:
         raise TypeError("c must be bfloat16")
     _dev(a, sa, b, sb, c, masked_m)
-    _check(_lib.dg_grouped_fp8_masked(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(c), _ptr(masked_m),
-                                      g, m_max, n, k, _stream(c)), "dg_grouped_fp8_masked")
+    _check(fn(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(c), _ptr(masked_m), g, m_max, n, k, _stream(c)), name)
     return c
 
 

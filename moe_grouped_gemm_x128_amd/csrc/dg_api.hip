@@ -1,6 +1,8 @@
 // dg_api.hip -- the C ABI (include/dg.h): host-side validation, the per-shape
 // tile heuristic and kernel dispatch.  Validation runs before any HIP call, so
 // every error path can be exercised on a machine without a GPU.
+#include <dlfcn.h>
+
 #include <atomic>
 #include <climits>
 #include <cstdint>
@@ -77,7 +79,7 @@ constexpr int kSplitMinBlocks = 12;
 // (G=1, N=4096, K=7168: 26 us at 8 splits against 31 us at 4, cold).
 constexpr int kMaskedSplitTarget = 8;
 constexpr int kMaskedSplitMinBlocks = 6;
-constexpr size_t kMaxWorkspaceBytes = size_t(256) << 20;  // split-K partials per stream
+constexpr size_t kMaxWorkspaceBytes = size_t(256) << 20;  // split-K partials per call
 
 int choose_splits(int kind, int rows, long tiles, int num_cus, int kbs) {
   if (kind != DG_KIND_DENSE && kind != DG_KIND_MASKED && !dense_like(kind)) return 1;
@@ -120,9 +122,16 @@ dg::TileShape heuristic(int kind, int rows, int n, int k, int groups, int num_cu
   if (kind == DG_KIND_MASKED && rows <= 256) {
     // 256 columns on 2x4 waves: 3-4% faster than 1x8 for 16 groups (cold)
     const dg::TileShape tall256{256, 256, 2, 4}, tall128{256, 128, 1, 4}, tall64{256, 64, 1, 4};
+    const dg::TileShape tall32{256, 32, 4, 1};
     const long cols128 = (long)groups * ceil_div(n, 128);
     if (cols128 * 2 >= 3L * num_cus) return tall256;   // enough tiles at 256 columns
     if (long_k) return tall128;
+    // without a split (short K, or a call being captured): 32 columns per
+    // tile when that still gives at most one tile per CU -- each tile then
+    // streams a quarter of a 128-column tile's B; G=1, N=4096, K=7168 51 us
+    // against 67 us on 64 columns, G=1, N=7168, K=2048 19.5 against 22.4 us
+    // (cold); with more groups the extra A re-reads cost more (G=4: 95 vs 69 us)
+    if ((long)groups * ceil_div(n, 32) <= num_cus) return tall32;
     return cols128 * 4 >= 3L * num_cus ? tall128 : tall64;
   }
   if (rows <= 128 || kind == DG_KIND_MASKED) {
@@ -228,23 +237,46 @@ dg_status plan(int kind, int rows, int n, int k, int groups, int num_cus, bool a
   return DG_SUCCESS;
 }
 
-// Split-K partials live in a workspace cached per (device, stream): calls on
-// one stream run in order, so they can share it; calls on different streams
-// get different buffers.  A workspace grows when a call needs more: the new
-// buffer comes from a memory pool the library owns per device and the old one
-// goes back to it, both in stream order (no device synchronisation).  The
-// buffers stay with the library until the process ends.
+// Split-K partials live in a workspace cached per stream: calls on one stream
+// run in order, so they share it.  A stream is identified by its unique id
+// where the HIP runtime in the process provides one (hipStreamGetId, looked up
+// at run time: the runtime that torch loads may predate it), so a stream
+// created after another was destroyed never inherits that one's buffer; with
+// an older runtime the stream handle is the key, and a caller that destroys a
+// stream while a split-K call on it is still running must not start calls on
+// a new stream before that work ends (the new stream may receive the same
+// handle).  A workspace grows when a call needs more: the new buffer comes
+// from a memory pool the library owns per device and the old one goes back to
+// it, both in the stream's order (no device synchronisation).  At most
+// kMaxCachedStreams streams keep a workspace; a call on any other stream takes
+// a buffer from the pool for itself and returns it after its two kernels, in
+// stream order.  The pool keeps freed blocks for reuse until the process
+// ends.  If no buffer can be had, the call runs without a split.  (An event
+// recorded after each call to order a reused handle behind the old work
+// would cost about 4 us of GPU time per call: measured, not used.)
+constexpr int kMaxCachedStreams = 64;
+
 struct StreamWorkspace {
   int dev;
-  hipStream_t stream;
+  unsigned long long key;  // stream id, or the handle's bits
   void* ptr;
   size_t bytes;
 };
 
 std::mutex g_ws_mutex;
 hipMemPool_t g_pool[kMaxDevices];
-StreamWorkspace g_ws[256];
+StreamWorkspace g_ws[kMaxCachedStreams];
 int g_ws_count = 0;
+
+// The cache key of `stream`: its id if the loaded runtime has hipStreamGetId.
+unsigned long long stream_key(hipStream_t stream) {
+  using GetId = hipError_t (*)(hipStream_t, unsigned long long*);
+  static const GetId get_id = reinterpret_cast<GetId>(dlsym(RTLD_DEFAULT, "hipStreamGetId"));
+  unsigned long long id = 0;
+  if (get_id && get_id(stream, &id) == hipSuccess) return id | (1ull << 63);
+  (void)hipGetLastError();
+  return reinterpret_cast<uintptr_t>(stream);
+}
 
 hipMemPool_t device_pool(int dev) {  // caller holds g_ws_mutex
   if (!g_pool[dev]) {
@@ -263,22 +295,31 @@ hipMemPool_t device_pool(int dev) {  // caller holds g_ws_mutex
   return g_pool[dev];
 }
 
-// A workspace of at least `bytes` usable in the order of `stream`, or null.
-void* stream_workspace(hipStream_t stream, size_t bytes) {
+// A split-K buffer of at least `bytes` usable in the order of `stream`, or
+// null.  *owned: the buffer is the call's own (return it with hipFreeAsync
+// after the kernels).
+void* stream_workspace(hipStream_t stream, size_t bytes, bool* owned) {
+  *owned = false;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  const unsigned long long key = stream_key(stream);
   std::lock_guard<std::mutex> lock(g_ws_mutex);
-  StreamWorkspace* w = nullptr;
-  for (int i = 0; i < g_ws_count; ++i)
-    if (g_ws[i].dev == dev && g_ws[i].stream == stream) w = &g_ws[i];
-  if (w && w->bytes >= bytes) return w->ptr;
-  if (!w) {
-    if (g_ws_count == (int)(sizeof(g_ws) / sizeof(g_ws[0]))) return nullptr;
-    w = &g_ws[g_ws_count++];
-    *w = StreamWorkspace{dev, stream, nullptr, 0};
-  }
   hipMemPool_t pool = device_pool(dev);
   if (!pool) return nullptr;
+  StreamWorkspace* w = nullptr;
+  for (int i = 0; i < g_ws_count; ++i)
+    if (g_ws[i].dev == dev && g_ws[i].key == key) w = &g_ws[i];
+  if (w && w->bytes >= bytes) return w->ptr;
+  if (!w && g_ws_count < kMaxCachedStreams) {
+    w = &g_ws[g_ws_count++];
+    *w = StreamWorkspace{dev, key, nullptr, 0};
+  }
+  if (!w) {  // not cached: a buffer for this call only
+    void* p = nullptr;
+    if (hipMallocFromPoolAsync(&p, bytes, pool, stream) != hipSuccess) return nullptr;
+    *owned = true;
+    return p;
+  }
   // grow geometrically so a sequence of slightly larger calls allocates rarely
   size_t want = w->bytes * 2 > bytes ? w->bytes * 2 : bytes;
   if (want > kMaxWorkspaceBytes) want = bytes;
@@ -296,29 +337,48 @@ bool stream_capturing(hipStream_t stream) {
   return cs != hipStreamCaptureStatusNone;
 }
 
-dg_status run(int kind, dg::Params& p, int rows, int n, int k, int groups, hipStream_t stream) {
+// Where split-K partials come from: the pool (scratch == nullptr; not while
+// the stream is being captured, then K is not split), or a device buffer of
+// scratch_floats floats that needs no allocation, which scratch() returns
+// (asked only once K is split; split K also under capture; a call whose
+// partials do not fit is rejected).
+dg_status run(int kind, dg::Params& p, int rows, int n, int k, int groups, hipStream_t stream,
+              float* (*scratch)() = nullptr, size_t scratch_floats = 0) {
   int cus = 0;
   if (device_cus(&cus) != 0) return DG_ERROR_LAUNCH;
   (void)hipGetLastError();  // clear a stale error from unrelated work
-  const bool may_split = (dense_like(kind) || kind == DG_KIND_MASKED) &&
-                         !stream_capturing(stream);
+  const bool splittable = dense_like(kind) || kind == DG_KIND_MASKED;
+  const bool may_split = splittable && (scratch != nullptr || !stream_capturing(stream));
   Launch l;
   dg_status st = plan(kind, rows, n, k, groups, cus, may_split, p, l);
   if (st != DG_SUCCESS) return st;
   auto launch_gemm = [&]() {
     return l.bdirect ? dg::launch_masked_bdirect(p, l.grid, stream) : dg::launch(kind, l.shape, p, l.grid, stream);
   };
-  if (p.splits <= 1) {
-    if (launch_gemm() != hipSuccess) return DG_ERROR_LAUNCH;
-    return DG_SUCCESS;
-  }
+  if (p.splits <= 1) return launch_gemm() == hipSuccess ? DG_SUCCESS : DG_ERROR_LAUNCH;
   p.ws_stride = (int64_t)groups * rows * n;
-  void* ws = stream_workspace(stream, (size_t)p.splits * p.ws_stride * sizeof(float));
-  if (!ws) return DG_ERROR_LAUNCH;
+  const size_t bytes = (size_t)p.splits * p.ws_stride * sizeof(float);
+  if (scratch) {
+    if (bytes > scratch_floats * sizeof(float)) return DG_ERROR_WORKSPACE;
+    p.ws = scratch();
+    if (!p.ws) return DG_ERROR_LAUNCH;
+    if (launch_gemm() != hipSuccess) return DG_ERROR_LAUNCH;
+    return dg::launch_splitk_reduce(kind, p, stream) == hipSuccess ? DG_SUCCESS : DG_ERROR_LAUNCH;
+  }
+  bool owned = false;
+  void* ws = stream_workspace(stream, bytes, &owned);
+  if (!ws) {
+    // no workspace to be had (out of memory): the same call without a split
+    (void)hipGetLastError();
+    st = plan(kind, rows, n, k, groups, cus, false, p, l);
+    if (st != DG_SUCCESS) return st;
+    return launch_gemm() == hipSuccess ? DG_SUCCESS : DG_ERROR_LAUNCH;
+  }
   p.ws = static_cast<float*>(ws);
-  if (launch_gemm() != hipSuccess) return DG_ERROR_LAUNCH;
-  if (dg::launch_splitk_reduce(kind, p, stream) != hipSuccess) return DG_ERROR_LAUNCH;
-  return DG_SUCCESS;
+  const bool ok = launch_gemm() == hipSuccess && dg::launch_splitk_reduce(kind, p, stream) == hipSuccess;
+  // the call's own buffer goes back to the pool after both kernels, in stream order
+  const bool freed = !owned || hipFreeAsync(ws, stream) == hipSuccess;
+  return ok && freed ? DG_SUCCESS : DG_ERROR_LAUNCH;
 }
 
 dg_status quantize(int mode, const float* x, void* q, float* s, int rows, int cols, hipStream_t stream) {
@@ -337,6 +397,36 @@ dg::Params base_params() {
 }
 
 }  // namespace
+
+namespace dg {
+// The masked-layout call with split-K partials from the pool (scratch ==
+// nullptr) or from the buffer scratch() returns (scratch_floats floats, no
+// allocation).
+dg_status grouped_masked(const void* a, const float* sa, const void* b, const float* sb, void* c,
+                         const int32_t* masked_m, int num_groups, int m_max, int n, int k, hipStream_t stream,
+                         float* (*scratch)(), size_t scratch_floats) {
+  if (!a || !sa || !b || !sb || !c || !masked_m) return DG_ERROR_INVALID_VALUE;
+  if (num_groups <= 0 || m_max <= 0 || n <= 0 || k <= 0) return DG_ERROR_INVALID_VALUE;
+  if (k % 128 != 0) return DG_ERROR_UNSUPPORTED;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(sa, 4) || !aligned(sb, 4) || !aligned(c, 2) ||
+      !aligned(masked_m, 4))
+    return DG_ERROR_UNSUPPORTED;
+  Params p = base_params();
+  p.a = static_cast<const uint8_t*>(a);
+  p.sa = sa;
+  p.b = static_cast<const uint8_t*>(b);
+  p.sb = sb;
+  p.out = c;
+  p.ctrl = masked_m;
+  p.m = m_max;
+  p.n = n;
+  p.lda = k;
+  p.kbs = k / 128;
+  p.groups = num_groups;
+  p.vec_out = (n % 4 == 0) && aligned(c, 8);
+  return run(KIND_MASKED, p, m_max, n, k, num_groups, stream, scratch, scratch_floats);
+}
+}  // namespace dg
 
 extern "C" {
 
@@ -431,26 +521,7 @@ dg_status dg_grouped_fp8_contiguous(const void* a, const float* sa, const void* 
 dg_status dg_grouped_fp8_masked(const void* a, const float* sa, const void* b, const float* sb,
                                 void* c, const int32_t* masked_m, int num_groups, int m_max, int n,
                                 int k, hipStream_t stream) {
-  if (!a || !sa || !b || !sb || !c || !masked_m) return DG_ERROR_INVALID_VALUE;
-  if (num_groups <= 0 || m_max <= 0 || n <= 0 || k <= 0) return DG_ERROR_INVALID_VALUE;
-  if (k % 128 != 0) return DG_ERROR_UNSUPPORTED;
-  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(sa, 4) || !aligned(sb, 4) || !aligned(c, 2) ||
-      !aligned(masked_m, 4))
-    return DG_ERROR_UNSUPPORTED;
-  dg::Params p = base_params();
-  p.a = static_cast<const uint8_t*>(a);
-  p.sa = sa;
-  p.b = static_cast<const uint8_t*>(b);
-  p.sb = sb;
-  p.out = c;
-  p.ctrl = masked_m;
-  p.m = m_max;
-  p.n = n;
-  p.lda = k;
-  p.kbs = k / 128;
-  p.groups = num_groups;
-  p.vec_out = (n % 4 == 0) && aligned(c, 8);
-  return run(dg::KIND_MASKED, p, m_max, n, k, num_groups, stream);
+  return dg::grouped_masked(a, sa, b, sb, c, masked_m, num_groups, m_max, n, k, stream, nullptr, 0);
 }
 
 dg_status dg_wgrad_fp8_nt(const void* a, const float* sa, const void* b, const float* sb, float* d,
@@ -517,6 +588,8 @@ const char* dg_status_string(dg_status s) {
     case DG_ERROR_INVALID_VALUE: return "invalid value (null pointer or a size <= 0)";
     case DG_ERROR_UNSUPPORTED: return "unsupported (K or row count not a multiple of 128, misaligned pointer, or layout limit)";
     case DG_ERROR_LAUNCH: return "kernel launch failed";
+    case DG_ERROR_WORKSPACE:
+      return "the call's split-K partials exceed the fixed scratch of the allocation-free entry point";
   }
   return "unknown status";
 }

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/dg.h"
+
 namespace dg {
 
 // Problem kinds; the kernel template is specialised on these.
@@ -73,6 +75,15 @@ hipError_t launch_swiglu_quantize(const uint16_t* c, uint8_t* q, float* s, int r
                                   hipStream_t stream);
 hipError_t launch_quantize(int mode, const float* x, uint8_t* q, float* s, int rows, int cols, int num_cus,
                            hipStream_t stream);
+
+// The masked-layout GEMM (dg_grouped_fp8_masked's contract) with split-K
+// partials from the library's pool (scratch == nullptr) or from the device
+// buffer of scratch_floats floats that scratch() returns, asked for only when
+// K is split, after the arguments are validated (no allocation; split K is
+// kept under graph capture; DG_ERROR_WORKSPACE if the partials do not fit).
+dg_status grouped_masked(const void* a, const float* sa, const void* b, const float* sb, void* c,
+                         const int32_t* masked_m, int num_groups, int m_max, int n, int k, hipStream_t stream,
+                         float* (*scratch)(), size_t scratch_floats);
 
 // True if an instance exists for (kind, shape).
 bool has_instance(int kind, const TileShape& shape);

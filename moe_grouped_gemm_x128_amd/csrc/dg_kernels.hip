@@ -1337,6 +1337,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const Params p, int 
 // (BM, BN, waves along M, waves along N, LDS ring stages)
 #define DG_SHAPES(X)      \
   X(256, 256, 1, 8, 2)    \
+  X(256, 32, 4, 1, 4)     \
+  X(256, 16, 4, 1, 4)     \
   X(256, 224, 4, 2, 2)    \
   X(256, 128, 1, 8, 3)    \
   X(256, 64, 1, 4, 3)     \
@@ -1367,8 +1369,11 @@ int lds_bytes_of(int kind, const TileShape& s) {
   const int sa_n = ((s.bm + 63) / 64) * 64;
   const int sb_n = row_sb ? ((s.bn + 63) / 64) * 64 : 64;
   const int stage = (s.bm + s.bn) * kBK + 4 * (sa_n + sb_n);
+  const int wtn = s.bn / s.wn;
+  const bool staged = !row_sb && (wtn == 64 || wtn == 32);  // bf16 epilogue staging buffers
+  const int out = staged ? s.wm * s.wn * 16 * (wtn * 2 + 16) : 16;
 #define X(BM, BN, WM, WN, S) \
-  if (s.bm == BM && s.bn == BN && s.wm == WM && s.wn == WN) return S * stage + 1024 + 8 * BM + 64;
+  if (s.bm == BM && s.bn == BN && s.wm == WM && s.wn == WN) return S * stage + 1024 + out;
   DG_SHAPES(X)
 #undef X
   return 0;

@@ -148,3 +148,113 @@ def test_quantise_then_gemm_pipeline_graph(dg):
         ob, osb = oracle.quantize_128x128(b)
         ref, _ = oracle.gemm_fp8_nt(oa, osa, ob, osb)
         check_close(bits_to_f64(bf16_bits(out)), bits_to_f64(ref), f"pipeline replay {rep}")
+
+
+def _masked_sample_check(x, bits, what, count=1536):
+    """Sampled valid outputs against the oracle; every row past masked_m keeps
+    its sentinel bits and every valid row is written."""
+    rng = np.random.default_rng(11)
+    valid = np.clip(x.masked_m, 0, x.m_max)
+    groups = [g for g in range(x.g) if valid[g] > 0]
+    if groups:
+        gs = rng.choice(groups, count)
+        rows = np.array([rng.integers(0, valid[g]) for g in gs], np.int64)
+        cols = rng.integers(0, x.n, count)
+        vals, wr = oracle.grouped_masked_at(x.a, x.sa, x.b, x.sb, x.masked_m, gs, rows, cols)
+        assert wr.all()
+        ref = oracle.round_bf16(vals)
+        check_close(bits_to_f64(bits[gs, rows, cols]), bits_to_f64(ref), what)
+    for g in range(x.g):
+        assert np.all(bits[g, valid[g]:] == 0xFFFF), f"{what}: group {g}: rows past masked_m written"
+        assert not np.any(bits[g, :valid[g]] == 0xFFFF), f"{what}: group {g}: valid rows left unwritten"
+
+
+@pytest.mark.parametrize("g,n,k", [(1, 4096, 7168), (1, 7168, 2048), (4, 4096, 7168), (4, 7168, 2048),
+                                   (16, 4096, 7168), (16, 7168, 2048)])
+def test_masked_graph_replays(dg, g, n, k):
+    """The masked decode GEMM captured at the decode workload sizes (the
+    pages' graph-captured case): replays with A, its scales and masked_m
+    rewritten on the device between them -- including 0, 1, M_max and more
+    than M_max rows -- each match the oracle, with the sentinel rows intact."""
+    m_max = 256
+    x = inputs.make_masked(g, m_max, n, k, seed=inputs.SEED_BASE + 120 + g)
+    cfg = dg.select_config(dg.KIND_MASKED, m_max, n, k, g)
+    say(f"masked graph G={g} N={n} K={k} (eager plan {cfg})")
+    a, sa = dev(x.a).view(torch.float8_e4m3fn), dev(x.sa)
+    b, sb = dev(x.b).view(torch.float8_e4m3fn), dev(x.sb)
+    mm = dev(x.masked_m)
+    out = sentinel_bf16((g, m_max, n))
+    graph = capture(lambda: dg.dg_grouped_fp8_masked(a, sa, b, sb, out, mm))
+    edge = [0, 1, m_max, m_max + 44]
+    rng = np.random.default_rng(g * 7 + k)
+    plans = [[edge[i % 4] for i in range(g)],
+             list(rng.integers(64, 193, g)),
+             [edge[(i + 2) % 4] for i in range(g)]]
+    for rep, counts in enumerate(plans):
+        y = inputs.make_masked(g, m_max, n, k, seed=inputs.SEED_BASE + 130 + rep, masked_m=counts)
+        a.copy_(dev(y.a).view(torch.float8_e4m3fn))
+        sa.copy_(dev(y.sa))
+        mm.copy_(dev(y.masked_m))
+        out.view(torch.int16).fill_(-1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        y.b, y.sb = x.b, x.sb  # B is not rewritten
+        _masked_sample_check(y, bf16_bits(out), f"masked G={g} N={n} K={k} replay {rep} masked_m={counts[:4]}")
+
+
+def test_contiguous_graph_replays(dg):
+    """The contiguous grouped GEMM captured once; replays with m_indices and A
+    rewritten on the device: padded segments, an empty expert, a segment
+    boundary inside a 256-row tile (two experts in one tile) and stray
+    out-of-range ids.  Each replay matches the oracle on every output, padding
+    rows keep their sentinel bits."""
+    g, rpe, n, k = 4, 512, 640, 2048
+    x = inputs.make_contiguous(g, rpe, n, k, seed=inputs.SEED_BASE + 140)
+    mt = x.m_total
+    say(f"contiguous graph G={g} rows/expert={rpe} N={n} K={k} ({dg.select_config(dg.KIND_CONTIGUOUS, mt, n, k, g)})")
+    a, sa = dev(x.a).view(torch.float8_e4m3fn), dev(x.sa)
+    b, sb = dev(x.b).view(torch.float8_e4m3fn), dev(x.sb)
+    ids = dev(x.m_indices)
+    out = sentinel_bf16((mt, n))
+    graph = capture(lambda: dg.dg_grouped_fp8_contiguous(a, sa, b, sb, out, ids))
+
+    def layout(kind):
+        m = np.full(mt, -1, np.int32)
+        if kind == 0:    # the harness's padded segments
+            return x.m_indices.copy()
+        if kind == 1:    # expert 1 empty; expert 2 takes two segments; 128-row segments
+            m[0:384] = 0
+            m[512:640] = 2
+            m[640:1000] = 2
+            m[1024:1100] = 3
+            m[1536:1920] = 3
+            return m
+        # segment boundaries at odd 128-row blocks (a 256-row tile holding two
+        # experts), padding at block ends, and out-of-range ids (skipped)
+        m[0:128] = 3
+        m[128:250] = 0
+        m[256:384] = 1
+        m[384:500] = 2
+        m[640:768] = 7
+        m[768:896] = -5
+        m[896:1020] = 1
+        return m
+
+    for rep in range(3):
+        y = inputs.make_contiguous(g, rpe, n, k, seed=inputs.SEED_BASE + 141 + rep)
+        mi = layout(rep)
+        a.copy_(dev(y.a).view(torch.float8_e4m3fn))
+        sa.copy_(dev(y.sa))
+        ids.copy_(dev(mi))
+        out.view(torch.int16).fill_(-1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        init = np.full((mt, n), 0xFFFF, np.uint16)
+        ref = oracle.grouped_contiguous(y.a, y.sa, x.b, x.sb, mi, init)
+        ref_bits = ref[0] if isinstance(ref, tuple) else ref
+        got = bf16_bits(out)
+        valid = (mi >= 0) & (mi < g)
+        assert np.all(got[~valid] == 0xFFFF), f"replay {rep}: padding or out-of-range rows written"
+        check_close(bits_to_f64(got[valid]), bits_to_f64(ref_bits[valid]), f"contiguous replay {rep}")
