@@ -121,6 +121,22 @@ dg_status dg_grouped_fp8_masked(const void* a, const float* sa, const void* b,
                                 const float* sb, void* c, const int32_t* masked_m,
                                 int num_groups, int m_max, int n, int k, hipStream_t stream);
 
+/* The masked-layout GEMM above for callers that cannot allocate device memory
+ * (code being captured into a HIP graph, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, layouts and results as
+ * dg_grouped_fp8_masked; the call allocates nothing: when K is split, the
+ * fp32 partials go to a fixed scratch array of 64 MB that the library holds
+ * on each GPU it runs on until the process ends (so split K is kept under
+ * capture, where dg_grouped_fp8_masked drops it).  Every call on a GPU
+ * shares that GPU's scratch: calls that overlap on one GPU (other streams,
+ * or graphs replayed concurrently) race and must be ordered by the caller.
+ * A call whose partials (splits * G * M_max * N * 4 bytes for the planned
+ * split) exceed the scratch returns DG_ERROR_WORKSPACE and enqueues nothing. */
+dg_status dg_grouped_fp8_masked_noalloc(const void* a, const float* sa, const void* b,
+                                        const float* sb, void* c, const int32_t* masked_m,
+                                        int num_groups, int m_max, int n, int k,
+                                        hipStream_t stream);
+
 /* Weight-gradient FP8 GEMM with fp32 output accumulated into D (DeepGEMM
  * pages, "反向传播中的梯度计算": dW from FP8 inputs, fp32 result without an
  * explicit cast).  K is the token dimension; both operands are token-

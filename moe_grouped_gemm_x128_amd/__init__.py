@@ -32,6 +32,7 @@ _vp, _i32 = ctypes.c_void_p, ctypes.c_int
 _lib.dg_gemm_fp8_nt.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]
 _lib.dg_grouped_fp8_contiguous.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]
 _lib.dg_grouped_fp8_masked.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]
+_lib.dg_grouped_fp8_masked_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]
 _lib.dg_wgrad_fp8_nt.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]
 _lib.dg_k_grouped_wgrad_fp8_nt.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]
 _lib.dg_gemm_fp8_nt_ue8m0.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]
@@ -40,7 +41,7 @@ _lib.dg_quantize_fp8_1x128.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
 _lib.dg_quantize_fp8_128x128.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
 _lib.dg_quantize_fp8_1x128_transposed.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
 _lib.dg_swiglu_quantize_fp8_1x128.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
-for _f in ("dg_gemm_fp8_nt", "dg_grouped_fp8_contiguous", "dg_grouped_fp8_masked",
+for _f in ("dg_gemm_fp8_nt", "dg_grouped_fp8_contiguous", "dg_grouped_fp8_masked", "dg_grouped_fp8_masked_noalloc",
            "dg_wgrad_fp8_nt", "dg_k_grouped_wgrad_fp8_nt", "dg_gemm_fp8_nt_ue8m0", "dg_gemm_bf16_nt", "dg_quantize_fp8_1x128",
            "dg_quantize_fp8_128x128", "dg_quantize_fp8_1x128_transposed", "dg_swiglu_quantize_fp8_1x128"):
     getattr(_lib, _f).restype = ctypes.c_int
@@ -190,6 +191,14 @@ def dg_grouped_fp8_contiguous(a, sa, b, sb, c, m_indices):
 
 def dg_grouped_fp8_masked(a, sa, b, sb, c, masked_m):
     return _grouped_masked(_lib.dg_grouped_fp8_masked, "dg_grouped_fp8_masked", a, sa, b, sb, c, masked_m)
+
+
+def dg_grouped_fp8_masked_noalloc(a, sa, b, sb, c, masked_m):
+    """dg_grouped_fp8_masked without any allocation (split-K partials in the
+    library's fixed 64 MB scratch; usable under graph capture).  Calls that
+    overlap on one GPU share the scratch and race."""
+    return _grouped_masked(_lib.dg_grouped_fp8_masked_noalloc, "dg_grouped_fp8_masked_noalloc",
+                           a, sa, b, sb, c, masked_m)
 
 
 def _grouped_masked(fn, name, a, sa, b, sb, c, masked_m):
