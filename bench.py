@@ -1,23 +1,35 @@
 """Benchmark of the FP8 fine-grained-scaled NT GEMM library on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload all]
 
 A step is one pass over the workload's GEMMs, each launched once through the
 C ABI on the current stream with inputs already resident in HBM.  The default
-workload is the dense sweep: M in {64,128,4096} x (N,K) in {(2112,7168),
-(24576,1536), (32768,512), (7168,16384), (4096,7168), (7168,2048)}, A scaled
-per 1x128, B per 128x128, bf16 out.  `value` is the step's algorithmic FLOPs
-(2*M*N*K per GEMM) over its measured time, in TFLOP/s; the timed steps launch
-the GEMMs back to back.  A separate pass brackets each GEMM by HIP events on the
-launch stream (the per-shape table); the one with the largest time is the
-"dominant kernel", which is also bracketed by events inside the timed steps,
-and whose roofline fraction is reported from those.  The CPU oracle is
-timed on a bounded sample of the same workload's outputs (`cpu_baseline`).
-Other workloads (contiguous, masked, wgrad, k_grouped_wgrad, small,
-dense_ue8m0 -- the sweep with power-of-two scales --, bf16 -- the sweep's
-shapes in BF16 against the bf16 peak --, quantize, the FP8 quantiser in
-GB/s, and swiglu_quantize, the SwiGLU + FP8 re-quantise step between an
-expert's two GEMMs in GB/s) print a line of the same form.  Exactly one JSON line goes to stdout.
+workload (`all`) is every configuration of the FP8 GEMM family at its real
+size: the dense sweep (M in {64,128,4096} x (N,K) in {(2112,7168),
+(24576,1536), (32768,512), (7168,16384), (4096,7168), (7168,2048)}), the MoE
+contiguous layout (G in {4,8} experts x 8192 rows, (N,K) in {(4096,7168),
+(7168,2048)}), the masked decode (G in {1,2,4,16}, M_max=256, same (N,K)) and
+the two weight gradients (7168x2048 over 4096 tokens, and over 4 experts of
+1024..4096 tokens), A scaled per 1x128, B per 128x128 (or per row along
+tokens), bf16 out (fp32 D for the weight gradients).  `value` is the step's
+algorithmic FLOPs (2*M_valid*N*K per GEMM) over its measured time, in
+TFLOP/s; the timed steps launch the GEMMs back to back.  A separate pass
+brackets each GEMM by HIP events on the launch stream (the per-shape table
+and the per-workload sub-results under `workloads`); the GEMM with the
+largest time is the "dominant kernel", which is also bracketed by events
+inside the timed steps, and whose roofline fraction is reported from those
+(`roofline.achieved`), next to the median of 50 dispatches each after a
+512 MB cache flush (`roofline.cold_median_us`).  The CPU oracle is timed on a
+bounded sample of the same workload's outputs (`cpu_baseline`).  The masked
+decode GEMMs are also captured into HIP graphs -- the default entry point and
+the allocation-free one -- and their replays timed (`masked_graph`).
+
+Other workloads (dense, contiguous, masked, wgrad, k_grouped_wgrad, small,
+dense_ue8m0 -- the dense sweep with power-of-two scales --, bf16 -- the
+sweep's shapes in BF16 against the bf16 peak --, quantize, the FP8 quantiser
+in GB/s, and swiglu_quantize, the SwiGLU + FP8 re-quantise step between an
+expert's two GEMMs in GB/s) print a line of the same form.  Exactly one JSON
+line goes to stdout.
 
 Before the W warmup steps the step runs untimed for at least half a second so
 the GPU clock has settled when timing starts.  `roofline.traffic` is the
@@ -57,6 +69,7 @@ def log(msg):
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "moe_grouped_gemm_x128_amd", "csrc", f)
                   for f in ("dg_kernels.hip", "dg_api.hip", "dg_kernel.h", "dg_quant.hip")]
+COLD_DISPATCHES = 50  # cold-cache dispatches of the dominant GEMM (median reported)
 
 
 def kernel_source_hash():
@@ -98,11 +111,15 @@ def copy_calibration():
 
 
 class Call:
-    """One GEMM launch of the step plus its algorithmic work."""
+    """One GEMM launch of the step plus its algorithmic work.  sample(rng,
+    count): the oracle on `count` uniformly drawn outputs of this GEMM,
+    returning the FLOPs that took (GEMMs) or (sample, width) for the
+    quantisers' row passes."""
 
-    def __init__(self, name, flops, nbytes, fn, sample=None, peak=PEAK_FP8_TFLOPS):
+    def __init__(self, name, flops, nbytes, fn, sample=None, peak=PEAK_FP8_TFLOPS, group=""):
         self.name, self.flops, self.bytes, self.fn, self.sample = name, flops, nbytes, fn, sample
         self.peak = peak  # dense MFMA peak of the launch's arithmetic type, TFLOP/s
+        self.group = group  # workload the GEMM belongs to
 
     @property
     def bound(self):
@@ -148,12 +165,14 @@ def build_dense(small=False, pow2=False):
               gemm(da_m, dsa_m, db, dsb, out))
         nbytes = m * k + m * (k // 128) * 4 + n * k + ((n + 127) // 128) * (k // 128) * 4 + m * n * 2
 
-        def sample(rng, count, a=a[:m], sa=sa[:m], b=b, sb=sb, m=m, n=n):
+        def sample(rng, count, a=a[:m], sa=sa[:m], b=b, sb=sb, m=m, n=n, k=k):
             import oracle
             r, c = _sample_idx(rng, count, m, n)
-            return oracle.gemm_fp8_nt_at(a, sa, b, sb, r, c)
+            oracle.gemm_fp8_nt_at(a, sa, b, sb, r, c)
+            return 2.0 * k * count
 
-        calls.append(Call(s["name"] + ("_ue8m0" if pow2 else ""), 2.0 * m * n * k, nbytes, fn, (sample, k)))
+        calls.append(Call(s["name"] + ("_ue8m0" if pow2 else ""), 2.0 * m * n * k, nbytes, fn, sample,
+                          group="dense"))
     desc = ("dense FP8 NT GEMM sweep: M in {64,128,4096} x (N,K) in {(2112,7168),(24576,1536),"
             "(32768,512),(7168,16384),(4096,7168),(7168,2048)}" if not small else "dense M=128 N=256 K=512")
     name = "dense_small" if small else ("dense_sweep_ue8m0" if pow2 else "dense_sweep")
@@ -162,21 +181,44 @@ def build_dense(small=False, pow2=False):
 
 
 def build_contiguous():
+    """MoE contiguous layout at 8192 rows per expert.  The G=4 problems are the
+    first four experts of the G=8 ones: the same seeded streams give the same
+    rows, weights and padding counts (make_contiguous draws them in order), so
+    each (N,K) is generated once and G=4 uses views of it."""
     import torch
     import moe_grouped_gemm_x128_amd as dg
     from harness import inputs, workloads
 
     calls = []
-    for s in workloads.contiguous_sweep():
-        c = inputs.make_contiguous(s["g"], s["rows_per_expert"], s["n"], s["k"], s["seed"])
-        da, dsa, db, dsb, ids = _dev(c.a), _dev(c.sa), _dev(c.b), _dev(c.sb), _dev(c.m_indices)
-        out = torch.empty((c.m_total, c.n), dtype=torch.bfloat16, device="cuda")
-        fn = (lambda da=da, dsa=dsa, db=db, dsb=dsb, out=out, ids=ids:
+    by_nk = {}
+    for s in sorted(workloads.contiguous_sweep(), key=lambda s: -s["g"]):
+        g, rpe, n, k = s["g"], s["rows_per_expert"], s["n"], s["k"]
+        if (n, k) not in by_nk:
+            c = inputs.make_contiguous(g, rpe, n, k, s["seed"])
+            by_nk[(n, k)] = (c, _dev(c.a), _dev(c.sa), _dev(c.b), _dev(c.sb), _dev(c.m_indices))
+        c, da, dsa, db, dsb, dids = by_nk[(n, k)]
+        assert g <= c.g
+        mt = g * rpe
+        a, sa, b, sb, ids = c.a[:mt], c.sa[:mt], c.b[:g], c.sb[:g], c.m_indices[:mt]
+        da_g, dsa_g, db_g, dsb_g, ids_g = da[:mt], dsa[:mt], db[:g], dsb[:g], dids[:mt]
+        out = torch.empty((mt, n), dtype=torch.bfloat16, device="cuda")
+        fn = (lambda da=da_g, dsa=dsa_g, db=db_g, dsb=dsb_g, out=out, ids=ids_g:
               dg.dg_grouped_fp8_contiguous(da, dsa, db, dsb, out, ids))
-        mv = int(c.valid.sum())
-        kb, nb = c.k // 128, (c.n + 127) // 128
-        nbytes = mv * c.k + mv * kb * 4 + c.g * c.n * c.k + c.g * nb * kb * 4 + c.m_total * 4 + mv * c.n * 2
-        calls.append(Call(s["name"], 2.0 * mv * c.n * c.k, nbytes, fn, None))
+        valid_rows = np.flatnonzero(ids >= 0)
+        mv = valid_rows.size
+        kb, nb = k // 128, (n + 127) // 128
+        nbytes = mv * k + mv * kb * 4 + g * n * k + g * nb * kb * 4 + mt * 4 + mv * n * 2
+
+        def sample(rng, count, a=a, sa=sa, b=b, sb=sb, ids=ids, rows=valid_rows, n=n, k=k):
+            import oracle
+            r = rows[rng.integers(0, rows.size, count)]
+            cl = rng.integers(0, n, count)
+            oracle.grouped_contiguous_at(a, sa, b, sb, ids, r, cl)
+            return 2.0 * k * count
+
+        calls.append(Call(s["name"], 2.0 * mv * n * k, nbytes, fn, sample, group="contiguous"))
+    order = [s["name"] for s in workloads.contiguous_sweep()]
+    calls.sort(key=lambda c: order.index(c.name))
     return calls, {"workload": "contiguous_sweep", "description":
                    "MoE contiguous: G in {4,8}, 8192 rows per expert minus U{0..127} padding rows, "
                    "(N,K) in {(4096,7168),(7168,2048)}"}
@@ -194,10 +236,24 @@ def build_masked():
         out = torch.empty((x.g, x.m_max, x.n), dtype=torch.bfloat16, device="cuda")
         fn = (lambda da=da, dsa=dsa, db=db, dsb=dsb, out=out, mm=mm:
               dg.dg_grouped_fp8_masked(da, dsa, db, dsb, out, mm))
-        mv = int(np.clip(x.masked_m, 0, x.m_max).sum())
+        fn_na = (lambda da=da, dsa=dsa, db=db, dsb=dsb, out=out, mm=mm:
+                 dg.dg_grouped_fp8_masked_noalloc(da, dsa, db, dsb, out, mm))
+        valid = np.clip(x.masked_m, 0, x.m_max)
+        mv = int(valid.sum())
         kb, nb = x.k // 128, (x.n + 127) // 128
         nbytes = mv * x.k + mv * kb * 4 + x.g * x.n * x.k + x.g * nb * kb * 4 + x.g * 4 + mv * x.n * 2
-        calls.append(Call(s["name"], 2.0 * mv * x.n * x.k, nbytes, fn, None))
+
+        def sample(rng, count, x=x, valid=valid):
+            import oracle
+            gs = rng.choice(np.flatnonzero(valid > 0), count)
+            rows = (rng.random(count) * valid[gs]).astype(np.int64)
+            cols = rng.integers(0, x.n, count)
+            oracle.grouped_masked_at(x.a, x.sa, x.b, x.sb, x.masked_m, gs, rows, cols)
+            return 2.0 * x.k * count
+
+        c = Call(s["name"], 2.0 * mv * x.n * x.k, nbytes, fn, sample, group="masked")
+        c.fn_noalloc = fn_na
+        calls.append(c)
     return calls, {"workload": "masked_sweep", "description":
                    "MoE masked decode: G in {1,2,4,16}, M_max=256, masked_m ~ U{64..192}, "
                    "(N,K) in {(4096,7168),(7168,2048)}"}
@@ -218,9 +274,35 @@ def build_wgrad(kgrouped=False):
     else:
         fn = lambda: dg.dg_wgrad_fp8_nt(da, dsa, db, dsb, d)
     nbytes = (w.m + w.n) * t + (w.m + w.n) * (t // 128) * 4 + g * 2 * 4 * w.m * w.n
-    calls = [Call(s["name"], 2.0 * w.m * w.n * t, nbytes, fn, None)]
+    ks = np.array(w.ks, np.int64)
+
+    def sample(rng, count):
+        import oracle
+        rows, cols = _sample_idx(rng, count, w.m, w.n)
+        if kgrouped:
+            gs = rng.integers(0, g, count)
+            oracle.k_grouped_wgrad_at(w.a, w.sa, w.b, w.sb, ks, w.d0, gs, rows, cols)
+            return 2.0 * float(ks[gs].sum())
+        oracle.wgrad_at(w.a, w.sa, w.b, w.sb, w.d0[0], rows, cols)
+        return 2.0 * t * count
+
+    calls = [Call(s["name"], 2.0 * w.m * w.n * t, nbytes, fn, sample, group="wgrad")]
     return calls, {"workload": s["name"], "description":
                    f"weight gradient D[{w.m},{w.n}] += over tokens {w.ks}, 1x128 scales on both operands, fp32 D"}
+
+
+def build_all():
+    """Every configuration of the GEMM family in one step: the dense sweep,
+    the contiguous and masked MoE layouts and both weight gradients."""
+    calls = []
+    for b in (build_dense, build_contiguous, build_masked, build_wgrad, lambda: build_wgrad(kgrouped=True)):
+        calls += b()[0]
+    return calls, {"workload": "fp8_gemm_all",
+                   "description": "dense sweep (18 GEMMs) + MoE contiguous (G 4/8 x 8192 rows, 4 GEMMs) + MoE "
+                                  "masked decode (G 1/2/4/16, 8 GEMMs) + weight gradient and K-grouped weight "
+                                  "gradient, one step",
+                   "gemms": len(calls), "scales": "A 1x128, B 128x128 (weight gradients: 1x128 on both)",
+                   "out": "bf16 (weight gradients: fp32 D)"}
 
 
 def build_bf16():
@@ -250,12 +332,14 @@ def build_bf16():
         fn = lambda da_m=da_m, db=db, out=out: dg.dg_gemm_bf16_nt(da_m, db, out)
         nbytes = 2 * (m * k + n * k + m * n)
 
-        def sample(rng, count, a=a[:m], b=b, m=m, n=n):
+        def sample(rng, count, a=a[:m], b=b, m=m, n=n, k=k):
             import oracle
             r, c = _sample_idx(rng, count, m, n)
-            return oracle.gemm_bf16_nt_at(a, b, r, c)
+            oracle.gemm_bf16_nt_at(a, b, r, c)
+            return 2.0 * k * count
 
-        calls.append(Call(s["name"] + "_bf16", 2.0 * m * n * k, nbytes, fn, (sample, k), peak=PEAK_BF16_TFLOPS))
+        calls.append(Call(s["name"] + "_bf16", 2.0 * m * n * k, nbytes, fn, sample, peak=PEAK_BF16_TFLOPS,
+                          group="bf16"))
     return calls, {"workload": "dense_sweep_bf16", "description": "the dense sweep's 18 shapes in BF16",
                    "shapes": len(calls), "scales": "none", "out": "bf16"}
 
@@ -305,7 +389,7 @@ def build_quantize():
             f(h)
             return rows * c * 5
 
-        calls.append(Call(name, 0.0, nbytes, fn, (sample, c)))
+        calls.append(Call(name, 0.0, nbytes, fn, (sample, c), group="quantize"))
     return calls, {"workload": "quantize", "description":
                    "FP8 quantiser: 1x128 activations [65536,7168] and [4096,7168], 128x128 weights "
                    "[7168,16384], token-contiguous 1x128 transposed [4096,7168] and [4096,2048]",
@@ -346,7 +430,7 @@ def build_swiglu():
             oracle.swiglu_quantize_1x128(bits)
             return rows * i * 5 + rows * (i // 128) * 4
 
-        calls.append(Call(name, 0.0, nbytes, fn, (sample, i)))
+        calls.append(Call(name, 0.0, nbytes, fn, (sample, i), group="swiglu_quantize"))
     return calls, {"workload": "swiglu_quantize", "description":
                    "SwiGLU (gate | up halves) + FP8 1x128 quantise of the first linear's bf16 output: "
                    "[65536, 4096], [65536, 7168] (G=8 x 8192 rows) and [4096, 4096] (16 x 256 decode rows)",
@@ -449,35 +533,114 @@ def time_steps(calls, steps, warmup, settle_s=0.5, cold=False):
 
 
 def cpu_baseline(calls, seconds):
-    """Time the CPU oracle on a bounded sample of the workload's outputs."""
+    """Time the CPU oracle on a bounded sample of the workload's outputs: the
+    same number of uniformly drawn outputs of every GEMM, sized so the timed
+    pass takes about `seconds`."""
     import oracle
     usable = [c for c in calls if c.sample is not None]
     if not usable:
         return None
     rng = np.random.default_rng(12345)
-    total_k = sum(c.sample[1] for c in usable)
     # calibrate: grow the sample until one pass takes a measurable share of
     # the budget, then size the timed sample to the whole budget
-    per_shape = 64
+    per_shape = 16
     while True:
         t = time.perf_counter()
         for c in usable:
-            c.sample[0](rng, per_shape)
+            c.sample(rng, per_shape)
         dt = time.perf_counter() - t
         if dt >= 0.1 * seconds or per_shape >= 1 << 22:
             break
         per_shape *= 4
-    rate = 2.0 * total_k * per_shape / max(dt, 1e-9)
-    per_shape = int(max(64, seconds * rate / (2.0 * total_k)))
+    per_shape = int(max(16, per_shape * seconds / max(dt, 1e-9)))
     t = time.perf_counter()
-    flops = 0.0
-    for c in usable:
-        c.sample[0](rng, per_shape)
-        flops += 2.0 * c.sample[1] * per_shape
+    flops = sum(c.sample(rng, per_shape) for c in usable)
     dt = time.perf_counter() - t
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{per_shape} uniformly drawn outputs of each of the {len(usable)} GEMMs "
                       f"({flops / 1e9:.1f} GFLOP, {dt:.1f} s, fp64 C oracle with OpenMP)"}
+
+
+def cold_median(call, dispatches=COLD_DISPATCHES):
+    """Median duration (ms) of `dispatches` launches of one GEMM, each after a
+    512 MB buffer (more than the MALL plus the L2s) is overwritten, each
+    bracketed by HIP events on the launch stream."""
+    import torch
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(dispatches)]
+    call.fn()
+    torch.cuda.synchronize()
+    for i in range(dispatches):
+        flush.fill_(i & 0xff)
+        ev[i][0].record()
+        call.fn()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+
+def graph_replay_ms(fns, reps=20):
+    """Capture `fns` (called in order) into one HIP graph on a side stream and
+    return the median replay time (ms), events around each replay."""
+    import torch
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        for f in fns:
+            f()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            for f in fns:
+                f()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        g.replay()
+        b.record()
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+
+def masked_graph(calls, per_ms):
+    """The masked decode GEMMs of the step: eager (sum of the per-call times),
+    captured with the default entry point (which does not split K under
+    capture) and captured with the allocation-free one (which keeps the split
+    in its fixed scratch)."""
+    idx = [i for i, c in enumerate(calls) if c.group == "masked"]
+    if not idx:
+        return None
+    ms = [calls[i] for i in idx]
+    eager = float(sum(per_ms[i] for i in idx))
+    default = graph_replay_ms([c.fn for c in ms])
+    noalloc = graph_replay_ms([c.fn_noalloc for c in ms])
+    flops = sum(c.flops for c in ms)
+    return {"gemms": len(ms), "eager_us": round(eager * 1e3, 1), "graph_us": round(default * 1e3, 1),
+            "graph_noalloc_us": round(noalloc * 1e3, 1),
+            "eager_tflops": round(flops / (eager * 1e-3) / 1e12, 1),
+            "graph_tflops": round(flops / (default * 1e-3) / 1e12, 1),
+            "graph_noalloc_tflops": round(flops / (noalloc * 1e-3) / 1e12, 1)}
+
+
+def workload_summary(calls, per_ms):
+    """Per workload of the step: its GEMMs' summed per-call time, TFLOP/s and
+    its dominant GEMM with that GEMM's fraction of its own bound."""
+    out = {}
+    for grp in dict.fromkeys(c.group for c in calls):
+        idx = [i for i, c in enumerate(calls) if c.group == grp]
+        ms = float(sum(per_ms[i] for i in idx))
+        flops = sum(calls[i].flops for i in idx)
+        nbytes = sum(calls[i].bytes for i in idx)
+        d = max(idx, key=lambda i: per_ms[i])
+        c = calls[d]
+        tf = c.flops / (per_ms[d] * 1e-3) / 1e12
+        gbs = c.bytes / (per_ms[d] * 1e-3) / 1e9
+        out[grp] = {"gemms": len(idx), "us": round(ms * 1e3, 1), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                    "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1), "dominant": c.name, "dominant_bound": c.bound,
+                    "dominant_frac": round(tf / c.peak if c.bound == "mfma" else gbs / PEAK_HBM_GBS, 4)}
+    return out
 
 
 def main():
@@ -485,11 +648,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="dense",
-                    choices=["dense", "small", "contiguous", "masked", "wgrad", "k_grouped_wgrad", "quantize",
+    ap.add_argument("--workload", default="all",
+                    choices=["all", "dense", "small", "contiguous", "masked", "wgrad", "k_grouped_wgrad", "quantize",
                              "dense_ue8m0", "bf16", "swiglu_quantize"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cold-median", action="store_true", help="skip the cold-cache median of the dominant GEMM")
     ap.add_argument("--settle-seconds", type=float, default=0.5, help="untimed run before the warmup steps")
     ap.add_argument("--only", default="", help="comma-separated GEMM names to time (others skipped)")
     ap.add_argument("--copy-calibration", action="store_true", help="run the counter-calibration copy and exit")
@@ -506,7 +670,7 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     log(f"device {torch.cuda.get_device_name(0)}, building workload {args.workload}")
-    builders = {"dense": build_dense, "small": lambda: build_dense(small=True),
+    builders = {"all": build_all, "dense": build_dense, "small": lambda: build_dense(small=True),
                 "contiguous": build_contiguous, "masked": build_masked,
                 "wgrad": build_wgrad, "k_grouped_wgrad": lambda: build_wgrad(kgrouped=True),
                 "quantize": build_quantize, "dense_ue8m0": lambda: build_dense(pow2=True), "bf16": build_bf16,
@@ -543,6 +707,18 @@ def main():
     roofline = {"bound": dc.bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": measured_traffic(dc.name), "kernel": dc.name,
                 "flops_per_launch": dc.flops, "bytes_per_launch": dc.bytes, "avg_us": round(dms * 1e3, 2)}
+    if not args.no_cold_median:
+        log(f"cold median of {COLD_DISPATCHES} dispatches of {dc.name}")
+        cms = cold_median(dc)
+        cold = dc.flops / (cms * 1e-3) / 1e12 if dc.bound == "mfma" else dc.bytes / (cms * 1e-3) / 1e9
+        roofline.update({"cold_median_us": round(cms * 1e3, 2), "cold_achieved": round(cold, 2),
+                         "cold_frac": round(cold / peak, 4), "cold_dispatches": COLD_DISPATCHES})
+    extra = {}
+    if len({c.group for c in calls}) > 1 or args.workload == "all":
+        extra["workloads"] = workload_summary(calls, per_ms)
+    if any(c.group == "masked" for c in calls) and not args.only:
+        log("masked decode GEMMs captured into HIP graphs")
+        extra["masked_graph"] = masked_graph(calls, per_ms)
 
     quant = args.workload in ("quantize", "swiglu_quantize")
     cpu = None
@@ -564,7 +740,7 @@ def main():
             "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": dtype, "data": data,
-            "config": config, "roofline": roofline, "cpu_baseline": cpu, "per_shape": shapes}
+            "config": config, "roofline": roofline, "cpu_baseline": cpu, **extra, "per_shape": shapes}
     print(json.dumps(line), flush=True)
 
 
