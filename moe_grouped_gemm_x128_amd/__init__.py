@@ -278,12 +278,20 @@ def dg_quantize_fp8_1x128_transposed(x, q, s):
     return q, s
 
 
+def _even_width(c):
+    """(M, 2I) of the first GEMM's output c: the gate and up halves need an
+    even width (an odd one would walk the rows with the wrong stride)."""
+    if c.dim() != 2 or c.shape[1] % 2:
+        raise ValueError(f"c must be [M, 2I] with an even width, got {tuple(c.shape)}")
+    return c.shape
+
+
 def dg_swiglu_quantize_fp8_1x128(c, q, s):
     """c bf16 [M,2I] (gate | up) -> q fp8 [M,I], s fp32 [M,I/128]: SwiGLU then
     the 1x128 quantise (see include/dg.h)."""
     _bf16(c, "c"); _fp8(q, "q"); _f32(s, "s")
+    m, i2 = _even_width(c)
     _dev(c, q, s)
-    m, i2 = c.shape
     i = i2 // 2
     _shape(q, (m, i), "q"); _shape(s, (m, i // 128), "s")
     _check(_lib.dg_swiglu_quantize_fp8_1x128(_ptr(c), _ptr(q), _ptr(s), m, i, _stream(c)),
@@ -345,7 +353,7 @@ def quantize_fp8_1x128_transposed(x):
 def swiglu_quantize_fp8_1x128(c):
     """Second-GEMM operand from the first GEMM's bf16 output c [M,2I]:
     (fp8 silu(gate)*up [M,I], fp32 scales [M,I/128])."""
-    m, i2 = c.shape
+    m, i2 = _even_width(c)
     i = i2 // 2
     return dg_swiglu_quantize_fp8_1x128(c, torch.empty((m, i), dtype=FP8, device=c.device),
                                         torch.empty((m, i // 128), dtype=torch.float32, device=c.device))

@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdg_mi355x.so")
-SOURCES = ["dg_api.hip", "dg_kernels.hip", "dg_quant.hip", "dg_noalloc.hip"]
+SOURCES = ["dg_api.hip", "dg_shapes.hip", "dg_kernels.hip", "dg_quant.hip", "dg_noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

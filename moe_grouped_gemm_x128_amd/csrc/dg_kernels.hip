@@ -31,6 +31,8 @@
 #include <type_traits>
 
 #include "dg_kernel.h"
+#include "dg_rsrc.h"
+#include "dg_shapes.h"
 
 namespace dg {
 namespace {
@@ -88,9 +90,10 @@ __device__ __forceinline__ Rsrc buffer_rsrc(const void* base, uint32_t num_bytes
 // did, and a dead or exhausted resource reads zeros without touching memory
 // (the range never wraps below zero).
 __device__ __forceinline__ v4i at(const Rsrc& r, uint32_t bytes, bool live) {
-  const uint64_t b = (((uint64_t)r.hi << 32) | r.lo) + bytes;
-  const uint32_t num = __builtin_amdgcn_readfirstlane(live && bytes < r.num ? r.num - bytes : 0u);  // wave-uniform
-  return v4i{(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xffffu), (int)num, (int)r.flags};
+  uint32_t lo, hi;
+  base_moved(r.lo, r.hi, bytes, &lo, &hi);
+  const uint32_t num = __builtin_amdgcn_readfirstlane(range_after(r.num, bytes, live));  // wave-uniform
+  return v4i{(int)lo, (int)hi, (int)num, (int)r.flags};
 }
 
 #pragma clang diagnostic push
@@ -434,10 +437,10 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   // r advanced by `bytes` with its range cut where it ended (empty if that is
   // past the end or !on); wave-uniform
   auto moved = [](const Rsrc& r, uint32_t bytes, bool on) {
-    const uint64_t b = (((uint64_t)r.hi << 32) | r.lo) + bytes;
-    return Rsrc{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b),
-                (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xffffu),
-                (uint32_t)__builtin_amdgcn_readfirstlane(on && bytes < r.num ? r.num - bytes : 0u), r.flags};
+    uint32_t lo, hi;
+    base_moved(r.lo, r.hi, bytes, &lo, &hi);
+    return Rsrc{(uint32_t)__builtin_amdgcn_readfirstlane(lo), (uint32_t)__builtin_amdgcn_readfirstlane(hi),
+                (uint32_t)__builtin_amdgcn_readfirstlane(range_after(r.num, bytes, on)), r.flags};
   };
   auto make_res = [&](const Tile& x) -> Res {
     const int bg = (KIND == KIND_KGROUPED) ? 0 : x.g;  // K-grouped: one B [N,T]
@@ -533,10 +536,10 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     // offset, so the range stays positive; a dead block or source reads
     // nothing.
     auto at_k = [](const Rsrc& r, uint32_t koff, bool live) {
-      const uint64_t b = (((uint64_t)r.hi << 32) | r.lo) + koff;
-      return v4i{(int)__builtin_amdgcn_readfirstlane((uint32_t)b),
-                 (int)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xffffu),
-                 (int)__builtin_amdgcn_readfirstlane((live && r.num != 0u) ? r.num - koff : 0u), (int)r.flags};
+      uint32_t lo, hi;
+      base_moved(r.lo, r.hi, koff, &lo, &hi);
+      return v4i{(int)__builtin_amdgcn_readfirstlane(lo), (int)__builtin_amdgcn_readfirstlane(hi),
+                 (int)__builtin_amdgcn_readfirstlane(range_at_k(r.num, koff, live)), (int)r.flags};
     };
     auto blk_of = [&](const Res& r, int rel, int st) -> Blk {
       const bool live = rel < r.nkb;
@@ -977,13 +980,6 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   wait_vm<0>();  // no DMA (dead blocks included) outlives the workgroup
 }
 
-// Instances left out: the 256x256 tile with 2x4 waves needs more than the
-// register file for the fp32 read-modify-write epilogue of the weight-gradient
-// kinds (it would spill); those kinds use the 1x8 layout of that tile.
-constexpr bool excluded(int bm, int bn, int wm, int kind) {
-  return bm == 256 && bn == 256 && wm == 2 && (kind == KIND_WGRAD || kind == KIND_KGROUPED);
-}
-
 template <int BM, int BN, int WM, int WN, int S, int KIND>
 void launch_kind(dim3 g, dim3 b, hipStream_t stream, const Params& p) {
   if constexpr (!excluded(BM, BN, WM, KIND))
@@ -1147,7 +1143,7 @@ __global__ __launch_bounds__(512) void masked_bdirect_kernel(const Params p) {
       const uint32_t koff = __builtin_amdgcn_readfirstlane((kb0 + rel) * kBK);
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
           (void*)((((uint64_t)rsB.hi << 32) | rsB.lo) + koff), (short)0,
-          (int)(live && koff < rsB.num ? rsB.num - koff : 0u),  // a wave past N reads nothing
+          (int)range_after(rsB.num, koff, live),  // a wave past N reads nothing
           (int)rsB.flags);
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
@@ -1334,50 +1330,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const Params p, int 
   }
 }
 
-// (BM, BN, waves along M, waves along N, LDS ring stages)
-#define DG_SHAPES(X)      \
-  X(256, 256, 1, 8, 2)    \
-  X(256, 32, 4, 1, 4)     \
-  X(256, 16, 4, 1, 4)     \
-  X(256, 224, 4, 2, 2)    \
-  X(256, 128, 1, 8, 3)    \
-  X(256, 64, 1, 4, 3)     \
-  X(256, 128, 1, 4, 3)    \
-  X(256, 128, 2, 2, 3)    \
-  X(256, 256, 2, 4, 2)    \
-  X(128, 128, 2, 2, 4)    \
-  X(128, 64, 2, 2, 4)     \
-  X(64, 128, 1, 4, 4)     \
-  X(64, 64, 1, 4, 4)      \
-  X(64, 32, 2, 2, 4)
-
 }  // namespace
-
-bool has_instance(int kind, const TileShape& s) {
-  if (kind < KIND_DENSE || kind > KIND_BF16) return false;
-#define X(BM, BN, WM, WN, S) \
-  if (s.bm == BM && s.bn == BN && s.wm == WM && s.wn == WN) return !excluded(BM, BN, WM, kind);
-  DG_SHAPES(X)
-#undef X
-  return false;
-}
-
-int threads_of(const TileShape& s) { return s.wm * s.wn * 64; }
-
-int lds_bytes_of(int kind, const TileShape& s) {
-  const bool row_sb = (kind == KIND_WGRAD || kind == KIND_KGROUPED);
-  const int sa_n = ((s.bm + 63) / 64) * 64;
-  const int sb_n = row_sb ? ((s.bn + 63) / 64) * 64 : 64;
-  const int stage = (s.bm + s.bn) * kBK + 4 * (sa_n + sb_n);
-  const int wtn = s.bn / s.wn;
-  const bool staged = !row_sb && (wtn == 64 || wtn == 32);  // bf16 epilogue staging buffers
-  const int out = staged ? s.wm * s.wn * 16 * (wtn * 2 + 16) : 16;
-#define X(BM, BN, WM, WN, S) \
-  if (s.bm == BM && s.bn == BN && s.wm == WM && s.wn == WN) return S * stage + 1024 + out;
-  DG_SHAPES(X)
-#undef X
-  return 0;
-}
 
 hipError_t launch_masked_bdirect(const Params& p, int grid, hipStream_t stream) {
   hipLaunchKernelGGL(masked_bdirect_kernel<3>, dim3(grid), dim3(512), 0, stream, p);

@@ -1,0 +1,35 @@
+// dg_shapes.h -- the GEMM kernel's tile instances (one table for the kernel
+// dispatch in dg_kernels.hip and the host-side queries in dg_shapes.hip).
+#pragma once
+
+#include "dg_kernel.h"
+
+namespace dg {
+
+constexpr int kBlockK = 128;  // K block = scale granularity
+
+// (BM, BN, waves along M, waves along N, LDS ring stages)
+#define DG_SHAPES(X)      \
+  X(256, 256, 1, 8, 2)    \
+  X(256, 32, 4, 1, 4)     \
+  X(256, 16, 4, 1, 4)     \
+  X(256, 224, 4, 2, 2)    \
+  X(256, 128, 1, 8, 3)    \
+  X(256, 64, 1, 4, 3)     \
+  X(256, 128, 1, 4, 3)    \
+  X(256, 128, 2, 2, 3)    \
+  X(256, 256, 2, 4, 2)    \
+  X(128, 128, 2, 2, 4)    \
+  X(128, 64, 2, 2, 4)     \
+  X(64, 128, 1, 4, 4)     \
+  X(64, 64, 1, 4, 4)      \
+  X(64, 32, 2, 2, 4)
+
+// Instances left out: the 256x256 tile with 2x4 waves needs more than the
+// register file for the fp32 read-modify-write epilogue of the weight-gradient
+// kinds (it would spill); those kinds use the 1x8 layout of that tile.
+constexpr bool excluded(int bm, int bn, int wm, int kind) {
+  return bm == 256 && bn == 256 && wm == 2 && (kind == KIND_WGRAD || kind == KIND_KGROUPED);
+}
+
+}  // namespace dg

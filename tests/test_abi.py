@@ -285,3 +285,10 @@ def test_python_binding_rejects_cpu_tensors_and_bad_shapes():
     with pytest.raises(TypeError):
         dg.dg_gemm_fp8_nt(a, sa.double(), b, sb, c)
     assert dg.select_config(dg.KIND_DENSE, 4096, 7168, 16384)["tiles"] > 0
+    # SwiGLU input of odd width: the gate / up halves are undefined
+    odd = torch.empty(4, 257, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        dg.dg_swiglu_quantize_fp8_1x128(odd, torch.empty(4, 128, dtype=torch.uint8).view(torch.float8_e4m3fn),
+                                        torch.empty(4, 1))
+    with pytest.raises(ValueError):
+        dg.swiglu_quantize_fp8_1x128(odd)
