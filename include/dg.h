@@ -41,10 +41,8 @@
  *   - environment overrides for tests and tuning, read at each call:
  *     DG_FORCE_TILE=BMxBNxWMxWN forces a tile instance (UNSUPPORTED if the kind
  *     has none), DG_FORCE_SPLITS=s forces s K splits where splitting is
- *     allowed, DG_MASKED_BDIRECT=1 runs the masked layout on the decode
- *     kernel that streams B into registers (by default the general kernel
- *     serves it), DG_LOG=1 prints each plan
- *     to stderr.  Results stay within the same accuracy bound either way.
+ *     allowed, DG_LOG=1 prints each plan to stderr.  Results stay within the
+ *     same accuracy bound either way.
  */
 #ifndef DG_MI355X_H
 #define DG_MI355X_H
@@ -240,8 +238,7 @@ typedef struct {
   int tiles;        /* tile count (an upper bound for the masked layout)     */
   int grid;         /* persistent workgroups launched                        */
   int k_splits;     /* workgroups sharing one output tile along K (1 = none) */
-  int kernel;       /* 0: general kernel; 1: masked decode kernel streaming B
-                       into registers (block 256x256, 8 waves)            */
+  int kernel;       /* always 0: every layout runs on the general kernel    */
 } dg_tile_config;
 
 dg_status dg_select_config(int kind, int m, int n, int k, int num_groups, int num_cus,

@@ -177,20 +177,7 @@ dg::TileShape heuristic(int kind, int rows, int n, int k, int groups, int num_cu
 struct Launch {
   dg::TileShape shape;
   int grid;
-  bool bdirect;  // masked layout: the B-in-registers decode kernel
 };
-
-// Masked layout: the decode kernel that streams B into registers (256x256
-// tiles, 8 waves, K blocks in pairs), taken only when DG_MASKED_BDIRECT=1.
-// It was faster than the general kernel until the general kernel's B loads
-// took the streaming cache policy; since then the general kernel wins on
-// every decode shape of the page workloads (cold: G=16, N=7168, K=2048 82 vs
-// 92 us; G=16, N=4096, K=7168 144 vs 148 us; G=4 54 vs 62 us).
-bool use_bdirect(int kind, int k) {
-  if (kind != DG_KIND_MASKED || (k / 128) % 2 != 0) return false;
-  const char* e = std::getenv("DG_MASKED_BDIRECT");
-  return e && e[0] == '1';
-}
 
 // `allow_split`: split-K needs a temporary workspace, so it is planned only
 // for calls that may allocate (not under stream capture).
@@ -199,16 +186,13 @@ dg_status plan(int kind, int rows, int n, int k, int groups, int num_cus, bool a
   dg::TileShape s;
   const bool forced = parse_forced(&s);
   if (!forced) s = heuristic(kind, rows, n, k, groups, num_cus, allow_split);
-  // (the decode kernel takes K blocks in pairs: an even count per work item)
-  l.bdirect = use_bdirect(kind, k);
-  if (l.bdirect) s = dg::TileShape{256, 256, 1, 8};
   if (!dg::has_instance(kind, s)) return DG_ERROR_UNSUPPORTED;
   p.tiles_m = ceil_div(rows, s.bm);
   p.tiles_n = ceil_div(n, s.bn);
   const long tiles = (long)groups * p.tiles_m * p.tiles_n;
   if (tiles > 0x7fffffffL / kMaxSplits) return DG_ERROR_UNSUPPORTED;
   p.tiles = (int)tiles;
-  const long slots = l.bdirect ? (long)num_cus : (long)num_cus * occupancy(kind, s);
+  const long slots = (long)num_cus * occupancy(kind, s);
   const int kbs = k / 128;
   int splits = allow_split ? choose_splits(kind, rows, tiles, num_cus, kbs) : 1;
   if (const char* e = std::getenv("DG_FORCE_SPLITS"))
@@ -221,7 +205,6 @@ dg_status plan(int kind, int rows, int n, int k, int groups, int num_cus, bool a
   while (splits > 1 && splits * split_bytes > (double)kMaxWorkspaceBytes) --splits;
   // equal chunks with no empty split: every partial the reduction reads is written
   int chunk = ceil_div(kbs, splits);
-  if (l.bdirect && chunk % 2) ++chunk;  // K blocks in pairs (kbs is even)
   splits = ceil_div(kbs, chunk);
   p.splits = splits;
   p.kchunk = chunk;
@@ -353,7 +336,7 @@ dg_status run(int kind, dg::Params& p, int rows, int n, int k, int groups, hipSt
   dg_status st = plan(kind, rows, n, k, groups, cus, may_split, p, l);
   if (st != DG_SUCCESS) return st;
   auto launch_gemm = [&]() {
-    return l.bdirect ? dg::launch_masked_bdirect(p, l.grid, stream) : dg::launch(kind, l.shape, p, l.grid, stream);
+    return dg::launch(kind, l.shape, p, l.grid, stream);
   };
   if (p.splits <= 1) return launch_gemm() == hipSuccess ? DG_SUCCESS : DG_ERROR_LAUNCH;
   p.ws_stride = (int64_t)groups * rows * n;
@@ -613,7 +596,7 @@ dg_status dg_select_config(int kind, int m, int n, int k, int num_groups, int nu
   out->tiles = p.tiles;
   out->grid = l.grid;
   out->k_splits = p.splits;
-  out->kernel = l.bdirect ? 1 : 0;
+  out->kernel = 0;
   return DG_SUCCESS;
 }
 

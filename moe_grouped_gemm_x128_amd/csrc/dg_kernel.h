@@ -60,10 +60,6 @@ struct TileShape {
 hipError_t launch(int kind, const TileShape& shape, const Params& p, int grid,
                   hipStream_t stream);
 
-// Masked layout, 256x256 tiles (p.tiles_n = ceil(N/256)), B streamed into
-// registers (8 waves, 512 threads; one workgroup per CU).
-hipError_t launch_masked_bdirect(const Params& p, int grid, hipStream_t stream);
-
 // Sums the split-K partials of p.ws in split order and writes bf16 p.out
 // (dense: every row; masked: rows below masked_m of each group).
 hipError_t launch_splitk_reduce(int kind, const Params& p, hipStream_t stream);

@@ -591,6 +591,10 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     if constexpr (kFp32Out) {
       // D += ...: the accumulators start from D, loaded here so the loads
       // overlap the tile's first K blocks and the epilogue only stores
+      // (lane indices opaque: see the epilogue)
+      const int lane = (int)opaque(threadIdx.x & 63u);
+      const int l16 = lane & 15;
+      const int lq = lane >> 4;
 #pragma unroll
       for (int j = 0; j < FM; ++j) {
         const int ml = wm * WTM + 16 * j + l16;
@@ -834,6 +838,12 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     }
 
     // ---- epilogue ----
+    // The lane's indices made anew, opaque to the compiler: otherwise it
+    // computes the epilogue's lane-dependent offsets and masks once before
+    // the first tile and keeps them in registers through every K loop.
+    const int lane = (int)opaque(threadIdx.x & 63u);
+    const int l16 = lane & 15;
+    const int lq = lane >> 4;
     // contiguous: does row 16*j + r of this wave's rows carry the tile's expert
     // (j a compile-time fragment row, r < 16)
     auto rbit = [&](int j, int r) -> bool {
@@ -1018,280 +1028,6 @@ hipError_t launch_shape(int kind, const Params& p, int grid, hipStream_t stream)
   return hipGetLastError();
 }
 
-// Masked decode with B streamed into registers (every work item has an even
-// number of K blocks: the host uses it only then).  The decode GEMM reads each
-// expert's B once and is bound by HBM; staging B through the LDS ring of the
-// general kernel keeps only one stage in flight per CU behind a barrier per K
-// block.  Here the 256 token rows of A (shared by all waves) and the scales go
-// through an LDS ring of SA stages, while each of the 8 waves loads its own 32
-// B columns straight into VGPRs, SA-1 K blocks ahead, with ordinary buffer
-// loads (so the compiler places the waits before their first use).  Tile:
-// 256 rows x 256 columns per workgroup, one wave per 32 columns; waves skip
-// the row quarters past masked_m as in the general kernel.
-template <int SA>
-__global__ __launch_bounds__(512) void masked_bdirect_kernel(const Params p) {
-  constexpr int BM = 256, BN = 256, NW = 8, WTN = 32;
-  constexpr int FM = BM / 16, NF = WTN / 16;  // 16 row fragments, 2 column fragments per wave
-  constexpr int NO = FM, NR = NF;             // rows streamed, columns resident
-  constexpr int P = SA - 1;                   // B lookahead (K blocks)
-  constexpr int OFF_SA = BM * kBK;
-  constexpr int OFF_SB = OFF_SA + BM * 4;
-  constexpr int STAGE = OFF_SB + 64 * 4;
-  constexpr int PA = BM / 8, QA = PA / NW;    // A pieces (1 KB) per wave
-  constexpr int PSA = BM / 64, PS = PSA + 1, QS = (PS + NW - 1) / NW;
-  constexpr int DA = QA + QS;                 // DMAs per K block per wave
-  constexpr int DB = 2 * NF;                  // B loads per K block per wave
-  static_assert(P == 2, "B ring of two register slots");
-
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[SA * STAGE + 1024];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l16 = lane & 15;
-  const int lq = lane >> 4;
-  const uint32_t smem_lds = lds_addr(smem);
-  const uint32_t frag_lo = l16 * kBK + (((2 * lq) ^ swz(l16)) << 4);
-  const uint32_t frag_hi = l16 * kBK + (((2 * lq + 1) ^ swz(l16)) << 4);
-
-  int T = 0;
-  for (int g = 0; g < p.groups; ++g) {
-    const int v = min(max(p.ctrl[g], 0), p.m);
-    T += ((v + BM - 1) / BM) * p.tiles_n;
-  }
-  const int splits = p.splits;
-  const int TS = T * splits;
-  const int per_xcd = (TS + 7) >> 3;
-  const int nb_rows = (p.n + kBK - 1) / kBK;
-
-  for (int t = blockIdx.x; t < per_xcd * 8; t += gridDim.x) {
-    const int LS = (t & 7) * per_xcd + (t >> 3);
-    if (LS >= TS) continue;
-    const int L = splits > 1 ? LS / splits : LS;
-    const int split = LS - L * splits;
-    int rem = L, mt = 0, v = 0, g = 0;
-    for (; g < p.groups; ++g) {
-      v = min(max(p.ctrl[g], 0), p.m);
-      mt = (v + BM - 1) / BM;
-      const int cnt = mt * p.tiles_n;
-      if (rem < cnt) break;
-      rem -= cnt;
-    }
-    if (g >= p.groups) continue;
-    const int m0 = (rem % mt) * BM;
-    const int n0 = (rem / mt) * BN;
-    const int rows = min(BM, v - m0);
-    const int64_t row0 = (int64_t)g * p.m + m0;
-    int kb0 = 0, kb1 = p.kbs;
-    if (splits > 1) {
-      kb0 = split * p.kchunk;
-      kb1 = min(p.kbs, kb0 + p.kchunk);
-    }
-    const int nkb = kb1 - kb0;
-    if (nkb <= 0) continue;
-
-    // ---- resources ----
-    const Rsrc rsA = buffer_rsrc(p.a + row0 * (int64_t)p.lda, (uint32_t)rows * p.lda);
-    const Rsrc rsSA = buffer_rsrc(p.sa + row0 * (int64_t)p.kbs, (uint32_t)rows * p.kbs * 4);
-    const int nb0 = n0 / kBK;
-    const int nbt = min(nb_rows - nb0, BN / kBK);
-    const Rsrc rsSB = buffer_rsrc(p.sb + ((int64_t)g * nb_rows + nb0) * p.kbs, (uint32_t)max(nbt, 0) * p.kbs * 4);
-    // this wave's B columns: rows n0 + 32*wave .. +31 of B[g]
-    const int wcol0 = n0 + wave * WTN;
-    const int wcols = max(0, min(WTN, p.n - wcol0));
-    const Rsrc rsB = buffer_rsrc(p.b + ((int64_t)g * p.n + wcol0) * (int64_t)p.lda, (uint32_t)wcols * p.lda);
-    const int r0 = wave * 8 + (lane >> 3);
-    const uint32_t voff0 = (uint32_t)r0 * p.lda + (((lane & 7) ^ swz(r0)) << 4);
-    const uint32_t step = (uint32_t)(NW * 8) * p.lda;
-    const uint32_t svoff = (uint32_t)lane * p.kbs * 4;
-    const uint32_t sstep = 64u * p.kbs * 4;
-    // B: lane (l16, lq) of column fragment f reads row 16f + l16, bytes 32*lq .. +31
-    const uint32_t bvoff = (uint32_t)l16 * p.lda + 32u * lq;
-
-    // A and scale DMAs of K block rel (dead past nkb: empty range, sink)
-    auto issue_a = [&](int rel, int lo, int hi) {
-      const bool live = rel < nkb;
-      const int kb = kb0 + rel;
-      const uint32_t base = smem_lds + (rel % SA) * STAGE;
-      const uint32_t koff = __builtin_amdgcn_readfirstlane(kb * kBK);
-      const uint32_t skoff = __builtin_amdgcn_readfirstlane(kb * 4);
-      const v4i ra = at(rsA, koff, live);
-#pragma unroll
-      for (int q = 0; q < QA; ++q)
-        if (q >= lo && q < hi) dma16(base + (wave + NW * q) * 1024, ra, voff0 + q * step);
-#pragma unroll
-      for (int q = 0; q < QS; ++q) {
-        if (QA + q < lo || QA + q >= hi) continue;
-        const int sp = wave + NW * q;
-        const bool is_a = sp < PSA, real = sp < PS && live;
-        const uint32_t f = (uint32_t)__builtin_amdgcn_readfirstlane(is_a ? 1 : 0);
-        Rsrc sel;
-        sel.lo = rsSB.lo + (rsSA.lo - rsSB.lo) * f;
-        sel.hi = rsSB.hi + (rsSA.hi - rsSB.hi) * f;
-        sel.num = rsSB.num + (rsSA.num - rsSB.num) * f;
-        sel.flags = rsSA.flags;
-        const v4i r4 = at(sel, skoff, real);
-        const v4i rs = v4i{(int)__builtin_amdgcn_readfirstlane(r4[0]), (int)__builtin_amdgcn_readfirstlane(r4[1]),
-                           (int)__builtin_amdgcn_readfirstlane(r4[2]), (int)__builtin_amdgcn_readfirstlane(r4[3])};
-        const uint32_t lds = __builtin_amdgcn_readfirstlane(sp < PS ? base + OFF_SA + sp * 256 : smem_lds + SA * STAGE);
-        dma4(lds, rs, svoff + (uint32_t)(is_a ? sp : sp - PSA) * sstep);
-      }
-    };
-    // B of K block rel into registers (zeros past nkb or past N)
-    auto load_b = [&](int rel, v8i (&dst)[NF]) {
-      const bool live = rel < nkb;
-      const uint32_t koff = __builtin_amdgcn_readfirstlane((kb0 + rel) * kBK);
-      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)((((uint64_t)rsB.hi << 32) | rsB.lo) + koff), (short)0,
-          (int)range_after(rsB.num, koff, live),  // a wave past N reads nothing
-          (int)rsB.flags);
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        const uint32_t off = bvoff + (uint32_t)(16 * f) * p.lda;
-        // (cache policy 2 = nontemporal: each expert's B is streamed once)
-        const v4i lo = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
-        const v4i hi = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 2));
-        dst[f] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
-    };
-
-    v4f acc[NF][FM];
-#pragma unroll
-    for (int i = 0; i < NF; ++i)
-#pragma unroll
-      for (int j = 0; j < FM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-    v4f part[NR];
-    float pend[NR];
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      part[r] = v4f{0.f, 0.f, 0.f, 0.f};
-      pend[r] = 0.f;
-    }
-    auto fma4 = [&](v4f& a, float sc, const v4f& pr) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) a[e] = __builtin_fmaf(sc, pr[e], a[e]);
-    };
-    v8i bq0[NF], bq1[NF];  // B ring: K blocks of even / odd index
-
-    auto k_loop = [&](auto nov_c) {
-      constexpr int NOV = decltype(nov_c)::value;
-      // prologue: blocks 0 .. SA-2 (A then B, as in the loop)
-#pragma unroll
-      for (int s = 0; s < SA - 1; ++s) {
-        issue_a(s, 0, DA);
-        if (s % 2 == 0) load_b(s, bq0); else load_b(s, bq1);
-      }
-      // one K block; SLOT = rel % 2 (static)
-      auto block = [&](int rel, auto slot_c) {
-        constexpr int SLOT = decltype(slot_c)::value;
-        // A(rel) is done once at most the ops issued after it remain: B(rel),
-        // then A and B of the SA-2 blocks that follow
-        wait_vm<DB + (SA - 2) * (DA + DB)>();
-        barrier();
-        const uint8_t* sA = smem + (rel % SA) * STAGE;
-        const float* sSA = reinterpret_cast<const float*>(sA + OFF_SA);
-        const float* sSB = reinterpret_cast<const float*>(sA + OFF_SB);
-        v8i(&res)[NR] = SLOT == 0 ? bq0 : bq1;  // this block's B, in place
-        const float sb = sSB[(wcol0 / kBK) - nb0];
-        auto load_a = [&](int o) { return load_frag(sA + o * 16 * kBK, frag_lo, frag_hi); };
-        v8i cur = NOV > 0 ? load_a(0) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
-        // the row scale of group o is read when the group starts: only the
-        // current and the previous group's scale are live (registers)
-        float s_prev = 0.f, s_cur = 0.f;
-        auto promote_pending = [&](int r) { fma4(acc[r][NOV > 0 ? NOV - 1 : 0], pend[r], part[r]); };
-        if constexpr (NOV == 0) issue_a(rel + SA - 1, 0, DA);
-#pragma unroll
-        for (int o = 0; o < NOV; ++o) {
-          v8i nxt = cur;
-          if (o + 1 < NOV) nxt = load_a(o + 1);
-          s_cur = sSA[16 * o + l16] * sb;
-#pragma unroll
-          for (int r = 0; r < NR; ++r) {
-            part[r] = mfma_block(res[r], cur);
-            if (r + 1 < NR) {
-              if (o > 0)
-                fma4(acc[r + 1][o - 1], s_prev, part[r + 1]);
-              else
-                promote_pending(r + 1);
-            }
-          }
-          constexpr int kSpread = NOV / 2 > 0 ? NOV / 2 : 1;
-          if (o < kSpread) issue_a(rel + SA - 1, (o * DA) / kSpread, ((o + 1) * DA) / kSpread);
-          fma4(acc[0][o], s_cur, part[0]);
-          s_prev = s_cur;
-          cur = nxt;
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        if constexpr (NOV > 0) {
-#pragma unroll
-          for (int r = 0; r < NR; ++r) pend[r] = s_prev;
-        }
-        // B of the block SA-1 ahead goes into the slot just consumed
-        if constexpr (SLOT == 0) load_b(rel + SA - 1, bq0); else load_b(rel + SA - 1, bq1);
-      };
-      // blocks strictly in pairs (nkb is even here): with a conditional second
-      // block the compiler's wait analysis merges the path without its loads
-      // and waits for every load before each MFMA, losing the lookahead
-#pragma unroll 1
-      for (int rel = 0; rel < nkb; rel += 2) {
-        block(rel, std::integral_constant<int, 0>{});
-        block(rel + 1, std::integral_constant<int, 1>{});
-      }
-      if constexpr (NOV > 0) {
-#pragma unroll
-        for (int r = 1; r < NR; ++r) fma4(acc[r][NOV - 1], pend[r], part[r]);
-      }
-    };
-    const int quarters = min(NO / 4, max(0, (rows + 63) / 64));
-    switch (quarters) {
-      case 0: k_loop(std::integral_constant<int, 0>{}); break;
-      case 1: k_loop(std::integral_constant<int, 4>{}); break;
-      case 2: k_loop(std::integral_constant<int, 8>{}); break;
-      case 3: k_loop(std::integral_constant<int, 12>{}); break;
-      default: k_loop(std::integral_constant<int, 16>{}); break;
-    }
-    wait_vm<0>();  // dead DMAs and loads of the last blocks
-    barrier();     // every wave is done with the ring before the next tile refills it
-
-    // ---- epilogue: bf16 (or split-K fp32 partials), masked rows dropped ----
-    const bool part_out = splits > 1;
-    const uint32_t esz = part_out ? 4u : 2u;
-    void* obase = part_out ? (void*)(p.ws + split * p.ws_stride + row0 * p.n)
-                           : (void*)(static_cast<uint16_t*>(p.out) + row0 * p.n);
-    const bool vec = p.vec_out && (int64_t)BM * p.n * 4 < 0x7fffffffLL;
-    const __amdgpu_buffer_rsrc_t ro =
-        __builtin_amdgcn_make_buffer_rsrc(obase, (short)0, (int)((uint32_t)BM * p.n * esz), 0x00020000);
-#pragma unroll
-    for (int j = 0; j < FM; ++j) {
-      const int ml = 16 * j + l16;
-      const bool row_ok = ml < rows;
-#pragma unroll
-      for (int i = 0; i < NF; ++i) {
-        const int n = wcol0 + 16 * i + 4 * lq;
-        if (vec) {
-          const uint32_t off = (row_ok && n < p.n) ? ((uint32_t)ml * p.n + n) * esz : 0x80000000u;
-          if (part_out) {
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, acc[i][j]), ro, off, 0, 0);
-          } else {
-            const uint32_t lo = (uint32_t)f32_to_bf16(acc[i][j][0]) | ((uint32_t)f32_to_bf16(acc[i][j][1]) << 16);
-            const uint32_t hi = (uint32_t)f32_to_bf16(acc[i][j][2]) | ((uint32_t)f32_to_bf16(acc[i][j][3]) << 16);
-            __builtin_amdgcn_raw_buffer_store_b64(v2i{(int)lo, (int)hi}, ro, off, 0, 0);
-          }
-        } else if (row_ok) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            if (n + r >= p.n) continue;
-            if (part_out)
-              (p.ws + split * p.ws_stride + (row0 + ml) * p.n)[n + r] = acc[i][j][r];
-            else
-              (static_cast<uint16_t*>(p.out) + (row0 + ml) * p.n)[n + r] = f32_to_bf16(acc[i][j][r]);
-          }
-        }
-      }
-    }
-  }
-}
-
 // Split-K reduction: C = bf16(sum of the fp32 partials in split order).  One
 // thread per 4 consecutive outputs of a row, one 16-byte load per split; the
 // masked layout skips rows at or past masked_m of their group, which the
@@ -1331,11 +1067,6 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const Params p, int 
 }
 
 }  // namespace
-
-hipError_t launch_masked_bdirect(const Params& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL(masked_bdirect_kernel<3>, dim3(grid), dim3(512), 0, stream, p);
-  return hipGetLastError();
-}
 
 hipError_t launch_splitk_reduce(int kind, const Params& p, hipStream_t stream) {
   if (kind != KIND_DENSE && kind != KIND_MASKED && kind != KIND_DENSE_POW2 && kind != KIND_BF16)

@@ -8,7 +8,6 @@
 namespace dg {
 
 hipError_t launch(int, const TileShape&, const Params&, int, hipStream_t) { return hipErrorInvalidValue; }
-hipError_t launch_masked_bdirect(const Params&, int, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_splitk_reduce(int, const Params&, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_swiglu_quantize(const uint16_t*, uint8_t*, float*, int, int, int, hipStream_t) {
   return hipErrorInvalidValue;

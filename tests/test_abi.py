@@ -229,11 +229,9 @@ def test_heuristic_invariants(lib, kind, m, n, k, g):
     assert _cfg(lib, kind, m, n, k, g) == c  # deterministic
 
 
-def test_masked_plan(lib, monkeypatch):
+def test_masked_plan(lib):
     """Masked decode: the general kernel's tall tiles serve every page shape,
-    long K is split until the CUs are covered, short K is not split, and the
-    register-streaming decode kernel runs only when asked for."""
-    monkeypatch.delenv("DG_MASKED_BDIRECT", raising=False)
+    long K is split until the CUs are covered, short K is not split."""
     for g in (1, 2, 4, 16):
         for n, k in ((4096, 7168), (7168, 2048)):
             c = _cfg(lib, 2, 256, n, k, g)
@@ -243,9 +241,9 @@ def test_masked_plan(lib, monkeypatch):
             elif c["tiles"] < 180:
                 assert c["tiles"] * c["k_splits"] >= 256 and (k // 128) // c["k_splits"] >= 6
     assert _cfg(lib, 2, 256, 4096, 7168, 16)["block_n"] == 256
-    monkeypatch.setenv("DG_MASKED_BDIRECT", "1")
-    c = _cfg(lib, 2, 256, 4096, 7168, 16)
-    assert c["kernel"] == 1 and (c["block_m"], c["block_n"]) == (256, 256)
+    # short K, one group: 32-column tiles fill the CUs without a split
+    c = _cfg(lib, 2, 256, 7168, 2048, 1)
+    assert (c["block_m"], c["block_n"], c["k_splits"]) == (256, 32, 1)
 
 
 def test_split_k_planning(lib):

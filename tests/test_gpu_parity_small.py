@@ -30,18 +30,13 @@ def dg():
 
 @pytest.fixture
 def force_tile(request):
-    """Force a tile shape; "bdirect" forces the masked decode kernel that
-    streams B into registers (its tile is fixed)."""
+    """Force a tile shape (None: the library's own choice)."""
     def _set(tile):
         os.environ.pop("DG_FORCE_TILE", None)
-        os.environ.pop("DG_MASKED_BDIRECT", None)
-        if tile == "bdirect":
-            os.environ["DG_MASKED_BDIRECT"] = "1"
-        elif tile is not None:
+        if tile is not None:
             os.environ["DG_FORCE_TILE"] = tile
     yield _set
     os.environ.pop("DG_FORCE_TILE", None)
-    os.environ.pop("DG_MASKED_BDIRECT", None)
 
 
 def _dense_run(dg, d):
@@ -108,7 +103,7 @@ def test_contiguous_small(dg, force_tile, tile):
     check_close(bits_to_f64(got[valid]), bits_to_f64(ref[valid]), "contiguous small")
 
 
-@pytest.mark.parametrize("tile", [None, "bdirect", "256x256x1x8", "256x224x4x2", "256x128x1x4", "256x128x2x2",
+@pytest.mark.parametrize("tile", [None, "256x32x4x1", "256x256x1x8", "256x224x4x2", "256x128x1x4", "256x128x2x2",
                                   "128x128x2x2", "64x32x2x2"])
 def test_masked_small(dg, force_tile, tile):
     g, m_max, n, k = 5, 96, 260, 256
@@ -166,7 +161,7 @@ def test_page_call_style(dg):
     check_close(bits_to_f64(bf16_bits(out)), bits_to_f64(ref), "page-style dense")
 
 
-@pytest.mark.parametrize("tile", [None, "bdirect", "256x256x1x8", "256x128x1x4", "256x256x2x4"])
+@pytest.mark.parametrize("tile", [None, "256x32x4x1", "256x16x4x1", "256x256x1x8", "256x128x1x4", "256x256x2x4"])
 def test_masked_row_quarters(dg, force_tile, tile):
     """Tall masked tiles skip 64-row quarters past masked_m: every boundary."""
     mm = np.array([0, 1, 63, 64, 65, 127, 128, 129, 191, 192, 193, 255, 256, 300], np.int32)
@@ -211,7 +206,7 @@ def test_dense_split_k(dg, force_tile, force_splits, m, n, k, tile, splits):
     assert np.array_equal(got, _dense_run(dg, d)), "split-K result not deterministic"
 
 
-@pytest.mark.parametrize("tile", ["bdirect", "256x256x1x8", "256x64x1x4", "64x32x2x2"])
+@pytest.mark.parametrize("tile", ["256x32x4x1", "256x256x1x8", "256x64x1x4", "64x32x2x2"])
 @pytest.mark.parametrize("splits", [2, 5])
 def test_masked_split_k(dg, force_tile, force_splits, tile, splits):
     mm = np.array([0, 1, 96, 300, 50, 64, 65], np.int32)  # empty, one row, full, clamped, partial
@@ -290,13 +285,13 @@ def test_contiguous_tall_tiles(dg, force_tile, tile):
     check_close(bits_to_f64(got[ok]), bits_to_f64(ref[ok]), f"contiguous tall {tile}")
 
 
-@pytest.mark.parametrize("tile", ["bdirect", None])
+@pytest.mark.parametrize("tile", ["256x32x4x1", None])
 @pytest.mark.parametrize("splits", [None, 2, 3])
 @pytest.mark.parametrize("k", [512, 2048])
 def test_masked_decode_kernels(dg, force_tile, force_splits, tile, splits, k):
-    """The masked decode kernels at longer K: ragged N (a last column tile
+    """The masked decode tiles at longer K: ragged N (a last column tile
     narrower than the tile), every row-quarter boundary of masked_m, forced K
-    splits (the B-in-registers kernel takes K blocks in pairs)."""
+    splits (an uneven last split)."""
     mm = np.array([0, 1, 63, 64, 65, 128, 191, 192, 255, 256, 300], np.int32)
     g, m_max, n = mm.size, 256, 392
     x = inputs.make_masked(g, m_max, n, k, seed=inputs.SEED_BASE + 61 + k, masked_m=mm)
