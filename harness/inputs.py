@@ -232,3 +232,39 @@ def make_wgrad(m: int, n: int, ks, seed: int) -> Wgrad:
     b, sb = quantize_1x128(_normal(_rng(seed, 1), (n, t)))
     d0 = _normal(_rng(seed, 2), (len(ks), m, n))
     return Wgrad(m, n, ks, a, sa, b, sb, d0)
+
+
+def _small_int_codes(rng: np.random.Generator, shape, top: int) -> np.ndarray:
+    """e4m3 bytes of uniform integers in [-top, top] (exact in e4m3 for top <= 16)."""
+    return _encode_e4m3(rng.integers(-top, top + 1, size=shape).astype(np.float32))
+
+
+def _pow2_scales(rng: np.random.Generator, shape, lo: int, hi: int) -> np.ndarray:
+    """fp32 scales 2^-e with e uniform in [lo, hi]."""
+    return np.ldexp(np.float32(1.0), -rng.integers(lo, hi + 1, size=shape)).astype(np.float32)
+
+
+def make_contiguous_exact(g: int, rows_per_expert: int, n: int, k: int, seed: int,
+                          max_pad: int = 127, rows_expo=(2, 7), cols_expo=(2, 3)) -> Contiguous:
+    """A contiguous problem whose every output is exactly representable in fp32.
+
+    A and B hold small integers (|a| <= 4, |b| <= 4) and every scale is a power
+    of two (sa = 2^-e per row and K block with e in `rows_expo`, sb = 2^-e per
+    128x128 block with e in `cols_expo`), so each output is a multiple of
+    2^-(max e sum) of modest size: any fp32 accumulation order gives it
+    exactly and its bf16 rounding is unique.  With the default exponents and
+    K <= 16384 the outputs are O(1) (|C| < 2^5)."""
+    assert rows_per_expert % BLOCK_K == 0 and k % BLOCK_K == 0
+    m_total = g * rows_per_expert
+    nb, kb = (n + BLOCK_K - 1) // BLOCK_K, k // BLOCK_K
+    a = _small_int_codes(_rng(seed, 0), (m_total, k), 4)
+    sa = _pow2_scales(_rng(seed, 5), (m_total, kb), *rows_expo)
+    b = _small_int_codes(_rng(seed, 1), (g, n, k), 4)
+    sb = _pow2_scales(_rng(seed, 6), (g, nb, kb), *cols_expo)
+    rng = _rng(seed, 3)
+    pads = np.minimum(rng.integers(0, max_pad + 1, size=g), rows_per_expert)
+    ids = np.full(m_total, -1, dtype=np.int32)
+    for e in range(g):
+        v = rows_per_expert - int(pads[e])
+        ids[e * rows_per_expert:e * rows_per_expert + v] = e
+    return Contiguous(g, m_total, n, k, a, sa, b, sb, ids, (rows_per_expert - pads).astype(np.int64))

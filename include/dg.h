@@ -107,6 +107,28 @@ dg_status dg_grouped_fp8_contiguous(const void* a, const float* sa, const void* 
                                     int m_total, int n, int k, int num_groups,
                                     hipStream_t stream);
 
+/* MoE grouped GEMM, contiguous layout, fused with SwiGLU and the FP8
+ * re-quantise of its output (the Russian overview of the DeepGEMM pages,
+ * "Ключевые функции: Mega MoE и индексация": Mega MoE fuses an expert's first
+ * linear layer with the SwiGLU activation; the second FP8 GEMM takes its input
+ * with 1x128 scales).  Same operands and row rules as
+ * dg_grouped_fp8_contiguous, with the first linear layer's stacked projection
+ * as B:
+ *   b [G,N,K] fp8 with N = 2I: rows [0,I) are the gate projection, rows
+ *     [I,2I) the up projection (the column layout of
+ *     dg_swiglu_quantize_fp8_1x128); sb [G,N/128,K_b] fp32
+ *   q [M_total,I] fp8 e4m3, s [M_total,I/128] fp32: for every row with an id
+ *     in [0,G), exactly what dg_grouped_fp8_contiguous into a bf16 C
+ *     [M_total,N] followed by dg_swiglu_quantize_fp8_1x128 on C gives, bit for
+ *     bit (the bf16 rounding of C included); other rows untouched.
+ * The bf16 C is never written to memory.  N % 256 == 0 (I % 128 == 0),
+ * (N/2 + 128) * K < 2^32, q and s 4-byte aligned.  Inputs must keep h finite
+ * in fp32. */
+dg_status dg_grouped_fp8_contiguous_swiglu(const void* a, const float* sa, const void* b,
+                                           const float* sb, void* q, float* s,
+                                           const int32_t* m_indices, int m_total, int n, int k,
+                                           int num_groups, hipStream_t stream);
+
 /* MoE grouped GEMM, masked layout (DeepGEMM pages, "分组 GEMM": inference
  * decode, the graph-captured case -- the valid row counts stay on the device
  * and no host synchronisation happens).
@@ -222,7 +244,8 @@ typedef enum {
   DG_KIND_WGRAD = 3,
   DG_KIND_K_GROUPED_WGRAD = 4,
   DG_KIND_DENSE_POW2 = 5,     /* dg_gemm_fp8_nt_ue8m0 */
-  DG_KIND_BF16 = 6            /* dg_gemm_bf16_nt (k counts bf16 values) */
+  DG_KIND_BF16 = 6,           /* dg_gemm_bf16_nt (k counts bf16 values) */
+  DG_KIND_CONTIGUOUS_SWIGLU = 7 /* dg_grouped_fp8_contiguous_swiglu (n = 2I) */
 } dg_kind;
 
 /* Tile configuration the per-shape heuristic picks (DeepGEMM pages: block

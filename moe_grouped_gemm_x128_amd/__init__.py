@@ -31,6 +31,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 _vp, _i32 = ctypes.c_void_p, ctypes.c_int
 _lib.dg_gemm_fp8_nt.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]
 _lib.dg_grouped_fp8_contiguous.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]
+_lib.dg_grouped_fp8_contiguous_swiglu.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]
 _lib.dg_grouped_fp8_masked.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]
 _lib.dg_grouped_fp8_masked_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]
 _lib.dg_wgrad_fp8_nt.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]
@@ -41,7 +42,7 @@ _lib.dg_quantize_fp8_1x128.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
 _lib.dg_quantize_fp8_128x128.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
 _lib.dg_quantize_fp8_1x128_transposed.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
 _lib.dg_swiglu_quantize_fp8_1x128.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
-for _f in ("dg_gemm_fp8_nt", "dg_grouped_fp8_contiguous", "dg_grouped_fp8_masked", "dg_grouped_fp8_masked_noalloc",
+for _f in ("dg_gemm_fp8_nt", "dg_grouped_fp8_contiguous", "dg_grouped_fp8_contiguous_swiglu", "dg_grouped_fp8_masked", "dg_grouped_fp8_masked_noalloc",
            "dg_wgrad_fp8_nt", "dg_k_grouped_wgrad_fp8_nt", "dg_gemm_fp8_nt_ue8m0", "dg_gemm_bf16_nt", "dg_quantize_fp8_1x128",
            "dg_quantize_fp8_128x128", "dg_quantize_fp8_1x128_transposed", "dg_swiglu_quantize_fp8_1x128"):
     getattr(_lib, _f).restype = ctypes.c_int
@@ -59,7 +60,8 @@ class TileConfig(ctypes.Structure):
 _lib.dg_select_config.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(TileConfig)]
 _lib.dg_select_config.restype = ctypes.c_int
 
-KIND_DENSE, KIND_CONTIGUOUS, KIND_MASKED, KIND_WGRAD, KIND_K_GROUPED_WGRAD, KIND_DENSE_POW2, KIND_BF16 = range(7)
+(KIND_DENSE, KIND_CONTIGUOUS, KIND_MASKED, KIND_WGRAD, KIND_K_GROUPED_WGRAD, KIND_DENSE_POW2, KIND_BF16,
+ KIND_CONTIGUOUS_SWIGLU) = range(8)
 FP8 = torch.float8_e4m3fn
 
 
@@ -189,6 +191,28 @@ def dg_grouped_fp8_contiguous(a, sa, b, sb, c, m_indices):
     return c
 
 
+def dg_grouped_fp8_contiguous_swiglu(a, sa, b, sb, q, s, m_indices):
+    """Contiguous grouped GEMM with B [G,2I,K] (gate rows | up rows), fused
+    with SwiGLU and the 1x128 re-quantise: q fp8 [M_total,I], s fp32
+    [M_total,I/128] (see include/dg.h)."""
+    _fp8(a, "a"); _fp8(b, "b"); _f32(sa, "sa"); _f32(sb, "sb"); _fp8(q, "q"); _f32(s, "s")
+    m_total, k = a.shape
+    g, n, _ = b.shape
+    if n % 256:
+        raise ValueError(f"b must stack gate and up projections of a width that is a multiple of 128 (N={n})")
+    i = n // 2
+    _shape(b, (g, n, k), "b"); _shape(sa, (m_total, k // 128), "sa")
+    _shape(sb, (g, n // 128, k // 128), "sb"); _shape(q, (m_total, i), "q"); _shape(s, (m_total, i // 128), "s")
+    _shape(m_indices, (m_total,), "m_indices")
+    if m_indices.dtype != torch.int32:
+        raise TypeError("m_indices must be int32")
+    _dev(a, sa, b, sb, q, s, m_indices)
+    _check(_lib.dg_grouped_fp8_contiguous_swiglu(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(q), _ptr(s),
+                                                 _ptr(m_indices), m_total, n, k, g, _stream(q)),
+           "dg_grouped_fp8_contiguous_swiglu")
+    return q, s
+
+
 def dg_grouped_fp8_masked(a, sa, b, sb, c, masked_m):
     return _grouped_masked(_lib.dg_grouped_fp8_masked, "dg_grouped_fp8_masked", a, sa, b, sb, c, masked_m)
 
@@ -315,6 +339,18 @@ def gemm_bf16_bf16_bf16_nt(lhs, rhs, out):
 
 def m_grouped_gemm_fp8_fp8_bf16_nt_contiguous(lhs, rhs, out, m_indices):
     return dg_grouped_fp8_contiguous(lhs[0], lhs[1], rhs[0], rhs[1], out, m_indices)
+
+
+def m_grouped_gemm_fp8_fp8_fp8_nt_contiguous_swiglu(lhs, rhs, m_indices):
+    """First expert linear layer + SwiGLU + 1x128 re-quantise: returns the
+    second layer's operand (fp8 [M_total,I], fp32 scales [M_total,I/128]);
+    rows of padding (-1) are left as torch.empty gives them."""
+    m_total = lhs[0].shape[0]
+    i = rhs[0].shape[1] // 2
+    dev = lhs[0].device
+    return dg_grouped_fp8_contiguous_swiglu(
+        lhs[0], lhs[1], rhs[0], rhs[1], torch.empty((m_total, i), dtype=FP8, device=dev),
+        torch.empty((m_total, i // 128), dtype=torch.float32, device=dev), m_indices)
 
 
 def m_grouped_gemm_fp8_fp8_bf16_nt_masked(lhs, rhs, out, masked_m):

@@ -117,6 +117,8 @@ struct Candidate {
 //     per CU) x (tile area / tile efficiency), so a large tile wins unless
 //     it leaves CUs idle.
 dg::TileShape heuristic(int kind, int rows, int n, int k, int groups, int num_cus, bool allow_split) {
+  // the fused SwiGLU epilogue has one tile: 128 gate + 128 up columns, 1x8 waves
+  if (kind == DG_KIND_CONTIGUOUS_SWIGLU) return dg::TileShape{256, 256, 1, 8};
   const int kbs = k / 128;
   const bool long_k = allow_split && kbs >= 3 * kSplitMinBlocks;
   if (kind == DG_KIND_MASKED && rows <= 256) {
@@ -501,6 +503,33 @@ dg_status dg_grouped_fp8_contiguous(const void* a, const float* sa, const void* 
   return run(dg::KIND_CONTIGUOUS, p, m_total, n, k, 1, stream);
 }
 
+dg_status dg_grouped_fp8_contiguous_swiglu(const void* a, const float* sa, const void* b, const float* sb,
+                                           void* q, float* s, const int32_t* m_indices, int m_total, int n, int k,
+                                           int num_groups, hipStream_t stream) {
+  if (!a || !sa || !b || !sb || !q || !s || !m_indices) return DG_ERROR_INVALID_VALUE;
+  if (m_total <= 0 || n <= 0 || k <= 0 || num_groups <= 0) return DG_ERROR_INVALID_VALUE;
+  if (k % 128 != 0 || m_total % 128 != 0 || n % 256 != 0) return DG_ERROR_UNSUPPORTED;
+  // one B range spans the tile's gate and up rows: (N/2 + 128) * K bytes
+  if ((int64_t)(n / 2 + 128) * k > (int64_t)0xffffffffLL) return DG_ERROR_UNSUPPORTED;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(sa, 4) || !aligned(sb, 4) || !aligned(q, 4) ||
+      !aligned(s, 4) || !aligned(m_indices, 4))
+    return DG_ERROR_UNSUPPORTED;
+  dg::Params p = base_params();
+  p.a = static_cast<const uint8_t*>(a);
+  p.sa = sa;
+  p.b = static_cast<const uint8_t*>(b);
+  p.sb = sb;
+  p.out = q;
+  p.out_scale = s;
+  p.ctrl = m_indices;
+  p.m = m_total;
+  p.n = n;
+  p.lda = k;
+  p.kbs = k / 128;
+  p.groups = num_groups;
+  return run(dg::KIND_CONTIG_SWIGLU, p, m_total, n, k, 1, stream);
+}
+
 dg_status dg_grouped_fp8_masked(const void* a, const float* sa, const void* b, const float* sb,
                                 void* c, const int32_t* masked_m, int num_groups, int m_max, int n,
                                 int k, hipStream_t stream) {
@@ -580,7 +609,8 @@ const char* dg_status_string(dg_status s) {
 dg_status dg_select_config(int kind, int m, int n, int k, int num_groups, int num_cus,
                            dg_tile_config* out) {
   if (!out) return DG_ERROR_INVALID_VALUE;
-  if (kind < DG_KIND_DENSE || kind > DG_KIND_BF16) return DG_ERROR_INVALID_VALUE;
+  if (kind < DG_KIND_DENSE || kind > DG_KIND_CONTIGUOUS_SWIGLU) return DG_ERROR_INVALID_VALUE;
+  if (kind == DG_KIND_CONTIGUOUS_SWIGLU && (n % 256 != 0 || m % 128 != 0)) return DG_ERROR_UNSUPPORTED;
   if (m <= 0 || n <= 0 || k <= 0 || num_groups <= 0 || num_cus <= 0) return DG_ERROR_INVALID_VALUE;
   if (kind == DG_KIND_BF16 && k > (1 << 22)) return DG_ERROR_UNSUPPORTED;
   dg::Params p = base_params();

@@ -19,6 +19,9 @@ enum Kind : int {
   KIND_DENSE_POW2 = 5,  // C bf16 [M,N]; power-of-two scales applied by the block-scaled MFMA
   KIND_BF16 = 6,        // C bf16 [M,N] = A bf16 [M,K] . B bf16 [N,K]^T; no scales; a "K block" is
                         // 128 bytes = 64 values (lda = 2K bytes, kbs = K/64)
+  KIND_CONTIG_SWIGLU = 7,  // contiguous layout with B [G,2I,K] (gate rows, then up rows); the
+                           // epilogue applies SwiGLU to the bf16-rounded pair and writes
+                           // fp8 q [M_tot,I] with 1x128 scales [M_tot,I/128] (out, out_scale)
 };
 
 constexpr int kMaxKGroups = 256;
@@ -28,7 +31,8 @@ struct Params {
   const float* sa;       // LHS scales, row stride kbs floats
   const uint8_t* b;      // fp8 RHS, [G][N][lda]
   const float* sb;       // RHS scales: [G][NB][kbs] (block) or [N][kbs] (row)
-  void* out;             // bf16 C or fp32 D
+  void* out;             // bf16 C or fp32 D (fused SwiGLU: fp8 codes)
+  float* out_scale;      // fused SwiGLU: the codes' 1x128 scales
   const int32_t* ctrl;   // m_indices (contiguous) or masked_m (masked)
   int m;                 // rows per group: M, M_total or M_max
   int n;                 // N

@@ -30,6 +30,7 @@
 // A rows or B columns meet in the same L2.
 #include <type_traits>
 
+#include "dg_fp8_codec.h"
 #include "dg_kernel.h"
 #include "dg_rsrc.h"
 #include "dg_shapes.h"
@@ -209,6 +210,13 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   constexpr bool kRowScaleB = (KIND == KIND_WGRAD || KIND == KIND_KGROUPED);
   constexpr bool kPow2 = (KIND == KIND_DENSE_POW2);  // scales applied by the MFMA
   constexpr bool kBf16 = (KIND == KIND_BF16);         // no scales at all
+  // contiguous layout with the SwiGLU + re-quantise epilogue: the tile's B
+  // rows are 128 gate rows and the 128 matching up rows, in LDS order
+  // [wave][gate 16 | up 16], so fragment 0 of a wave holds the gate and
+  // fragment 1 the up value of the same output element in the same lane
+  constexpr bool kSwiGLU = (KIND == KIND_CONTIG_SWIGLU);
+  constexpr bool kContig = (KIND == KIND_CONTIGUOUS) || kSwiGLU;
+  static_assert(!kSwiGLU || (BM == 256 && BN == 256 && WM == 1 && WN == 8), "fused SwiGLU tile");
   // B loaded with the streaming (nontemporal) cache policy by the instances
   // whose launches read each B tile with one row of tiles: the dense tiles of
   // at most 128 rows (the heuristic's choice for M <= 128) and the masked
@@ -222,7 +230,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   constexpr bool kDirectAcc = kPow2 || kBf16;         // MFMAs accumulate into acc: no promotion
   constexpr bool kFp32Out = kRowScaleB;
   // the columns of one wave tile sit inside one 128-block: one sb per wave
-  constexpr bool kWaveUniformSb = !kRowScaleB && (kBK % WTN == 0) && (BN % WTN == 0);
+  constexpr bool kWaveUniformSb = !kRowScaleB && !kSwiGLU && (kBK % WTN == 0) && (BN % WTN == 0);
   constexpr bool kStreamM = FM >= FN;  // keep the smaller fragment set resident
   // Masked layout with tall tiles: a wave whose rows run past the group's
   // valid rows skips those row fragments (no LDS read, no MFMA; their zero
@@ -258,9 +266,11 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   // bf16 epilogue staging: a wave's 16-row fragment row goes through LDS so
   // that each store covers whole (64 columns) or half (32 columns) 128-byte
   // lines; rows padded by 16 bytes against bank conflicts
-  constexpr bool kStage = !kFp32Out && (WTN == 64 || WTN == 32);
+  constexpr bool kStage = !kFp32Out && !kSwiGLU && (WTN == 64 || WTN == 32);
   constexpr int kStageRow = WTN * 2 + 16;
   __shared__ __attribute__((aligned(16))) uint8_t sOut[kStage ? NW : 1][kStage ? 16 * kStageRow : 16];
+  // fused SwiGLU: each wave's |h| maximum over its 16 columns, per tile row
+  __shared__ __attribute__((aligned(16))) float sRowMax[kSwiGLU ? BM : 1][kSwiGLU ? NW : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -296,7 +306,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   // block of padding rows).
   // contiguous: bit i of rmask[i / 64] says whether row wm * WTM + i of the
   // tile carries the tile's expert (this wave's rows only)
-  constexpr int RMW = KIND == KIND_CONTIGUOUS ? (WTM + 63) / 64 : 1;
+  constexpr int RMW = kContig ? (WTM + 63) / 64 : 1;
   struct Tile {
     int live, g, m0, n0, rows, kb0, nkb, split;
     int64_t a_row0, out_row0;
@@ -344,7 +354,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
       int tm, tn;
       raster(L, p.tiles_m, p.tiles_n, tm, tn);
       x.m0 = tm * BM;
-      x.n0 = tn * BN;
+      x.n0 = tn * (kSwiGLU ? BN / 2 : BN);  // fused SwiGLU: the first output (gate) column
       x.rows = min(BM, p.m - x.m0);
       x.a_row0 = x.m0;
       x.out_row0 = x.m0;
@@ -405,7 +415,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   // the first live item at or after `t` (or a queued second pass); `t`
   // moves past it
   auto next_live = [&](int& t) -> Tile {
-    if constexpr (KIND == KIND_CONTIGUOUS) {
+    if constexpr (kContig) {
       if (pend_t >= 0) {
         Tile x = decode(pend_t);
         x.g = pend_g;
@@ -417,7 +427,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     Tile x = decode(t_end);
     while (t < t_end) {
       x = decode(t);
-      if constexpr (KIND == KIND_CONTIGUOUS)
+      if constexpr (kContig)
         if (x.live) find_expert(x, t);
       t += gridDim.x;
       if (x.live) break;
@@ -449,15 +459,19 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     const uint32_t son = kBf16 ? 0u : on;  // BF16: the scale pieces read nothing
     Res r;
     r.a = buffer_rsrc(p.a + x.a_row0 * (int64_t)p.lda, on * (uint32_t)x.rows * p.lda);
-    r.b = buffer_rsrc(p.b + ((int64_t)bg * p.n + x.n0) * (int64_t)p.lda, on * (uint32_t)bcols * p.lda);
+    // fused SwiGLU: gate rows n0.. and up rows I + n0.. (I = N/2), one range
+    const uint32_t brows = kSwiGLU ? (uint32_t)(p.n / 2 + BN / 2) : (uint32_t)bcols;
+    r.b = buffer_rsrc(p.b + ((int64_t)bg * p.n + x.n0) * (int64_t)p.lda, on * brows * p.lda);
     const Rsrc sa = buffer_rsrc(p.sa + x.a_row0 * (int64_t)p.kbs, son * (uint32_t)x.rows * p.kbs * 4);
     Rsrc sb;
     if constexpr (kRowScaleB) {
       sb = buffer_rsrc(p.sb + (int64_t)x.n0 * p.kbs, on * (uint32_t)bcols * p.kbs * 4);
     } else {
       // only the 128-column blocks the tile touches
+      // (fused SwiGLU: the gate block n0/128 through the up block (I + n0)/128)
       const int nb0 = x.n0 / kBK;
-      const int nbt = min(nb_rows - nb0, (x.n0 - nb0 * kBK + BN + kBK - 1) / kBK);  // a tile may straddle blocks
+      const int nbt = kSwiGLU ? p.n / 2 / kBK + 1
+                              : min(nb_rows - nb0, (x.n0 - nb0 * kBK + BN + kBK - 1) / kBK);  // a tile may straddle blocks
       sb = buffer_rsrc(p.sb + ((int64_t)x.g * nb_rows + nb0) * p.kbs, son * (uint32_t)max(nbt, 0) * p.kbs * 4);
     }
     const uint32_t prow = 64u * p.kbs * 4;  // bytes of 64 scale rows
@@ -517,8 +531,19 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     const int r0 = wave * 8 + (lane >> 3);
     const uint32_t voff0 = (uint32_t)r0 * p.lda + (((lane & 7) ^ swz(r0)) << 4);
     const uint32_t step = (uint32_t)(NW * 8) * p.lda;  // bytes between a wave's pieces
+    // fused SwiGLU: LDS row j of B is gate row n0 + 16 (j / 32) + j % 16 when
+    // (j / 16) is even, else the up row I + n0 + ...; a wave's pieces are 64
+    // LDS rows = 32 source rows apart
+    const uint32_t voffb0 =
+        kSwiGLU ? (uint32_t)(((r0 >> 4) & 1) * (p.n / 2) + 16 * (r0 >> 5) + (r0 & 15)) * p.lda +
+                      (((lane & 7) ^ swz(r0)) << 4)
+                : voff0;
+    const uint32_t stepb = kSwiGLU ? (uint32_t)(NW * 4) * p.lda : step;
     // scale pieces: 64 rows (or columns / 128-blocks) each, one float per lane
     const uint32_t svoff = (uint32_t)lane * p.kbs * 4;
+    // fused SwiGLU: the B scale piece's lane 1 reads the up block I/128 blocks
+    // on, so the stage holds sb(gate) at 0 and sb(up) at 1
+    const uint32_t svoff_b = kSwiGLU && lane == 1 ? (uint32_t)(p.n / 2 / kBK) * p.kbs * 4 : svoff;
 
     // The DMAs of one K block: each source moved to the block (empty past
     // the tile's K range or for a dead tile: such a block reads zeros and
@@ -563,9 +588,9 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
         const int pi = wave + NW * q;
         if constexpr (PB % NW == 0) {
           if constexpr (kStreamB)
-            dma16_nt(d.base + OFF_B + pi * 1024, d.b, voff0 + q * step);
+            dma16_nt(d.base + OFF_B + pi * 1024, d.b, voffb0 + q * stepb);
           else
-            dma16(d.base + OFF_B + pi * 1024, d.b, voff0 + q * step);
+            dma16(d.base + OFF_B + pi * 1024, d.b, voffb0 + q * stepb);
         } else {
           // past the last B piece: read nothing into the sink
           const bool real = pi < PB;
@@ -578,7 +603,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
       for (int q = 0; q < QS; ++q) {
         if (QA + QB + q < lo || QA + QB + q >= hi) continue;
         const int sp = wave + NW * q;
-        dma4(sp < PS ? d.base + OFF_SA + sp * 256 : smem_lds + S * STAGE, d.s[q], svoff);
+        dma4(sp < PS ? d.base + OFF_SA + sp * 256 : smem_lds + S * STAGE, d.s[q], sp < PSA ? svoff : svoff_b);
       }
     };
     const int qs = qbase % S;
@@ -726,6 +751,9 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
           const float sb = sSB[(n0 + wn * WTN) / kBK - n0 / kBK];
   #pragma unroll
           for (int i = 0; i < FN; ++i) sbv[i] = sb;
+        } else if constexpr (kSwiGLU) {
+          sbv[0] = sSB[0];  // gate block
+          sbv[1] = sSB[1];  // up block
         } else {
   #pragma unroll
           for (int i = 0; i < FN; ++i) sbv[i] = sSB[(n0 + wn * WTN + 16 * i) / kBK - n0 / kBK];
@@ -849,7 +877,46 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     auto rbit = [&](int j, int r) -> bool {
       return ((cur.rmask[((16 * j) / 64) % RMW] >> (uint32_t)(16 * (j % 4) + r)) & 1u) != 0;
     };
-    if (kStage && staged) {
+    if constexpr (kSwiGLU) {
+      // h = silu(gate) * up on the bf16-rounded GEMM outputs (what the unfused
+      // path stores and its SwiGLU kernel reads), then the 1x128 rule over the
+      // tile's 128 output columns [n0, n0 + 128) of each row: the waves' |h|
+      // maxima over their 16 columns meet in LDS.  Lane (l16, lq) of fragment
+      // row j holds columns 16 wn + 4 lq .. + 3 of row 16 j + l16.
+      const int half = p.n / 2;
+      auto bf16r = [](float x) { return __uint_as_float((uint32_t)f32_to_bf16(x) << 16); };
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        float m = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float h = codec::silu(bf16r(acc[0][j][e])) * bf16r(acc[1][j][e]);
+          acc[0][j][e] = h;
+          m = fmaxf(m, fabsf(h));
+        }
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        if (lq == 0) sRowMax[16 * j + l16][wave] = m;
+      }
+      barrier();  // every wave's maxima are in LDS
+      uint8_t* qo = static_cast<uint8_t*>(p.out);
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        const int r = 16 * j + l16;
+        const float4 a = *reinterpret_cast<const float4*>(&sRowMax[r][0]);
+        const float4 b = *reinterpret_cast<const float4*>(&sRowMax[r][4]);
+        const float amax = fmaxf(fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w)), fmaxf(fmaxf(b.x, b.y), fmaxf(b.z, b.w)));
+        const float sc = codec::scale_of(amax);
+        const codec::GroupRecip gr = codec::group_recip(sc);
+        const uint32_t w = codec::encode4(codec::scaled(acc[0][j][0], gr), codec::scaled(acc[0][j][1], gr),
+                                          codec::scaled(acc[0][j][2], gr), codec::scaled(acc[0][j][3], gr));
+        if (rbit(j, l16)) {
+          const int64_t orow = out_row0 + r;
+          *reinterpret_cast<uint32_t*>(qo + orow * half + n0 + 16 * wn + 4 * lq) = w;
+          if (wn == 0 && lq == 0) p.out_scale[orow * (half / kBK) + n0 / kBK] = sc;
+        }
+      }
+    } else if (kStage && staged) {
       // fragment row j: lanes write their 4 bf16 per column fragment into the
       // wave's LDS rows, then read 16 contiguous bytes each along the rows
       constexpr int kLanesPerRow = WTN * 2 / 16;    // 8 (64 columns) or 4 (32)
@@ -874,7 +941,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
           const uint4 v = *reinterpret_cast<const uint4*>(so + r * kStageRow + cb);
           const int ml = wm * WTM + 16 * j + r;
           bool row_ok;
-          if constexpr (KIND == KIND_CONTIGUOUS)
+          if constexpr (kContig)
             row_ok = rbit(j, r);
           else
             row_ok = ml < rows;
@@ -903,7 +970,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
       for (int j = 0; j < FM; ++j) {
         const int ml = wm * WTM + 16 * j + l16;
         bool row_ok;
-        if constexpr (KIND == KIND_CONTIGUOUS)
+        if constexpr (kContig)
           row_ok = rbit(j, l16);
         else
           row_ok = ml < rows;
@@ -927,7 +994,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     for (int j = 0; j < FM; ++j) {
       const int ml = wm * WTM + 16 * j + l16;
       bool row_ok;
-      if constexpr (KIND == KIND_CONTIGUOUS)
+      if constexpr (kContig)
         row_ok = rbit(j, l16);
       else
         row_ok = ml < rows;
@@ -979,7 +1046,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
       }
     }
     }
-    stores_pending = xfer && exact_stores;
+    stores_pending = xfer && exact_stores && !kSwiGLU;
 
     // ---- next tile ----
     if (!xfer) nxt = next_live(t_next);
@@ -1021,6 +1088,9 @@ hipError_t launch_shape(int kind, const Params& p, int grid, hipStream_t stream)
       break;
     case KIND_BF16:
       launch_kind<BM, BN, WM, WN, S, KIND_BF16>(g, b, stream, p);
+      break;
+    case KIND_CONTIG_SWIGLU:
+      launch_kind<BM, BN, WM, WN, S, KIND_CONTIG_SWIGLU>(g, b, stream, p);
       break;
     default:
       return hipErrorInvalidValue;

@@ -29,6 +29,7 @@
 // The quotient x / s is computed without a full division per element (see
 // quotient()): one division per group for RN(1/s), then multiplies and FMAs
 // that reproduce the IEEE quotient bit for bit.
+#include "dg_fp8_codec.h"
 #include "dg_kernel.h"
 
 namespace dg {
@@ -37,11 +38,13 @@ namespace {
 constexpr int kQ = 128;          // group / tile edge
 constexpr int kQThreads = 512;   // 8 waves
 constexpr int kQStrips = 8;      // float4 loads per thread: 128 rows x 32 float4 / 512
-constexpr float kE4m3Max = 448.0f;
+using codec::kE4m3Max;
+using codec::scale_of;
+using codec::encode4;
+using codec::silu;
 
 enum QuantMode : int { Q_ROWS = 0, Q_BLOCKS = 1, Q_TRANSPOSED = 2 };
 
-__device__ __forceinline__ float scale_of(float amax) { return amax == 0.0f ? 1.0f : amax / kE4m3Max; }
 
 // x / s, equal to the IEEE fp32 quotient: y0 = x * RN(1/s), then two
 // residual corrections y += RN(1/s) * (x - y*s) with the residual exact in an
@@ -59,14 +62,6 @@ __device__ __forceinline__ float quotient(float x, float s) {
   e = __builtin_fmaf(-y, s, x);
   y = __builtin_copysignf(__builtin_fmaf(e, r, y), x);
   return fminf(fmaxf(y, -kE4m3Max), kE4m3Max);
-}
-
-// Four values (already within +-448) -> four e4m3fn codes, round to nearest
-// even (v_cvt_pk_fp8_f32; gfx950's FP8 conversion uses the OCP E4M3FN encoding).
-__device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
-  return (uint32_t)w;
 }
 
 __device__ __forceinline__ float max_xor(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
@@ -247,21 +242,6 @@ __global__ __launch_bounds__(kQThreads) void quant_rows_kernel(const float* __re
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// silu(g) = g / (1 + e^-g) for a bf16 gate g.  e^-g = 2^(-g log2 e) with
-// log2 e split into a 15-bit head, whose product with g (8 significant bits)
-// is exact in fp32, and a tail t = log2 e - head applied as the factor
-// 2^(-g t) ~= 1 - g t ln 2 (|g t ln 2| < 4.4e-4 wherever e is finite, so the
-// dropped second-order term is under 2 ulp).  The exp unit then sees an exact
-// argument, and h stays within a few fp32 ulp of exact for every gate instead
-// of losing |g| * 2^-24 to the rounding of g * log2 e.  Large negative g gives
-// e = inf and silu = -0; large positive g gives e = 0 and silu = g.
-__device__ __forceinline__ float silu(float g) {
-  constexpr float kLog2eHead = 1.44268798828125f;     // 15 significant bits
-  constexpr float kTailLn2 = -4.888495368504664e-06f;  // -(log2 e - head) * ln 2
-  const float e = __builtin_amdgcn_exp2f(g * -kLog2eHead) * __builtin_fmaf(g, kTailLn2, 1.0f);
-  return g * __builtin_amdgcn_rcpf(1.0f + e);
-}
-
 __global__ __launch_bounds__(kQThreads) void swiglu_quant_kernel(const uint16_t* __restrict__ c,
                                                                  uint8_t* __restrict__ q, float* __restrict__ s,
                                                                  int64_t groups, int64_t groups_per_row) {
@@ -301,13 +281,10 @@ __global__ __launch_bounds__(kQThreads) void swiglu_quant_kernel(const uint16_t*
       m = max_xor(m, 2);
       m = max_xor(m, 1);
       const float sc = scale_of(m);
-      // a scale below 2^-60 is raised by 2^64 (h alike, exactly) so that
-      // 1/s stays finite
-      const float k = sc < 0x1p-60f ? 0x1p64f : 1.0f;
-      const float r = 1.0f / (sc * k);
+      const codec::GroupRecip gr = codec::group_recip(sc);
       float y[8];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) y[t] = fminf(fmaxf(h[t] * k * r, -kE4m3Max), kE4m3Max);
+      for (int t = 0; t < 8; ++t) y[t] = codec::scaled(h[t], gr);
       const int64_t g = ch * 16 + 4 * j + (lane >> 4);
       if (g < groups) {
         if (sub == 0) s[g] = sc;

@@ -102,6 +102,32 @@ def test_grouped_argument_errors(lib):
     assert m(A16, A16, A16, A16, A16, A16, 2, 256, 8, 200, None) == UNSUPPORTED
 
 
+def test_fused_swiglu_argument_errors(lib):
+    f = lib.dg_grouped_fp8_contiguous_swiglu
+    f.argtypes = [ctypes.c_void_p] * 7 + [ctypes.c_int] * 4 + [ctypes.c_void_p]
+    ok = (A16, A16, A16, A16, A16, A16, A16)
+    for i in range(7):
+        args = list(ok)
+        args[i] = None
+        assert f(*args, 256, 512, 128, 2, None) == INVALID, i
+    assert f(*ok, 0, 512, 128, 2, None) == INVALID
+    assert f(*ok, 256, 512, 128, 0, None) == INVALID
+    assert f(*ok, 256, 384, 128, 2, None) == UNSUPPORTED      # N % 256: I not a multiple of 128
+    assert f(*ok, 200, 512, 128, 2, None) == UNSUPPORTED      # M_total % 128
+    assert f(*ok, 256, 512, 200, 2, None) == UNSUPPORTED      # K % 128
+    assert f(*ok, 256, 1 << 20, 1 << 13, 2, None) == UNSUPPORTED  # one B range past 32 bits
+    assert f(MIS, A16, A16, A16, A16, A16, A16, 256, 512, 128, 2, None) == UNSUPPORTED
+    assert f(A16, A16, A16, A16, A16 + 2, A16, A16, 256, 512, 128, 2, None) == UNSUPPORTED  # q alignment
+    assert f(A16, A16, A16, A16, A16, A16 + 2, A16, 256, 512, 128, 2, None) == UNSUPPORTED  # s alignment
+
+
+def test_fused_swiglu_plan(lib):
+    """One tile: 256 rows x (128 gate + 128 up columns) on 1x8 waves, never split."""
+    c = _cfg(lib, 7, 65536, 4096, 7168)
+    assert (c["block_m"], c["block_n"], c["waves_m"], c["waves_n"]) == (256, 256, 1, 8)
+    assert c["tiles"] == (65536 // 256) * (4096 // 256) and c["k_splits"] == 1
+
+
 def test_bf16_argument_errors(lib):
     f = lib.dg_gemm_bf16_nt
     f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 3 + [ctypes.c_void_p]
@@ -263,7 +289,11 @@ def test_heuristic_rejects_bad_queries(lib):
     out = c()
     lib.dg_select_config.argtypes = [ctypes.c_int] * 6 + [ctypes.c_void_p]
     assert lib.dg_select_config(9, 1, 1, 128, 1, 256, ctypes.addressof(out)) == INVALID
-    assert lib.dg_select_config(7, 1, 1, 128, 1, 256, ctypes.addressof(out)) == INVALID
+    assert lib.dg_select_config(8, 1, 1, 128, 1, 256, ctypes.addressof(out)) == INVALID
+    assert lib.dg_select_config(-1, 1, 1, 128, 1, 256, ctypes.addressof(out)) == INVALID
+    # the fused SwiGLU kind needs N % 256 == 0 and M % 128 == 0
+    assert lib.dg_select_config(7, 128, 384, 128, 1, 256, ctypes.addressof(out)) == UNSUPPORTED
+    assert lib.dg_select_config(7, 100, 512, 128, 1, 256, ctypes.addressof(out)) == UNSUPPORTED
     assert lib.dg_select_config(0, 0, 1, 128, 1, 256, ctypes.addressof(out)) == INVALID
     assert lib.dg_select_config(0, 1, 1, 128, 1, 256, None) == INVALID
 
