@@ -22,13 +22,16 @@ inside the timed steps, and whose roofline fraction is reported from those
 512 MB cache flush (`roofline.cold_median_us`).  The CPU oracle is timed on a
 bounded sample of the same workload's outputs (`cpu_baseline`).  The masked
 decode GEMMs are also captured into HIP graphs -- the default entry point and
-the allocation-free one -- and their replays timed (`masked_graph`).
+the allocation-free one -- and their replays timed (`masked_graph`); the
+contiguous G=8, N=4096, K=7168 GEMM is timed against its form with SwiGLU and
+the FP8 re-quantise fused into the epilogue (`fused_swiglu`).
 
 Other workloads (dense, contiguous, masked, wgrad, k_grouped_wgrad, small,
 dense_ue8m0 -- the dense sweep with power-of-two scales --, bf16 -- the
 sweep's shapes in BF16 against the bf16 peak --, quantize, the FP8 quantiser
 in GB/s, and swiglu_quantize, the SwiGLU + FP8 re-quantise step between an
-expert's two GEMMs in GB/s) print a line of the same form.  Exactly one JSON
+expert's two GEMMs in GB/s, and contiguous_swiglu, the contiguous sweep with
+SwiGLU + re-quantise fused into the GEMM) print a line of the same form.  Exactly one JSON
 line goes to stdout.
 
 Before the W warmup steps the step runs untimed for at least half a second so
@@ -217,12 +220,99 @@ def build_contiguous():
             oracle.grouped_contiguous_at(a, sa, b, sb, ids, r, cl)
             return 2.0 * k * count
 
-        calls.append(Call(s["name"], 2.0 * mv * n * k, nbytes, fn, sample, group="contiguous"))
+        call = Call(s["name"], 2.0 * mv * n * k, nbytes, fn, sample, group="contiguous")
+        call.operands = (da_g, dsa_g, db_g, dsb_g, ids_g, out)
+        calls.append(call)
     order = [s["name"] for s in workloads.contiguous_sweep()]
     calls.sort(key=lambda c: order.index(c.name))
     return calls, {"workload": "contiguous_sweep", "description":
                    "MoE contiguous: G in {4,8}, 8192 rows per expert minus U{0..127} padding rows, "
                    "(N,K) in {(4096,7168),(7168,2048)}"}
+
+
+def build_contiguous_swiglu():
+    """The contiguous sweep's problems as an expert's first linear layer with
+    SwiGLU and the 1x128 FP8 re-quantise fused into the GEMM epilogue
+    (dg_grouped_fp8_contiguous_swiglu): B [G, N, K] holds the gate rows
+    [0, N/2) and the up rows [N/2, N); out fp8 [M_total, N/2] + fp32 scales.
+    Algorithmic FLOPs as the GEMM's; bytes = operands + codes + scales."""
+    import torch
+    import moe_grouped_gemm_x128_amd as dg
+
+    base, _ = build_contiguous()
+    calls = []
+    for c in base:
+        da, dsa, db, dsb, ids, _ = c.operands
+        mt, k = da.shape
+        g, n, _ = db.shape
+        i = n // 2
+        q = torch.empty((mt, i), dtype=torch.uint8, device="cuda")
+        sc = torch.empty((mt, i // 128), dtype=torch.float32, device="cuda")
+        fn = (lambda da=da, dsa=dsa, db=db, dsb=dsb, q=q, sc=sc, ids=ids:
+              dg.dg_grouped_fp8_contiguous_swiglu(da, dsa, db, dsb, q, sc, ids))
+        ids_h = ids.cpu().numpy()
+        valid_rows = np.flatnonzero(ids_h >= 0)
+        mv = valid_rows.size
+        nbytes = c.bytes - mv * n * 2 + mv * i + mv * (i // 128) * 4
+        a_h, sa_h = da.cpu().numpy(), dsa.cpu().numpy()
+        b_h, sb_h = db.cpu().numpy(), dsb.cpu().numpy()
+
+        def sample(rng, count, a=a_h, sa=sa_h, b=b_h, sb=sb_h, ids=ids_h, rows=valid_rows, i=i, k=k):
+            """The oracle's composition on whole 1x128 output groups: the
+            gate and up GEMM outputs of each, rounded to bf16, then its SwiGLU
+            + quantiser; returns the GEMM FLOPs that took."""
+            import oracle
+            groups = max(1, count // 256)
+            r = rows[rng.integers(0, rows.size, groups)]
+            gi = rng.integers(0, i // 128, groups)
+            cols = (gi[:, None] * 128 + np.arange(128)[None, :])
+            cols = np.concatenate([cols, cols + i], axis=1)           # gate | up
+            x, _ = oracle.grouped_contiguous_at(a, sa, b, sb, ids, np.repeat(r, 256), cols.ravel())
+            oracle.swiglu_quantize_1x128(oracle.round_bf16(x).reshape(groups, 256))
+            return 2.0 * k * 256 * groups
+
+        name = c.name.replace("contig_", "contig_swiglu_")
+        calls.append(Call(name, c.flops, nbytes, fn, sample, group="contiguous_swiglu"))
+    return calls, {"workload": "contiguous_swiglu_sweep", "description":
+                   "MoE contiguous first linear layer with SwiGLU + FP8 1x128 re-quantise fused: G in {4,8}, "
+                   "8192 rows per expert minus U{0..127} padding rows, (N=2I,K) in {(4096,7168),(7168,2048)}",
+                   "out": "e4m3 [M_total, N/2] + fp32 1x128 scales"}
+
+
+def fused_swiglu_compare(calls, per_ms, reps=20):
+    """The contiguous G=8, N=4096, K=7168 GEMM of the step against its fused
+    form: the unfused path is the GEMM (its per-call time from the step's
+    table) plus the stand-alone SwiGLU quantiser on its bf16 output; the fused
+    path is one call.  Medians of `reps` event-bracketed launches."""
+    import torch
+    import moe_grouped_gemm_x128_amd as dg
+    idx = [j for j, c in enumerate(calls) if c.name == "contig_g8_n4096_k7168" and hasattr(c, "operands")]
+    if not idx:
+        return None
+    c = calls[idx[0]]
+    da, dsa, db, dsb, ids, out = c.operands
+    mt, i = da.shape[0], db.shape[1] // 2
+    q = torch.empty((mt, i), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((mt, i // 128), dtype=torch.float32, device="cuda")
+
+    def med(fn):
+        fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+    swiglu = med(lambda: dg.dg_swiglu_quantize_fp8_1x128(out, q, sc))
+    fused = med(lambda: dg.dg_grouped_fp8_contiguous_swiglu(da, dsa, db, dsb, q, sc, ids))
+    gemm = float(per_ms[idx[0]])
+    return {"problem": "contig_g8_n4096_k7168 as gate|up, I=2048", "gemm_us": round(gemm * 1e3, 1),
+            "swiglu_quantize_us": round(swiglu * 1e3, 1), "unfused_us": round((gemm + swiglu) * 1e3, 1),
+            "fused_us": round(fused * 1e3, 1), "fused_tflops": round(c.flops / (fused * 1e-3) / 1e12, 1),
+            "speedup": round((gemm + swiglu) / fused, 3)}
 
 
 def build_masked():
@@ -651,7 +741,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="all",
                     choices=["all", "dense", "small", "contiguous", "masked", "wgrad", "k_grouped_wgrad", "quantize",
-                             "dense_ue8m0", "bf16", "swiglu_quantize"])
+                             "dense_ue8m0", "bf16", "swiglu_quantize", "contiguous_swiglu"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold-median", action="store_true", help="skip the cold-cache median of the dominant GEMM")
@@ -675,7 +765,7 @@ def main():
                 "contiguous": build_contiguous, "masked": build_masked,
                 "wgrad": build_wgrad, "k_grouped_wgrad": lambda: build_wgrad(kgrouped=True),
                 "quantize": build_quantize, "dense_ue8m0": lambda: build_dense(pow2=True), "bf16": build_bf16,
-                "swiglu_quantize": build_swiglu}
+                "swiglu_quantize": build_swiglu, "contiguous_swiglu": build_contiguous_swiglu}
     if args.copy_calibration:
         copy_calibration()
         return
@@ -720,6 +810,9 @@ def main():
     if any(c.group == "masked" for c in calls) and not args.only:
         log("masked decode GEMMs captured into HIP graphs")
         extra["masked_graph"] = masked_graph(calls, per_ms)
+    if any(c.group == "contiguous" for c in calls) and not args.only:
+        log("contiguous GEMM against its fused SwiGLU + re-quantise form")
+        extra["fused_swiglu"] = fused_swiglu_compare(calls, per_ms)
 
     quant = args.workload in ("quantize", "swiglu_quantize")
     cpu = None
