@@ -154,8 +154,12 @@ dg::TileShape heuristic(int kind, int rows, int n, int k, int groups, int num_cu
   static const Candidate cands[] = {
       // efficiencies measured relative to the 256x256 tile on full waves
       // (the 256x224 tile, 4x2 waves, balances N=7168 over the CUs but ran
-      // slower per tile than 256x256 by more than it gains: not a candidate)
-      {{256, 256, 2, 4}, 1.00}, {{256, 256, 1, 8}, 0.98}, {{256, 128, 2, 2}, 0.85}, {{128, 128, 2, 2}, 0.70},
+      // slower per tile than 256x256 by more than it gains: not a candidate;
+      // nor are 256x144 and 256x176 on 8x1 waves, fitted to N=2112, measured
+      // at half the per-tile rate; the 192-row tile gives M=4096, N=2112 198
+      // tiles instead of 144 on 256 CUs, 10% faster)
+      {{256, 256, 2, 4}, 1.00}, {{256, 256, 1, 8}, 0.98}, {{192, 256, 2, 4}, 0.80}, {{256, 128, 2, 2}, 0.85},
+      {{128, 128, 2, 2}, 0.70},
       {{128, 64, 2, 2}, 0.50},  {{64, 128, 1, 4}, 0.50},  {{64, 64, 1, 4}, 0.35},
   };
   double best = 1e300;
@@ -211,8 +215,14 @@ dg_status plan(int kind, int rows, int n, int k, int groups, int num_cus, bool a
   p.splits = splits;
   p.kchunk = chunk;
   const long work = tiles * splits;
-  long grid = work < slots ? work : slots;
-  if (grid > 8) grid -= grid % 8;  // keep workgroup -> XCD round robin aligned
+  // a multiple of 8 workgroups keeps the workgroup -> XCD round robin
+  // aligned with the kernel's per-XCD item ranges: rounded up when the work
+  // fits in one pass (the extra workgroups find no item), so no workgroup
+  // takes a second item while others idle; else the largest multiple of 8
+  // that fits on the CUs
+  long grid = work < slots ? (work + 7) / 8 * 8 : slots;
+  if (grid > slots && slots >= 8) grid = slots - slots % 8;
+  if (grid > 8 && grid == slots) grid -= grid % 8;
   if (grid < 1) grid = 1;
   l.shape = s;
   l.grid = (int)grid;

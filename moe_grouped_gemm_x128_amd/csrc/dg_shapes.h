@@ -14,6 +14,7 @@ constexpr int kBlockK = 128;  // K block = scale granularity
   X(256, 32, 4, 1, 4)     \
   X(256, 16, 4, 1, 4)     \
   X(256, 224, 4, 2, 2)    \
+  X(192, 256, 2, 4, 2)    \
   X(256, 128, 1, 8, 3)    \
   X(256, 64, 1, 4, 3)     \
   X(256, 128, 1, 4, 3)    \
@@ -33,6 +34,9 @@ constexpr int kBlockK = 128;  // K block = scale granularity
 // the tile's 128 output columns are exactly one 1x128 scale group.
 constexpr bool excluded(int bm, int bn, int wm, int kind) {
   if (kind == KIND_CONTIG_SWIGLU) return !(bm == 256 && bn == 256 && wm == 1);
+  // 192-row tiles: dense layouts only (a grouped layout's 128-row blocks would
+  // straddle them)
+  if (bm == 192) return !(kind == KIND_DENSE || kind == KIND_DENSE_POW2 || kind == KIND_BF16);
   return bm == 256 && bn == 256 && wm == 2 && (kind == KIND_WGRAD || kind == KIND_KGROUPED);
 }
 

@@ -38,7 +38,8 @@ int main(void) {
               CHECK(cfg.waves_m > 0 && cfg.waves_n > 0);
               CHECK(cfg.tiles >= 1 && cfg.grid >= 1);
               CHECK(cfg.k_splits >= 1 && cfg.k_splits <= kblocks);
-              CHECK((long)cfg.grid <= (long)cfg.tiles * cfg.k_splits);
+              CHECK((long)cfg.grid <= ((long)cfg.tiles * cfg.k_splits + 7) / 8 * 8);
+              CHECK(cfg.grid <= 8 || cfg.grid % 8 == 0);
             }
   CHECK(plans > 1000);
   /* rejected queries */

@@ -18,7 +18,7 @@ from tests.parity import (SENTINEL_BF16, bf16_bits, bits_to_f64, check_close, de
 
 pytestmark = pytest.mark.gpu
 
-TILES = [None, "256x128x2x2", "256x256x2x4", "256x224x4x2", "128x128x2x2", "128x64x2x2", "64x128x1x4", "64x64x1x4",
+TILES = [None, "256x128x2x2", "256x256x2x4", "256x224x4x2", "192x256x2x4", "128x128x2x2", "128x64x2x2", "64x128x1x4", "64x64x1x4",
          "64x32x2x2"]
 
 
@@ -190,7 +190,7 @@ def force_splits():
     os.environ.pop("DG_FORCE_SPLITS", None)
 
 
-@pytest.mark.parametrize("tile", ["64x32x2x2", "128x128x2x2", "256x256x1x8", "256x224x4x2"])
+@pytest.mark.parametrize("tile", ["64x32x2x2", "128x128x2x2", "256x256x1x8", "256x224x4x2", "192x256x2x4"])
 @pytest.mark.parametrize("splits", [2, 3, 4, 10])
 @pytest.mark.parametrize("m,n,k", [(70, 300, 1280), (1, 130, 512), (200, 2112, 1792)])
 def test_dense_split_k(dg, force_tile, force_splits, m, n, k, tile, splits):
