@@ -559,19 +559,30 @@ def cpu_baseline_quantize(calls, seconds):
 
 # --------------------------------------------------------------- timing ---
 
+SPIN_CYCLES = 4_000_000  # ~2 ms of GPU clock: covers the host's enqueue of one pass
+
+
 def per_call_times(calls, steps, cold=False):
     """Mean duration (ms) of each GEMM: HIP events around every call on the
     launch stream, over `steps` passes.  Used for the per-shape table and to
     find the dominant GEMM; not the timed steps (each event record takes GPU
-    time between kernels that a real caller would not spend).  cold: a 512 MB
-    buffer (more than the 256 MB MALL plus the L2s) is overwritten before each
-    call, outside its event pair, so every call starts with cold caches."""
+    time between kernels that a real caller would not spend).  Each pass
+    starts with a short spin kernel (torch.cuda._sleep) so the host enqueues
+    the pass while the GPU spins: the event pairs then time the GPU's
+    execution of each call, as the profiler's kernel durations do, rather
+    than the host's launch cost, which a call shorter than ~10 us would
+    otherwise show.  cold: a 512 MB buffer (more than the 256 MB MALL plus
+    the L2s) is overwritten before each call, outside its event pair, so
+    every call starts with cold caches."""
     import torch
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if cold else None
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
           for _ in range(steps)]
+    spin = getattr(torch.cuda, "_sleep", None)
     torch.cuda.synchronize()
     for s in range(steps):
+        if spin is not None:
+            spin(SPIN_CYCLES)
         for i, c in enumerate(calls):
             if cold:
                 flush.fill_(s & 0xff)

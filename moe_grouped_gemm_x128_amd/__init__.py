@@ -77,20 +77,27 @@ def _check(status: int, where: str):
         raise DGError(status, where)
 
 
+# The current stream's raw handle without building a torch Stream object
+# (a few microseconds per call otherwise, which small GEMMs would feel).
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(t: torch.Tensor):
-    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    if _raw_stream is not None:
+        return _raw_stream(t.get_device())
+    return torch.cuda.current_stream(t.device).cuda_stream
 
 
 def _ptr(t):
-    return ctypes.c_void_p(t.data_ptr())
+    return t.data_ptr()
 
 
 def _dev(*ts):
-    dev = ts[0].device
-    if dev.type != "cuda":
+    if not ts[0].is_cuda:
         raise ValueError("tensors must live on the GPU")
+    dev = ts[0].get_device()
     for t in ts:
-        if t.device != dev:
+        if not t.is_cuda or t.get_device() != dev:
             raise ValueError("all tensors must be on the same device")
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
