@@ -14,19 +14,22 @@
  *
  * Conventions shared by every entry point:
  *   - every tensor pointer is a DEVICE pointer owned by the caller; the
- *     library never allocates, frees or keeps user memory;
+ *     library never allocates, frees or keeps the caller's memory;
  *   - split K: for shapes with too few output tiles to occupy every compute
  *     unit (few rows, long K), the dense and masked calls split K over several
  *     workgroups and add the fp32 partials in a second kernel, in a fixed
  *     order (results are deterministic).  The partials (splits * rows * N * 4
- *     bytes, at most 256 MB) live in a buffer taken from a memory pool the
- *     library owns per device, allocated before the two kernels and freed
- *     after them in the order of `stream`, so the buffer is never seen by
- *     another stream and does not outlive the call; the pool keeps freed
- *     blocks for reuse until the process ends.  If no buffer can be had the
- *     call runs without a split instead.  A call made while `stream` is being
- *     captured into a HIP graph never splits, so it allocates nothing and
- *     records only the GEMM kernel;
+ *     bytes, at most 256 MB) live in a workspace the library keeps per (device,
+ *     stream) -- calls on one stream are ordered, so they share it -- taken
+ *     from a memory pool the library owns per device and grown in the
+ *     stream's order (no device synchronisation); it is the one piece of
+ *     device memory the library holds beyond the caller's tensors, kept until
+ *     the process ends.  At most 64 streams keep one; a call on any further
+ *     stream takes a buffer for itself and returns it to the pool after its
+ *     kernels.  If no buffer can be had the call runs without a split.  A call
+ *     made while `stream` is being captured into a HIP graph never splits, so
+ *     it allocates nothing and records only the GEMM kernel
+ *     (dg_grouped_fp8_masked_noalloc keeps the split there, see below);
  *   - tensors are row-major with the last dimension contiguous;
  *   - fp8 = OCP E4M3FN bytes (what torch calls float8_e4m3fn); scales fp32;
  *   - K_b = K/128, NB = ceil(N/128);
