@@ -72,7 +72,7 @@ def log(msg):
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "moe_grouped_gemm_x128_amd", "csrc", f)
                   for f in ("dg_kernels.hip", "dg_api.hip", "dg_kernel.h", "dg_quant.hip", "dg_shapes.h",
-                            "dg_shapes.hip", "dg_rsrc.h")]
+                            "dg_shapes.hip", "dg_rsrc.h", "dg_fp8_codec.h")]
 COLD_DISPATCHES = 50  # cold-cache dispatches of the dominant GEMM (median reported)
 
 
