@@ -158,7 +158,8 @@ dg::TileShape heuristic(int kind, int rows, int n, int k, int groups, int num_cu
       // nor are 256x144 and 256x176 on 8x1 waves, fitted to N=2112, measured
       // at half the per-tile rate; the 192-row tile gives M=4096, N=2112 198
       // tiles instead of 144 on 256 CUs, 10% faster)
-      {{256, 256, 2, 4}, 1.00}, {{256, 256, 1, 8}, 0.98}, {{192, 256, 2, 4}, 0.80}, {{256, 128, 2, 2}, 0.85},
+      {{256, 256, 2, 4}, 1.00}, {{256, 256, 1, 8}, 0.98}, {{224, 256, 1, 8}, 0.92}, {{192, 256, 2, 4}, 0.80},
+      {{256, 128, 2, 2}, 0.85},
       {{128, 128, 2, 2}, 0.70},
       {{128, 64, 2, 2}, 0.50},  {{64, 128, 1, 4}, 0.50},  {{64, 64, 1, 4}, 0.35},
   };

@@ -253,13 +253,13 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   // every wave) and scale pieces w, w+NW, ... (some waves one fewer).
   constexpr int PA = BM / 8, PB = BN / 8, PSA = SA_N / 64, PSB = SB_N / 64;
   constexpr int PS = PSA + PSB;
-  // (a block width that is not a multiple of 8 * NW rows, e.g. 224, leaves
-  // some waves one piece short: they issue a dead piece into the sink instead)
+  // (a block width or height that is not a multiple of 8 * NW rows, e.g.
+  // 224, leaves some waves one piece short: they issue a dead piece into the
+  // sink instead)
   constexpr int QA = (PA + NW - 1) / NW, QB = (PB + NW - 1) / NW, QS = (PS + NW - 1) / NW;
   // every wave issues QA + QB + QS DMAs per stage: scale pieces past PS are
   // padding that reads nothing and lands in a sink slot after the ring
   constexpr int DMIN = QA + QB + QS;
-  static_assert(PA % NW == 0, "A pieces split evenly over the waves");
   static_assert(BN % 16 == 0, "whole 16-column fragments");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE + 1024];  // + padding-DMA sink
@@ -581,7 +581,17 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     auto issue = [&](const Blk& d, int lo, int hi) {
 #pragma unroll
       for (int q = 0; q < QA; ++q)
-        if (q >= lo && q < hi) dma16(d.base + OFF_A + (wave + NW * q) * 1024, d.a, voff0 + q * step);
+        if (q >= lo && q < hi) {
+          if constexpr (PA % NW == 0) {
+            dma16(d.base + OFF_A + (wave + NW * q) * 1024, d.a, voff0 + q * step);
+          } else {
+            // past the last A piece: read nothing into the sink
+            const bool real = wave + NW * q < PA;
+            v4i rq = d.a;
+            rq[2] = real ? d.a[2] : 0;
+            dma16(real ? d.base + OFF_A + (wave + NW * q) * 1024 : smem_lds + S * STAGE, rq, voff0 + q * step);
+          }
+        }
 #pragma unroll
       for (int q = 0; q < QB; ++q) {
         if (QA + q < lo || QA + q >= hi) continue;

@@ -121,7 +121,7 @@ def test_masked_small(dg, force_tile, tile):
     check_close(bits_to_f64(got[rows]), bits_to_f64(ref[rows]), "masked small")
 
 
-@pytest.mark.parametrize("tile", [None, "256x224x4x2", "256x128x2x2", "128x128x2x2", "64x128x1x4"])
+@pytest.mark.parametrize("tile", [None, "256x224x4x2", "224x256x1x8", "256x128x2x2", "128x128x2x2", "64x128x1x4"])
 def test_wgrad_small(dg, force_tile, tile):
     w = inputs.make_wgrad(200, 130, [384], seed=inputs.SEED_BASE + 4)
     force_tile(tile)
@@ -133,11 +133,13 @@ def test_wgrad_small(dg, force_tile, tile):
     check_close(d.cpu().numpy(), ref, "wgrad small")
 
 
-def test_k_grouped_wgrad_small(dg):
+@pytest.mark.parametrize("m,n,tile", [(130, 72, None), (500, 300, None), (500, 300, "256x256x1x8")])
+def test_k_grouped_wgrad_small(dg, force_tile, m, n, tile):
     ks = [128, 0, 256, 384]
-    w = inputs.make_wgrad(130, 72, ks, seed=inputs.SEED_BASE + 5)
+    w = inputs.make_wgrad(m, n, ks, seed=inputs.SEED_BASE + 5)
+    force_tile(tile)
     d = dev(w.d0)
-    say("k-grouped wgrad 130x72 ks=[128,0,256,384]")
+    say(f"k-grouped wgrad {m}x{n} ks=[128,0,256,384] tile={tile}")
     dg.dg_k_grouped_wgrad_fp8_nt(dev(w.a), dev(w.sa), dev(w.b), dev(w.sb), d, ks)
     torch.cuda.synchronize()
     ref, _ = oracle.k_grouped_wgrad(w.a, w.sa, w.b, w.sb, ks, w.d0)
