@@ -1,6 +1,8 @@
-"""The entry points added beside the GEMM family under HIP graph capture:
-the quantiser, the power-of-two-scale GEMM and the BF16 GEMM, alone and as
-one captured quantise -> GEMM pipeline.  Each graph is replayed several times
+"""Entry points under HIP graph capture: the quantiser, the power-of-two-scale
+GEMM and the BF16 GEMM, alone and as one captured quantise -> GEMM pipeline;
+the masked and contiguous grouped GEMMs with their device-side control data
+(masked_m, m_indices) rewritten between replays; and the contiguous GEMM with
+the fused SwiGLU + re-quantise epilogue.  Each graph is replayed several times
 with new inputs copied in between (eager work and synchronisations between the
 replays); every replay must match the oracle on those inputs.  A call made
 while its stream is captured never splits K, so it allocates nothing."""
@@ -258,3 +260,51 @@ def test_contiguous_graph_replays(dg):
         valid = (mi >= 0) & (mi < g)
         assert np.all(got[~valid] == 0xFFFF), f"replay {rep}: padding or out-of-range rows written"
         check_close(bits_to_f64(got[valid]), bits_to_f64(ref_bits[valid]), f"contiguous replay {rep}")
+
+
+def test_fused_swiglu_graph_replays(dg):
+    """The contiguous GEMM with the fused SwiGLU + re-quantise epilogue,
+    captured once and replayed with A and m_indices rewritten on the device
+    (exact-output operands): every replay gives the oracle composition's codes
+    and scales on the valid rows (the stand-alone step's bar) and leaves the
+    padding rows' sentinels."""
+    g, rpe, i, k = 3, 384, 256, 512
+    x = inputs.make_contiguous_exact(g, rpe, 2 * i, k, seed=inputs.SEED_BASE + 150)
+    mt = x.m_total
+    say(f"fused swiglu graph G={g} rows/expert={rpe} I={i} K={k}")
+    a, sa = dev(x.a), dev(x.sa)
+    b, sb = dev(x.b), dev(x.sb)
+    ids = dev(x.m_indices)
+    q = torch.full((mt, i), 0x7F, dtype=torch.uint8, device="cuda")
+    s = torch.full((mt, i // 128), float("nan"), dtype=torch.float32, device="cuda")
+    graph = capture(lambda: dg.dg_grouped_fp8_contiguous_swiglu(a, sa, b, sb, q, s, ids))
+    margin = 2.0 ** -18
+    for rep in range(3):
+        y = inputs.make_contiguous_exact(g, rpe, 2 * i, k, seed=inputs.SEED_BASE + 151 + rep)
+        mi = y.m_indices.copy()
+        if rep == 1:
+            mi[rpe:2 * rpe] = -1       # an empty expert
+        if rep == 2:
+            mi[:128] = g + 2           # out-of-range ids are skipped
+        a.copy_(dev(y.a))
+        sa.copy_(dev(y.sa))
+        ids.copy_(dev(mi))
+        q.fill_(0x7F)
+        s.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got_q, got_s = q.cpu().numpy(), s.cpu().numpy()
+        valid = (mi >= 0) & (mi < g)
+        assert np.all(got_q[~valid] == 0x7F) and np.all(np.isnan(got_s[~valid])), f"replay {rep}: padding written"
+        bits, exact = oracle.grouped_contiguous(y.a, y.sa, x.b, x.sb, mi, np.zeros((mt, 2 * i), np.uint16))
+        assert np.array_equal(exact[valid].astype(np.float32).astype(np.float64), exact[valid])
+        q_ref, s_ref, h = oracle.swiglu_quantize_1x128(np.ascontiguousarray(bits[valid]))
+        gq, gs = got_q[valid], got_s[valid]
+        assert np.all(np.abs(gs.astype(np.float64) - s_ref) <= 2.0 ** -20 * s_ref), f"replay {rep}: scales"
+        yv = np.clip(h / np.repeat(s_ref.astype(np.float64), 128, axis=1), -448.0, 448.0)
+        lo = oracle.e4m3_encode(np.clip(yv * (1 - margin), -448.0, 448.0).astype(np.float32))
+        hi = oracle.e4m3_encode(np.clip(yv * (1 + margin), -448.0, 448.0).astype(np.float32))
+        firm = lo == hi
+        assert np.array_equal(gq[firm], q_ref[firm]), f"replay {rep}: codes"
+        assert np.all((gq[~firm] == lo[~firm]) | (gq[~firm] == hi[~firm])), f"replay {rep}: code outside the bracket"
