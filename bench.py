@@ -27,7 +27,7 @@ contiguous G=8, N=4096, K=7168 GEMM is timed against its form with SwiGLU and
 the FP8 re-quantise fused into the epilogue (`fused_swiglu`).
 
 Other workloads (dense, contiguous, masked, wgrad, k_grouped_wgrad, small,
-dense_ue8m0 -- the dense sweep with power-of-two scales --, bf16 -- the
+dense_ue8m0 -- the dense sweep with packed UE8M0 scales --, bf16 -- the
 sweep's shapes in BF16 against the bf16 peak --, quantize, the FP8 quantiser
 in GB/s, and swiglu_quantize, the SwiGLU + FP8 re-quantise step between an
 expert's two GEMMs in GB/s, and contiguous_swiglu, the contiguous sweep with
@@ -142,8 +142,9 @@ def _sample_idx(rng, count, *highs):
 # ------------------------------------------------------------- workloads ---
 
 def build_dense(small=False, pow2=False):
-    """The dense sweep; pow2: power-of-two (UE8M0) scales through
-    dg_gemm_fp8_nt_ue8m0 (scales applied by the block-scaled MFMA)."""
+    """The dense sweep; pow2: power-of-two scales in the packed UE8M0 format
+    (four exponent bytes per int32) through dg_gemm_fp8_nt_ue8m0_packed
+    (scales applied by the block-scaled MFMA)."""
     import torch
     import moe_grouped_gemm_x128_amd as dg
     from harness import inputs, workloads
@@ -154,20 +155,22 @@ def build_dense(small=False, pow2=False):
     for s in shapes:
         m, n, k = s["m"], s["n"], s["k"]
         mmax = max(x["m"] for x in shapes if x["k"] == k)
+        pack = inputs.pack_ue8m0 if pow2 else (lambda s: s)
         if k not in a_by_k:
             a, sa = inputs.quantize_1x128(inputs._normal(inputs._rng(seed + k, 0), (mmax, k)), pow2)
-            a_by_k[k] = (a, sa, _dev(a), _dev(sa))
+            a_by_k[k] = (a, sa, _dev(a), _dev(pack(sa)))
         if (n, k) not in b_by_nk:
             b, sb = inputs.quantize_128x128(inputs._normal(inputs._rng(seed + n * 7 + k, 1), (n, k)), pow2)
-            b_by_nk[(n, k)] = (b, sb, _dev(b), _dev(sb))
+            b_by_nk[(n, k)] = (b, sb, _dev(b), _dev(pack(sb)))
         a, sa, da, dsa = a_by_k[k]
         b, sb, db, dsb = b_by_nk[(n, k)]
         da_m, dsa_m = da[:m], dsa[:m]
         out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
-        gemm = dg.dg_gemm_fp8_nt_ue8m0 if pow2 else dg.dg_gemm_fp8_nt
+        gemm = dg.dg_gemm_fp8_nt_ue8m0_packed if pow2 else dg.dg_gemm_fp8_nt
         fn = (lambda da_m=da_m, dsa_m=dsa_m, db=db, dsb=dsb, out=out, gemm=gemm:
               gemm(da_m, dsa_m, db, dsb, out))
-        nbytes = m * k + m * (k // 128) * 4 + n * k + ((n + 127) // 128) * (k // 128) * 4 + m * n * 2
+        swords = (k // 128 + 3) // 4 if pow2 else k // 128  # 4-byte scale words per row
+        nbytes = m * k + m * swords * 4 + n * k + ((n + 127) // 128) * swords * 4 + m * n * 2
 
         def sample(rng, count, a=a[:m], sa=sa[:m], b=b, sb=sb, m=m, n=n, k=k):
             import oracle
@@ -180,7 +183,7 @@ def build_dense(small=False, pow2=False):
     desc = ("dense FP8 NT GEMM sweep: M in {64,128,4096} x (N,K) in {(2112,7168),(24576,1536),"
             "(32768,512),(7168,16384),(4096,7168),(7168,2048)}" if not small else "dense M=128 N=256 K=512")
     name = "dense_small" if small else ("dense_sweep_ue8m0" if pow2 else "dense_sweep")
-    scales = "A 1x128, B 128x128, " + ("power-of-two (UE8M0) values in fp32" if pow2 else "fp32")
+    scales = "A 1x128, B 128x128, " + ("packed UE8M0 (four exponent bytes per int32)" if pow2 else "fp32")
     return calls, {"workload": name, "description": desc, "shapes": len(calls), "scales": scales, "out": "bf16"}
 
 

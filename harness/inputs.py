@@ -46,6 +46,22 @@ def _pow2_ceil(s: np.ndarray) -> np.ndarray:
     return np.ldexp(1.0, np.where(m == 0.5, e - 1, e)).astype(np.float32)
 
 
+def pack_ue8m0(s: np.ndarray) -> np.ndarray:
+    """Power-of-two fp32 scales [R, KB] -> packed UE8M0 words int32 [R, ceil(KB/4)]:
+    the byte of K block 4w+i is byte i of word w (little-endian), and the byte
+    is the scale's fp32 exponent field (2^-127 .. 2^127 -> 0 .. 254).  Padding
+    bytes past KB hold 255 (the E8M0 NaN code), so reading one shows up."""
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    r, kb = s.shape
+    m, _ = np.frexp(s.astype(np.float64))
+    assert np.all(m == 0.5) and np.all(s > 0), "scales must be positive powers of two"
+    assert np.all(s >= np.float32(2.0 ** -127)), "below the UE8M0 range"
+    kw = (kb + 3) // 4
+    raw = np.full((r, 4 * kw), 255, np.uint8)
+    raw[:, :kb] = ((s.view(np.uint32) >> 23) & 0xFF).astype(np.uint8)
+    return np.frombuffer(raw.tobytes(), dtype="<i4").reshape(r, kw).astype(np.int32)
+
+
 def quantize_1x128(x: np.ndarray, pow2: bool = False) -> tuple[np.ndarray, np.ndarray]:
     """x fp32 [R, K] (K % 128 == 0) -> (q uint8 [R, K], s fp32 [R, K/128]).
 

@@ -85,6 +85,21 @@ dg_status dg_gemm_fp8_nt(const void* a, const float* sa, const void* b, const fl
 dg_status dg_gemm_fp8_nt_ue8m0(const void* a, const float* sa, const void* b, const float* sb,
                                void* c, int m, int n, int k, hipStream_t stream);
 
+/* The same GEMM with the scales in the packed UE8M0 format (DeepGEMM pages,
+ * aikraft.ru support table: packed UE8M0, four values in one torch.int).
+ * Each int32 word holds the 8-bit biased exponents E of four consecutive
+ * 128-wide K blocks, K block 4w + i in byte i (bits 8i..8i+7) of word w; the
+ * scale is 2^(E - 127), E in 0..254 (E = 255 is the E8M0 NaN code and makes
+ * the outputs it touches NaN).  Layouts, with K_w = ceil(K/512):
+ *   sa [M, K_w] int32 (row r, word w: K blocks 4w..4w+3 of row r)
+ *   sb [ceil(N/128), K_w] int32 (one exponent per 128x128 block)
+ * The bytes of the last word past K/128 blocks are ignored.  The result is
+ * bit-identical to dg_gemm_fp8_nt_ue8m0 with the fp32 scales 2^(E - 127).
+ * sa, sb 4-byte aligned; the rest as dg_gemm_fp8_nt. */
+dg_status dg_gemm_fp8_nt_ue8m0_packed(const void* a, const int32_t* sa, const void* b,
+                                      const int32_t* sb, void* c, int m, int n, int k,
+                                      hipStream_t stream);
+
 /* Dense BF16 NT GEMM (DeepGEMM pages: aikraft.ru lists BF16 GEMM beside FP8
  * in its support table; DeepSeek DeepGEMM 中文讲解, "未来计划": BF16 support).
  * The same scheduler, operand staging and layouts as the FP8 path, with bf16

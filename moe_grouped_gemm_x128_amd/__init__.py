@@ -37,13 +37,14 @@ _lib.dg_grouped_fp8_masked_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i3
 _lib.dg_wgrad_fp8_nt.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]
 _lib.dg_k_grouped_wgrad_fp8_nt.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]
 _lib.dg_gemm_fp8_nt_ue8m0.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]
+_lib.dg_gemm_fp8_nt_ue8m0_packed.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]
 _lib.dg_gemm_bf16_nt.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _vp]
 _lib.dg_quantize_fp8_1x128.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
 _lib.dg_quantize_fp8_128x128.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
 _lib.dg_quantize_fp8_1x128_transposed.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
 _lib.dg_swiglu_quantize_fp8_1x128.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
 for _f in ("dg_gemm_fp8_nt", "dg_grouped_fp8_contiguous", "dg_grouped_fp8_contiguous_swiglu", "dg_grouped_fp8_masked", "dg_grouped_fp8_masked_noalloc",
-           "dg_wgrad_fp8_nt", "dg_k_grouped_wgrad_fp8_nt", "dg_gemm_fp8_nt_ue8m0", "dg_gemm_bf16_nt", "dg_quantize_fp8_1x128",
+           "dg_wgrad_fp8_nt", "dg_k_grouped_wgrad_fp8_nt", "dg_gemm_fp8_nt_ue8m0", "dg_gemm_fp8_nt_ue8m0_packed", "dg_gemm_bf16_nt", "dg_quantize_fp8_1x128",
            "dg_quantize_fp8_128x128", "dg_quantize_fp8_1x128_transposed", "dg_swiglu_quantize_fp8_1x128"):
     getattr(_lib, _f).restype = ctypes.c_int
 _lib.dg_status_string.argtypes = [ctypes.c_int]
@@ -165,6 +166,27 @@ def dg_gemm_fp8_nt_ue8m0(a, sa, b, sb, c):
     _dev(a, sa, b, sb, c)
     _check(_lib.dg_gemm_fp8_nt_ue8m0(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(c), m, n, k, _stream(c)),
            "dg_gemm_fp8_nt_ue8m0")
+    return c
+
+
+def dg_gemm_fp8_nt_ue8m0_packed(a, sa, b, sb, c):
+    """dg_gemm_fp8_nt_ue8m0 with packed UE8M0 scales: int32 words holding the
+    biased exponents of four consecutive K blocks, block 4w+i in byte i
+    (sa [M, ceil(K/512)], sb [ceil(N/128), ceil(K/512)]; see include/dg.h)."""
+    _fp8(a, "a"); _fp8(b, "b")
+    for t, name in ((sa, "sa"), (sb, "sb")):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32 (packed UE8M0), got {t.dtype}")
+    m, k = a.shape
+    n = b.shape[0]
+    kw = (k // 128 + 3) // 4
+    _shape(b, (n, k), "b"); _shape(sa, (m, kw), "sa"); _shape(sb, ((n + 127) // 128, kw), "sb")
+    _shape(c, (m, n), "c")
+    if c.dtype != torch.bfloat16:
+        raise TypeError("c must be bfloat16")
+    _dev(a, sa, b, sb, c)
+    _check(_lib.dg_gemm_fp8_nt_ue8m0_packed(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(c), m, n, k, _stream(c)),
+           "dg_gemm_fp8_nt_ue8m0_packed")
     return c
 
 
@@ -337,6 +359,9 @@ def gemm_fp8_fp8_bf16_nt(lhs, rhs, out):
 
 
 def gemm_fp8_fp8_bf16_nt_ue8m0(lhs, rhs, out):
+    """Power-of-two scales as fp32 values, or packed UE8M0 (int32 words)."""
+    if lhs[1].dtype == torch.int32:
+        return dg_gemm_fp8_nt_ue8m0_packed(lhs[0], lhs[1], rhs[0], rhs[1], out)
     return dg_gemm_fp8_nt_ue8m0(lhs[0], lhs[1], rhs[0], rhs[1], out)
 
 

@@ -343,6 +343,7 @@ dg_status run(int kind, dg::Params& p, int rows, int n, int k, int groups, hipSt
   int cus = 0;
   if (device_cus(&cus) != 0) return DG_ERROR_LAUNCH;
   (void)hipGetLastError();  // clear a stale error from unrelated work
+  if (p.sks == 0) p.sks = p.kbs;  // one fp32 scale per K block unless packed
   const bool splittable = dense_like(kind) || kind == DG_KIND_MASKED;
   const bool may_split = splittable && (scratch != nullptr || !stream_capturing(stream));
   Launch l;
@@ -465,6 +466,30 @@ dg_status dg_gemm_fp8_nt_ue8m0(const void* a, const float* sa, const void* b, co
   p.n = n;
   p.lda = k;
   p.kbs = k / 128;
+  p.groups = 1;
+  p.vec_out = (n % 4 == 0) && aligned(c, 8);
+  return run(dg::KIND_DENSE_POW2, p, m, n, k, 1, stream);
+}
+
+dg_status dg_gemm_fp8_nt_ue8m0_packed(const void* a, const int32_t* sa, const void* b, const int32_t* sb, void* c,
+                                      int m, int n, int k, hipStream_t stream) {
+  if (!a || !sa || !b || !sb || !c) return DG_ERROR_INVALID_VALUE;
+  if (m <= 0 || n <= 0 || k <= 0) return DG_ERROR_INVALID_VALUE;
+  if (k % 128 != 0) return DG_ERROR_UNSUPPORTED;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(sa, 4) || !aligned(sb, 4) || !aligned(c, 2))
+    return DG_ERROR_UNSUPPORTED;
+  dg::Params p = base_params();
+  p.a = static_cast<const uint8_t*>(a);
+  p.sa = reinterpret_cast<const float*>(sa);  // the kernel copies the words and reads their bytes
+  p.b = static_cast<const uint8_t*>(b);
+  p.sb = reinterpret_cast<const float*>(sb);
+  p.out = c;
+  p.m = m;
+  p.n = n;
+  p.lda = k;
+  p.kbs = k / 128;
+  p.sks = (p.kbs + 3) / 4;
+  p.spk = 2;
   p.groups = 1;
   p.vec_out = (n % 4 == 0) && aligned(c, 8);
   return run(dg::KIND_DENSE_POW2, p, m, n, k, 1, stream);

@@ -28,7 +28,7 @@ constexpr int kMaxKGroups = 256;
 
 struct Params {
   const uint8_t* a;      // fp8 LHS (row stride lda bytes)
-  const float* sa;       // LHS scales, row stride kbs floats
+  const float* sa;       // LHS scales, row stride sks words
   const uint8_t* b;      // fp8 RHS, [G][N][lda]
   const float* sb;       // RHS scales: [G][NB][kbs] (block) or [N][kbs] (row)
   void* out;             // bf16 C or fp32 D (fused SwiGLU: fp8 codes)
@@ -37,7 +37,10 @@ struct Params {
   int m;                 // rows per group: M, M_total or M_max
   int n;                 // N
   int lda;               // bytes per operand row: K, or total tokens T
-  int kbs;               // scale row stride in 128-blocks (lda / 128)
+  int kbs;               // K blocks per operand row (lda / 128)
+  int sks;               // scale row stride in 4-byte words: kbs (fp32 scales) or
+                         // ceil(kbs / 4) (packed UE8M0: four exponent bytes per word)
+  int spk;               // log2 of the K blocks per scale word: 0 or 2 (packed)
   int groups;            // G (1 for dense and wgrad)
   int tiles_m;           // ceil(m / BM)
   int tiles_n;           // ceil(n / BN)

@@ -170,8 +170,11 @@ __device__ __forceinline__ v8i load_frag(const uint8_t* frag_base, uint32_t lo, 
 // lane holding that chunk supplies (byte 0 of its scale operand), and adds
 // srcC: acc + sb * sa * (block sum), with the scaling applied inside the matrix
 // unit and no vector-unit promotion.  A positive power-of-two fp32 scale
-// 2^(E-127) has E as its exponent field: bits >> 23.
-__device__ __forceinline__ int ue8m0_of(float s) { return (int)(__builtin_bit_cast(uint32_t, s) >> 23); }
+// 2^(E-127) has E as its exponent field (shift 23); a packed word holds the
+// bytes E of four consecutive K blocks, K block 4w + i in byte i (shift 8i).
+__device__ __forceinline__ int ue8m0_of(float s, uint32_t shift) {
+  return (int)((__builtin_bit_cast(uint32_t, s) >> shift) & 0xffu);
+}
 
 __device__ __forceinline__ v4f mfma_block_scaled(const v8i& b_rows, const v8i& a_rows, const v4f& acc, int sb_e,
                                                  int sa_e) {
@@ -462,19 +465,19 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     // fused SwiGLU: gate rows n0.. and up rows I + n0.. (I = N/2), one range
     const uint32_t brows = kSwiGLU ? (uint32_t)(p.n / 2 + BN / 2) : (uint32_t)bcols;
     r.b = buffer_rsrc(p.b + ((int64_t)bg * p.n + x.n0) * (int64_t)p.lda, on * brows * p.lda);
-    const Rsrc sa = buffer_rsrc(p.sa + x.a_row0 * (int64_t)p.kbs, son * (uint32_t)x.rows * p.kbs * 4);
+    const Rsrc sa = buffer_rsrc(p.sa + x.a_row0 * (int64_t)p.sks, son * (uint32_t)x.rows * p.sks * 4);
     Rsrc sb;
     if constexpr (kRowScaleB) {
-      sb = buffer_rsrc(p.sb + (int64_t)x.n0 * p.kbs, on * (uint32_t)bcols * p.kbs * 4);
+      sb = buffer_rsrc(p.sb + (int64_t)x.n0 * p.sks, on * (uint32_t)bcols * p.sks * 4);
     } else {
       // only the 128-column blocks the tile touches
       // (fused SwiGLU: the gate block n0/128 through the up block (I + n0)/128)
       const int nb0 = x.n0 / kBK;
       const int nbt = kSwiGLU ? p.n / 2 / kBK + 1
                               : min(nb_rows - nb0, (x.n0 - nb0 * kBK + BN + kBK - 1) / kBK);  // a tile may straddle blocks
-      sb = buffer_rsrc(p.sb + ((int64_t)x.g * nb_rows + nb0) * p.kbs, son * (uint32_t)max(nbt, 0) * p.kbs * 4);
+      sb = buffer_rsrc(p.sb + ((int64_t)x.g * nb_rows + nb0) * p.sks, son * (uint32_t)max(nbt, 0) * p.sks * 4);
     }
-    const uint32_t prow = 64u * p.kbs * 4;  // bytes of 64 scale rows
+    const uint32_t prow = 64u * p.sks * 4;  // bytes of 64 scale rows
 #pragma unroll
     for (int q = 0; q < QS; ++q) {
       const int sp = wave + NW * q;  // scale piece: sa rows 64*sp.., then sb
@@ -540,10 +543,10 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
                 : voff0;
     const uint32_t stepb = kSwiGLU ? (uint32_t)(NW * 4) * p.lda : step;
     // scale pieces: 64 rows (or columns / 128-blocks) each, one float per lane
-    const uint32_t svoff = (uint32_t)lane * p.kbs * 4;
+    const uint32_t svoff = (uint32_t)lane * p.sks * 4;
     // fused SwiGLU: the B scale piece's lane 1 reads the up block I/128 blocks
     // on, so the stage holds sb(gate) at 0 and sb(up) at 1
-    const uint32_t svoff_b = kSwiGLU && lane == 1 ? (uint32_t)(p.n / 2 / kBK) * p.kbs * 4 : svoff;
+    const uint32_t svoff_b = kSwiGLU && lane == 1 ? (uint32_t)(p.n / 2 / kBK) * p.sks * 4 : svoff;
 
     // The DMAs of one K block: each source moved to the block (empty past
     // the tile's K range or for a dead tile: such a block reads zeros and
@@ -573,7 +576,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
       d.a = at_k(r.a, kb * kBK, live);
       d.b = at_k(r.b, kb * kBK, live);
 #pragma unroll
-      for (int q = 0; q < QS; ++q) d.s[q] = at_k(r.s[q], kb * 4, live);
+      for (int q = 0; q < QS; ++q) d.s[q] = at_k(r.s[q], (kb >> p.spk) * 4, live);
       d.base = __builtin_amdgcn_readfirstlane(smem_lds + st * STAGE);
       return d;
     };
@@ -704,6 +707,9 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
       // one K block; `dma` is the block issued during it (S-1 ahead)
       auto block = [&](int rel, const Blk& dma) {
         const int st = (qs + rel) % S;
+        // power-of-two scales: where this block's exponent byte sits in the
+        // scale words read from LDS (fp32 exponent field, or packed byte)
+        const uint32_t esh = p.spk ? 8u * ((uint32_t)(rc.kb0 + rel) & 3u) : 23u;
         // this wave's DMAs for block `rel` are done once at most
         // (blocks issued after it) x DMIN of its operations remain in flight;
         // with cross-tile prefetch S-2 blocks always follow (epilogue stores
@@ -803,8 +809,10 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
               // B fragment i carries sb, A fragment j carries its rows' sa
               const int j = kStreamM ? o : r, i = kStreamM ? r : o;
               const float sa = kStreamM ? sa_cur : sav[kStreamM ? 0 : j];
-              acc_at(o, r) = kStreamM ? mfma_block_scaled(res[r], cur, acc_at(o, r), ue8m0_of(sbv[i]), ue8m0_of(sa))
-                                      : mfma_block_scaled(cur, res[r], acc_at(o, r), ue8m0_of(sbv[i]), ue8m0_of(sa));
+              acc_at(o, r) = kStreamM ? mfma_block_scaled(res[r], cur, acc_at(o, r), ue8m0_of(sbv[i], esh),
+                                                          ue8m0_of(sa, esh))
+                                      : mfma_block_scaled(cur, res[r], acc_at(o, r), ue8m0_of(sbv[i], esh),
+                                                          ue8m0_of(sa, esh));
             } else {
               part[r] = kStreamM ? mfma_block(res[r], cur) : mfma_block(cur, res[r]);
               if (r + 1 < NR) {

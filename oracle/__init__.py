@@ -150,6 +150,34 @@ def gemm_fp8_nt_at(a, sa, b, sb, rows, cols):
     return out
 
 
+def unpack_ue8m0(words, kblocks: int) -> np.ndarray:
+    """Packed UE8M0 scales -> fp32 scale values [R, kblocks].
+
+    DeepGEMM pages (aikraft.ru, support table): the scale format of the newer
+    architecture is packed UE8M0, four values in one torch.int.  Read here as:
+    word w of a row holds the scales of K blocks 4w..4w+3, K block 4w+i in
+    byte i (little-endian, bits 8i..8i+7); a byte E is the unsigned 8-bit
+    exponent of the E8M0 format, scale 2^(E - 127), with E = 255 the format's
+    NaN.  Bytes past `kblocks` are padding and ignored.  Every 2^(E - 127) for
+    E <= 254 is an fp32 value (2^-127 a subnormal), so the result is exact.
+    """
+    w = np.ascontiguousarray(words).astype(np.int64) & 0xFFFFFFFF
+    r, kw = w.shape
+    assert 4 * kw >= kblocks, "too few words for the K blocks"
+    out = np.empty((r, kblocks), np.float64)
+    for kb in range(kblocks):
+        e = (w[:, kb // 4] >> (8 * (kb % 4))) & 0xFF
+        out[:, kb] = np.where(e == 255, np.nan, np.ldexp(1.0, (e - 127).astype(np.int32)))
+    return out.astype(np.float32)
+
+
+def gemm_fp8_nt_ue8m0_packed(a, sa_words, b, sb_words):
+    """Dense GEMM with packed UE8M0 scales: the scales unpacked, then the
+    dense oracle (the packed format only encodes power-of-two fp32 scales)."""
+    kb = np.asarray(a).shape[1] // 128
+    return gemm_fp8_nt(a, unpack_ue8m0(sa_words, kb), b, unpack_ue8m0(sb_words, kb))
+
+
 def grouped_contiguous(a, sa, b, sb, m_indices, c_init):
     """Contiguous MoE: returns (C bits with valid rows written over c_init, exact fp64)."""
     a, b = _c(a, np.uint8), _c(b, np.uint8)

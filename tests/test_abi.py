@@ -151,6 +151,19 @@ def test_ue8m0_argument_errors(lib):
     assert f(A16, A16 + 2, A16, A16, A16, 1, 1, 128, None) == UNSUPPORTED
 
 
+def test_ue8m0_packed_argument_errors(lib):
+    f = lib.dg_gemm_fp8_nt_ue8m0_packed
+    f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 3 + [ctypes.c_void_p]
+    assert f(None, A16, A16, A16, A16, 1, 1, 128, None) == INVALID
+    assert f(A16, None, A16, A16, A16, 1, 1, 128, None) == INVALID
+    assert f(A16, A16, A16, None, A16, 1, 1, 128, None) == INVALID
+    assert f(A16, A16, A16, A16, A16, 1, -1, 128, None) == INVALID
+    assert f(A16, A16, A16, A16, A16, 1, 1, 640 + 64, None) == UNSUPPORTED   # K % 128
+    assert f(A16, A16 + 2, A16, A16, A16, 1, 1, 128, None) == UNSUPPORTED    # sa words
+    assert f(A16, A16, A16, A16 + 1, A16, 1, 1, 128, None) == UNSUPPORTED    # sb words
+    assert f(A16, A16, A16 + 8, A16, A16, 1, 1, 128, None) == UNSUPPORTED    # b alignment
+
+
 def test_quantizer_argument_errors(lib):
     vp, i = ctypes.c_void_p, ctypes.c_int
     for name in ("dg_quantize_fp8_1x128", "dg_quantize_fp8_128x128", "dg_quantize_fp8_1x128_transposed"):

@@ -4,7 +4,10 @@ special case of the oracle's fp32 scales, so the oracle is the same function
 and the bar is the same as for dg_gemm_fp8_nt: every output at small sizes
 over every tile instance, ragged tails, N not a multiple of 4 and forced K
 splits; sampled outputs at a full workload size in the benchmark's launch
-configuration."""
+configuration.  The packed format (int32 words of four exponent bytes) meets
+the same bar against the oracle's unpack-then-GEMM, and is bit-identical to
+the fp32-scale entry point on the same scales; the packer fills the bytes
+past the last K block with the NaN code, so reading one would show."""
 from __future__ import annotations
 
 import os
@@ -128,3 +131,90 @@ def test_ue8m0_full_size_sampled(dg, m, n, k):
     ref_bits = oracle.round_bf16(oracle.gemm_fp8_nt_at(d.a, d.sa, d.b, d.sb, rows, cols))
     check_close(bits_to_f64(got[rows, cols]), bits_to_f64(ref_bits), f"ue8m0 full {m}x{n}x{k}")
     assert not np.any(got == 0xFFFF), "outputs left unwritten"
+
+
+def run_packed(dg, d, sa_w=None, sb_w=None):
+    sa_w = inputs.pack_ue8m0(d.sa) if sa_w is None else sa_w
+    sb_w = inputs.pack_ue8m0(d.sb) if sb_w is None else sb_w
+    c = sentinel_bf16((d.m, d.n))
+    dg.dg_gemm_fp8_nt_ue8m0_packed(dev(d.a), dev(sa_w), dev(d.b), dev(sb_w), c)
+    torch.cuda.synchronize()
+    return bf16_bits(c)
+
+
+@pytest.mark.parametrize("tile", [None, "256x256x2x4", "256x256x1x8", "128x128x2x2", "64x64x1x4", "64x32x2x2"])
+@pytest.mark.parametrize("m,n,k", [(1, 1, 128), (17, 130, 384), (257, 390, 640), (129, 18, 1024),
+                                   (300, 1000, 1152)])
+def test_ue8m0_packed_ragged(dg, force, m, n, k, tile):
+    """K blocks 1, 3, 5, 8, 9: whole and padded last words."""
+    d = inputs.make_dense(m, n, k, seed=inputs.SEED_BASE + 61 + m + n, pow2=True)
+    force(tile)
+    say(f"ue8m0 packed {m}x{n}x{k} tile={tile}")
+    got = run_packed(dg, d)
+    bits, _ = oracle.gemm_fp8_nt_ue8m0_packed(d.a, inputs.pack_ue8m0(d.sa), d.b, inputs.pack_ue8m0(d.sb))
+    check_close(bits_to_f64(got), bits_to_f64(bits), f"ue8m0 packed {m}x{n}x{k} {tile}")
+    assert np.array_equal(got, run(dg, d)), "packed and fp32 power-of-two scales differ"
+
+
+@pytest.mark.parametrize("splits", [2, 3, 7])
+def test_ue8m0_packed_split_k(dg, force, splits):
+    """Splits that start inside a scale word (14 K blocks over 3 or 7 splits)."""
+    d = inputs.make_dense(64, 500, 1792, seed=inputs.SEED_BASE + 62, pow2=True)
+    force("64x64x1x4", splits)
+    say(f"ue8m0 packed 64x500x1792 splits={splits}")
+    got = run_packed(dg, d)
+    bits, _ = oracle.gemm_fp8_nt_ue8m0_packed(d.a, inputs.pack_ue8m0(d.sa), d.b, inputs.pack_ue8m0(d.sb))
+    check_close(bits_to_f64(got), bits_to_f64(bits), f"ue8m0 packed split {splits}")
+    assert np.array_equal(got, run(dg, d)), "packed and fp32 power-of-two scales differ"
+
+
+def test_ue8m0_packed_scale_range(dg):
+    """Exponent bytes over 67..167 (scales 2^-60 .. 2^40) in every byte lane."""
+    rng = np.random.default_rng(63)
+    m, n, k = 200, 260, 896
+    a = rng.integers(0, 256, (m, k), dtype=np.uint8)
+    b = rng.integers(0, 256, (n, k), dtype=np.uint8)
+    a[(a & 0x7F) == 0x7F] = 0x7E
+    b[(b & 0x7F) == 0x7F] = 0x7E
+    sa = np.ldexp(1.0, rng.integers(-60, 40, (m, k // 128))).astype(np.float32)
+    sb = np.ldexp(1.0, rng.integers(-60, 40, ((n + 127) // 128, k // 128))).astype(np.float32)
+    d = inputs.Dense(m, n, k, a, sa, b, sb)
+    say("ue8m0 packed scale range")
+    got = run_packed(dg, d)
+    bits, _ = oracle.gemm_fp8_nt_ue8m0_packed(a, inputs.pack_ue8m0(sa), b, inputs.pack_ue8m0(sb))
+    check_close(bits_to_f64(got), bits_to_f64(bits), "ue8m0 packed scale range")
+
+
+def test_ue8m0_packed_nan_code(dg):
+    """The E8M0 NaN code (255) in one row's K block makes that row NaN and
+    leaves every other row as the oracle gives it."""
+    d = inputs.make_dense(70, 200, 512, seed=inputs.SEED_BASE + 64, pow2=True)
+    sa_w = inputs.pack_ue8m0(d.sa)
+    raw = sa_w.view(np.uint8).reshape(70, -1).copy()
+    raw[5, 2] = 255                                   # row 5, K block 2
+    sa_w = raw.view(np.int32).reshape(sa_w.shape)
+    say("ue8m0 packed NaN code")
+    got = run_packed(dg, d, sa_w=sa_w)
+    vals = bits_to_f64(got)
+    assert np.all(np.isnan(vals[5])), "row with the NaN code"
+    bits, _ = oracle.gemm_fp8_nt_ue8m0_packed(d.a, sa_w, d.b, inputs.pack_ue8m0(d.sb))
+    keep = np.arange(70) != 5
+    check_close(vals[keep], bits_to_f64(bits)[keep], "ue8m0 packed other rows")
+
+
+def test_ue8m0_packed_full_size_sampled(dg):
+    """4096x7168x16384 (128 K blocks, 32 words per row) in the library's own
+    launch configuration: bit-identical to the fp32-scale entry point
+    everywhere, sampled outputs against the oracle."""
+    m, n, k = 4096, 7168, 16384
+    d = inputs.make_dense(m, n, k, seed=inputs.SEED_BASE + 1, pow2=True)
+    say(f"ue8m0 packed full {m}x{n}x{k}")
+    got = run_packed(dg, d)
+    assert np.array_equal(got, run(dg, d)), "packed and fp32 power-of-two scales differ"
+    rng = np.random.default_rng(65)
+    rows = np.concatenate([rng.integers(0, m, 1024), [0, m - 1, 0, m - 1]]).astype(np.int64)
+    cols = np.concatenate([rng.integers(0, n, 1024), [0, n - 1, n - 1, 0]]).astype(np.int64)
+    ref_bits = oracle.round_bf16(oracle.gemm_fp8_nt_at(d.a, oracle.unpack_ue8m0(inputs.pack_ue8m0(d.sa), k // 128),
+                                                      d.b, oracle.unpack_ue8m0(inputs.pack_ue8m0(d.sb), k // 128),
+                                                      rows, cols))
+    check_close(bits_to_f64(got[rows, cols]), bits_to_f64(ref_bits), "ue8m0 packed full")
