@@ -27,7 +27,8 @@ contiguous G=8, N=4096, K=7168 GEMM is timed against its form with SwiGLU and
 the FP8 re-quantise fused into the epilogue (`fused_swiglu`).
 
 Other workloads (dense, contiguous, masked, wgrad, k_grouped_wgrad, small,
-dense_ue8m0 -- the dense sweep with packed UE8M0 scales --, bf16 -- the
+dense_ue8m0, contiguous_ue8m0, masked_ue8m0 -- those sweeps with packed UE8M0
+scales --, bf16 -- the
 sweep's shapes in BF16 against the bf16 peak --, quantize, the FP8 quantiser
 in GB/s, and swiglu_quantize, the SwiGLU + FP8 re-quantise step between an
 expert's two GEMMs in GB/s, and contiguous_swiglu, the contiguous sweep with
@@ -187,33 +188,36 @@ def build_dense(small=False, pow2=False):
     return calls, {"workload": name, "description": desc, "shapes": len(calls), "scales": scales, "out": "bf16"}
 
 
-def build_contiguous():
+def build_contiguous(pow2=False):
     """MoE contiguous layout at 8192 rows per expert.  The G=4 problems are the
     first four experts of the G=8 ones: the same seeded streams give the same
     rows, weights and padding counts (make_contiguous draws them in order), so
-    each (N,K) is generated once and G=4 uses views of it."""
+    each (N,K) is generated once and G=4 uses views of it.  pow2: power-of-two
+    scales in the packed UE8M0 format (dg_grouped_fp8_contiguous_ue8m0_packed)."""
     import torch
     import moe_grouped_gemm_x128_amd as dg
     from harness import inputs, workloads
 
+    pack = inputs.pack_ue8m0 if pow2 else (lambda s: s)
+    gemm = dg.dg_grouped_fp8_contiguous_ue8m0_packed if pow2 else dg.dg_grouped_fp8_contiguous
     calls = []
     by_nk = {}
     for s in sorted(workloads.contiguous_sweep(), key=lambda s: -s["g"]):
         g, rpe, n, k = s["g"], s["rows_per_expert"], s["n"], s["k"]
         if (n, k) not in by_nk:
-            c = inputs.make_contiguous(g, rpe, n, k, s["seed"])
-            by_nk[(n, k)] = (c, _dev(c.a), _dev(c.sa), _dev(c.b), _dev(c.sb), _dev(c.m_indices))
+            c = inputs.make_contiguous(g, rpe, n, k, s["seed"], pow2=pow2)
+            by_nk[(n, k)] = (c, _dev(c.a), _dev(pack(c.sa)), _dev(c.b), _dev(pack(c.sb)), _dev(c.m_indices))
         c, da, dsa, db, dsb, dids = by_nk[(n, k)]
         assert g <= c.g
         mt = g * rpe
         a, sa, b, sb, ids = c.a[:mt], c.sa[:mt], c.b[:g], c.sb[:g], c.m_indices[:mt]
         da_g, dsa_g, db_g, dsb_g, ids_g = da[:mt], dsa[:mt], db[:g], dsb[:g], dids[:mt]
         out = torch.empty((mt, n), dtype=torch.bfloat16, device="cuda")
-        fn = (lambda da=da_g, dsa=dsa_g, db=db_g, dsb=dsb_g, out=out, ids=ids_g:
-              dg.dg_grouped_fp8_contiguous(da, dsa, db, dsb, out, ids))
+        fn = (lambda da=da_g, dsa=dsa_g, db=db_g, dsb=dsb_g, out=out, ids=ids_g, gemm=gemm:
+              gemm(da, dsa, db, dsb, out, ids))
         valid_rows = np.flatnonzero(ids >= 0)
         mv = valid_rows.size
-        kb, nb = k // 128, (n + 127) // 128
+        kb, nb = (k // 128 + 3) // 4 if pow2 else k // 128, (n + 127) // 128  # 4-byte scale words per row
         nbytes = mv * k + mv * kb * 4 + g * n * k + g * nb * kb * 4 + mt * 4 + mv * n * 2
 
         def sample(rng, count, a=a, sa=sa, b=b, sb=sb, ids=ids, rows=valid_rows, n=n, k=k):
@@ -223,14 +227,16 @@ def build_contiguous():
             oracle.grouped_contiguous_at(a, sa, b, sb, ids, r, cl)
             return 2.0 * k * count
 
-        call = Call(s["name"], 2.0 * mv * n * k, nbytes, fn, sample, group="contiguous")
+        call = Call(s["name"] + ("_ue8m0" if pow2 else ""), 2.0 * mv * n * k, nbytes, fn, sample,
+                    group="contiguous_ue8m0" if pow2 else "contiguous")
         call.operands = (da_g, dsa_g, db_g, dsb_g, ids_g, out)
         calls.append(call)
-    order = [s["name"] for s in workloads.contiguous_sweep()]
+    order = [s["name"] + ("_ue8m0" if pow2 else "") for s in workloads.contiguous_sweep()]
     calls.sort(key=lambda c: order.index(c.name))
-    return calls, {"workload": "contiguous_sweep", "description":
+    return calls, {"workload": "contiguous_sweep_ue8m0" if pow2 else "contiguous_sweep", "description":
                    "MoE contiguous: G in {4,8}, 8192 rows per expert minus U{0..127} padding rows, "
-                   "(N,K) in {(4096,7168),(7168,2048)}"}
+                   "(N,K) in {(4096,7168),(7168,2048)}"
+                   + ("; packed UE8M0 scales (four exponent bytes per int32)" if pow2 else "")}
 
 
 def build_contiguous_swiglu():
@@ -318,23 +324,27 @@ def fused_swiglu_compare(calls, per_ms, reps=20):
             "speedup": round((gemm + swiglu) / fused, 3)}
 
 
-def build_masked():
+def build_masked(pow2=False):
+    """MoE masked decode; pow2: power-of-two scales in the packed UE8M0 format
+    (dg_grouped_fp8_masked_ue8m0_packed)."""
     import torch
     import moe_grouped_gemm_x128_amd as dg
     from harness import inputs, workloads
 
+    pack = inputs.pack_ue8m0 if pow2 else (lambda s: s)
+    gemm = dg.dg_grouped_fp8_masked_ue8m0_packed if pow2 else dg.dg_grouped_fp8_masked
     calls = []
     for s in workloads.masked_sweep():
-        x = inputs.make_masked(s["g"], s["m_max"], s["n"], s["k"], s["seed"])
-        da, dsa, db, dsb, mm = _dev(x.a), _dev(x.sa), _dev(x.b), _dev(x.sb), _dev(x.masked_m)
+        x = inputs.make_masked(s["g"], s["m_max"], s["n"], s["k"], s["seed"], pow2=pow2)
+        da, dsa, db, dsb, mm = _dev(x.a), _dev(pack(x.sa)), _dev(x.b), _dev(pack(x.sb)), _dev(x.masked_m)
         out = torch.empty((x.g, x.m_max, x.n), dtype=torch.bfloat16, device="cuda")
-        fn = (lambda da=da, dsa=dsa, db=db, dsb=dsb, out=out, mm=mm:
-              dg.dg_grouped_fp8_masked(da, dsa, db, dsb, out, mm))
+        fn = (lambda da=da, dsa=dsa, db=db, dsb=dsb, out=out, mm=mm, gemm=gemm:
+              gemm(da, dsa, db, dsb, out, mm))
         fn_na = (lambda da=da, dsa=dsa, db=db, dsb=dsb, out=out, mm=mm:
                  dg.dg_grouped_fp8_masked_noalloc(da, dsa, db, dsb, out, mm))
         valid = np.clip(x.masked_m, 0, x.m_max)
         mv = int(valid.sum())
-        kb, nb = x.k // 128, (x.n + 127) // 128
+        kb, nb = (x.k // 128 + 3) // 4 if pow2 else x.k // 128, (x.n + 127) // 128  # scale words per row
         nbytes = mv * x.k + mv * kb * 4 + x.g * x.n * x.k + x.g * nb * kb * 4 + x.g * 4 + mv * x.n * 2
 
         def sample(rng, count, x=x, valid=valid):
@@ -345,12 +355,15 @@ def build_masked():
             oracle.grouped_masked_at(x.a, x.sa, x.b, x.sb, x.masked_m, gs, rows, cols)
             return 2.0 * x.k * count
 
-        c = Call(s["name"], 2.0 * mv * x.n * x.k, nbytes, fn, sample, group="masked")
-        c.fn_noalloc = fn_na
+        c = Call(s["name"] + ("_ue8m0" if pow2 else ""), 2.0 * mv * x.n * x.k, nbytes, fn, sample,
+                 group="masked_ue8m0" if pow2 else "masked")
+        if not pow2:
+            c.fn_noalloc = fn_na
         calls.append(c)
-    return calls, {"workload": "masked_sweep", "description":
+    return calls, {"workload": "masked_sweep_ue8m0" if pow2 else "masked_sweep", "description":
                    "MoE masked decode: G in {1,2,4,16}, M_max=256, masked_m ~ U{64..192}, "
-                   "(N,K) in {(4096,7168),(7168,2048)}"}
+                   "(N,K) in {(4096,7168),(7168,2048)}"
+                   + ("; packed UE8M0 scales (four exponent bytes per int32)" if pow2 else "")}
 
 
 def build_wgrad(kgrouped=False):
@@ -755,7 +768,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="all",
                     choices=["all", "dense", "small", "contiguous", "masked", "wgrad", "k_grouped_wgrad", "quantize",
-                             "dense_ue8m0", "bf16", "swiglu_quantize", "contiguous_swiglu"])
+                             "dense_ue8m0", "bf16", "swiglu_quantize", "contiguous_swiglu", "contiguous_ue8m0",
+                             "masked_ue8m0"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold-median", action="store_true", help="skip the cold-cache median of the dominant GEMM")
@@ -779,7 +793,9 @@ def main():
                 "contiguous": build_contiguous, "masked": build_masked,
                 "wgrad": build_wgrad, "k_grouped_wgrad": lambda: build_wgrad(kgrouped=True),
                 "quantize": build_quantize, "dense_ue8m0": lambda: build_dense(pow2=True), "bf16": build_bf16,
-                "swiglu_quantize": build_swiglu, "contiguous_swiglu": build_contiguous_swiglu}
+                "swiglu_quantize": build_swiglu, "contiguous_swiglu": build_contiguous_swiglu,
+                "contiguous_ue8m0": lambda: build_contiguous(pow2=True),
+                "masked_ue8m0": lambda: build_masked(pow2=True)}
     if args.copy_calibration:
         copy_calibration()
         return

@@ -47,11 +47,13 @@ def _pow2_ceil(s: np.ndarray) -> np.ndarray:
 
 
 def pack_ue8m0(s: np.ndarray) -> np.ndarray:
-    """Power-of-two fp32 scales [R, KB] -> packed UE8M0 words int32 [R, ceil(KB/4)]:
+    """Power-of-two fp32 scales [..., KB] -> packed UE8M0 words int32 [..., ceil(KB/4)]:
     the byte of K block 4w+i is byte i of word w (little-endian), and the byte
     is the scale's fp32 exponent field (2^-127 .. 2^127 -> 0 .. 254).  Padding
     bytes past KB hold 255 (the E8M0 NaN code), so reading one shows up."""
     s = np.ascontiguousarray(s, dtype=np.float32)
+    lead = s.shape[:-1]
+    s = s.reshape(-1, s.shape[-1])
     r, kb = s.shape
     m, _ = np.frexp(s.astype(np.float64))
     assert np.all(m == 0.5) and np.all(s > 0), "scales must be positive powers of two"
@@ -59,7 +61,7 @@ def pack_ue8m0(s: np.ndarray) -> np.ndarray:
     kw = (kb + 3) // 4
     raw = np.full((r, 4 * kw), 255, np.uint8)
     raw[:, :kb] = ((s.view(np.uint32) >> 23) & 0xFF).astype(np.uint8)
-    return np.frombuffer(raw.tobytes(), dtype="<i4").reshape(r, kw).astype(np.int32)
+    return np.frombuffer(raw.tobytes(), dtype="<i4").reshape(*lead, kw).astype(np.int32)
 
 
 def quantize_1x128(x: np.ndarray, pow2: bool = False) -> tuple[np.ndarray, np.ndarray]:
@@ -152,13 +154,13 @@ def make_dense_bf16(m: int, n: int, k: int, seed: int) -> DenseBf16:
                      _to_bf16_bits(_normal(_rng(seed, 1), (n, k))))
 
 
-def _grouped_rhs(g: int, n: int, k: int, seed: int) -> tuple[np.ndarray, np.ndarray]:
+def _grouped_rhs(g: int, n: int, k: int, seed: int, pow2: bool = False) -> tuple[np.ndarray, np.ndarray]:
     nb = (n + BLOCK_K - 1) // BLOCK_K
     b = np.empty((g, n, k), dtype=np.uint8)
     sb = np.empty((g, nb, k // BLOCK_K), dtype=np.float32)
     rng = _rng(seed, 1)
     for e in range(g):
-        b[e], sb[e] = quantize_128x128(_normal(rng, (n, k)))
+        b[e], sb[e] = quantize_128x128(_normal(rng, (n, k)), pow2)
     return b, sb
 
 
@@ -183,11 +185,12 @@ class Contiguous:
 
 
 def make_contiguous(g: int, rows_per_expert: int, n: int, k: int, seed: int,
-                    pad: bool = True, max_pad: int = 127) -> Contiguous:
+                    pad: bool = True, max_pad: int = 127, pow2: bool = False) -> Contiguous:
+    """pow2: scales rounded up to powers of two (UE8M0-representable)."""
     assert rows_per_expert % BLOCK_K == 0
     m_total = g * rows_per_expert
-    a, sa = quantize_1x128(_normal(_rng(seed, 0), (m_total, k)))
-    b, sb = _grouped_rhs(g, n, k, seed)
+    a, sa = quantize_1x128(_normal(_rng(seed, 0), (m_total, k)), pow2)
+    b, sb = _grouped_rhs(g, n, k, seed, pow2)
     rng = _rng(seed, 3)
     pads = rng.integers(0, max_pad + 1, size=g) if pad else np.zeros(g, np.int64)
     pads = np.minimum(pads, rows_per_expert)
@@ -214,9 +217,10 @@ class Masked:
 
 
 def make_masked(g: int, m_max: int, n: int, k: int, seed: int,
-                lo: int = 64, hi: int = 192, masked_m=None) -> Masked:
-    a, sa = quantize_1x128(_normal(_rng(seed, 0), (g * m_max, k)))
-    b, sb = _grouped_rhs(g, n, k, seed)
+                lo: int = 64, hi: int = 192, masked_m=None, pow2: bool = False) -> Masked:
+    """pow2: scales rounded up to powers of two (UE8M0-representable)."""
+    a, sa = quantize_1x128(_normal(_rng(seed, 0), (g * m_max, k)), pow2)
+    b, sb = _grouped_rhs(g, n, k, seed, pow2)
     if masked_m is None:
         masked_m = _rng(seed, 4).integers(lo, hi + 1, size=g)
     masked_m = np.asarray(masked_m, dtype=np.int32)

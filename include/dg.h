@@ -175,6 +175,25 @@ dg_status dg_grouped_fp8_masked_noalloc(const void* a, const float* sa, const vo
                                         int num_groups, int m_max, int n, int k,
                                         hipStream_t stream);
 
+/* The two grouped layouts with packed UE8M0 scales (the format of
+ * dg_gemm_fp8_nt_ue8m0_packed: int32 words holding the biased exponents E of
+ * four consecutive 128-wide K blocks, K block 4w + i in byte i; scale
+ * 2^(E - 127), E = 255 NaN; bytes past the last K block ignored), applied
+ * inside the block-scaled MFMA.  Operands, row rules, results and alignment
+ * as dg_grouped_fp8_contiguous / dg_grouped_fp8_masked, with K_w = ceil(K/512):
+ *   contiguous: sa [M_total,K_w] int32, sb [G,ceil(N/128),K_w] int32
+ *   masked:     sa [G,M_max,K_w] int32, sb [G,ceil(N/128),K_w] int32
+ * (the masked call may split K like dg_grouped_fp8_masked, with the same
+ * workspace rules). */
+dg_status dg_grouped_fp8_contiguous_ue8m0_packed(const void* a, const int32_t* sa, const void* b,
+                                                 const int32_t* sb, void* c,
+                                                 const int32_t* m_indices, int m_total, int n,
+                                                 int k, int num_groups, hipStream_t stream);
+dg_status dg_grouped_fp8_masked_ue8m0_packed(const void* a, const int32_t* sa, const void* b,
+                                             const int32_t* sb, void* c,
+                                             const int32_t* masked_m, int num_groups,
+                                             int m_max, int n, int k, hipStream_t stream);
+
 /* Weight-gradient FP8 GEMM with fp32 output accumulated into D (DeepGEMM
  * pages, "反向传播中的梯度计算": dW from FP8 inputs, fp32 result without an
  * explicit cast).  K is the token dimension; both operands are token-
@@ -261,9 +280,11 @@ typedef enum {
   DG_KIND_MASKED = 2,
   DG_KIND_WGRAD = 3,
   DG_KIND_K_GROUPED_WGRAD = 4,
-  DG_KIND_DENSE_POW2 = 5,     /* dg_gemm_fp8_nt_ue8m0 */
+  DG_KIND_DENSE_POW2 = 5,     /* dg_gemm_fp8_nt_ue8m0, dg_gemm_fp8_nt_ue8m0_packed */
   DG_KIND_BF16 = 6,           /* dg_gemm_bf16_nt (k counts bf16 values) */
-  DG_KIND_CONTIGUOUS_SWIGLU = 7 /* dg_grouped_fp8_contiguous_swiglu (n = 2I) */
+  DG_KIND_CONTIGUOUS_SWIGLU = 7, /* dg_grouped_fp8_contiguous_swiglu (n = 2I) */
+  DG_KIND_CONTIGUOUS_POW2 = 8,   /* dg_grouped_fp8_contiguous_ue8m0_packed */
+  DG_KIND_MASKED_POW2 = 9        /* dg_grouped_fp8_masked_ue8m0_packed */
 } dg_kind;
 
 /* Tile configuration the per-shape heuristic picks (DeepGEMM pages: block

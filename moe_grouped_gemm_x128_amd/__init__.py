@@ -38,13 +38,16 @@ _lib.dg_wgrad_fp8_nt.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]
 _lib.dg_k_grouped_wgrad_fp8_nt.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]
 _lib.dg_gemm_fp8_nt_ue8m0.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]
 _lib.dg_gemm_fp8_nt_ue8m0_packed.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]
+_lib.dg_grouped_fp8_contiguous_ue8m0_packed.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]
+_lib.dg_grouped_fp8_masked_ue8m0_packed.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]
 _lib.dg_gemm_bf16_nt.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _vp]
 _lib.dg_quantize_fp8_1x128.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
 _lib.dg_quantize_fp8_128x128.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
 _lib.dg_quantize_fp8_1x128_transposed.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
 _lib.dg_swiglu_quantize_fp8_1x128.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
 for _f in ("dg_gemm_fp8_nt", "dg_grouped_fp8_contiguous", "dg_grouped_fp8_contiguous_swiglu", "dg_grouped_fp8_masked", "dg_grouped_fp8_masked_noalloc",
-           "dg_wgrad_fp8_nt", "dg_k_grouped_wgrad_fp8_nt", "dg_gemm_fp8_nt_ue8m0", "dg_gemm_fp8_nt_ue8m0_packed", "dg_gemm_bf16_nt", "dg_quantize_fp8_1x128",
+           "dg_wgrad_fp8_nt", "dg_k_grouped_wgrad_fp8_nt", "dg_gemm_fp8_nt_ue8m0", "dg_gemm_fp8_nt_ue8m0_packed", "dg_grouped_fp8_contiguous_ue8m0_packed",
+           "dg_grouped_fp8_masked_ue8m0_packed", "dg_gemm_bf16_nt", "dg_quantize_fp8_1x128",
            "dg_quantize_fp8_128x128", "dg_quantize_fp8_1x128_transposed", "dg_swiglu_quantize_fp8_1x128"):
     getattr(_lib, _f).restype = ctypes.c_int
 _lib.dg_status_string.argtypes = [ctypes.c_int]
@@ -62,7 +65,7 @@ _lib.dg_select_config.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, ctypes.POI
 _lib.dg_select_config.restype = ctypes.c_int
 
 (KIND_DENSE, KIND_CONTIGUOUS, KIND_MASKED, KIND_WGRAD, KIND_K_GROUPED_WGRAD, KIND_DENSE_POW2, KIND_BF16,
- KIND_CONTIGUOUS_SWIGLU) = range(8)
+ KIND_CONTIGUOUS_SWIGLU, KIND_CONTIGUOUS_POW2, KIND_MASKED_POW2) = range(10)
 FP8 = torch.float8_e4m3fn
 
 
@@ -203,20 +206,44 @@ def dg_gemm_bf16_nt(a, b, c):
     return c
 
 
+def _scale_cols(sa, sb, k, packed):
+    """Columns of the scale tensors: K/128 fp32 scales, or ceil(K/512) int32
+    words of packed UE8M0 exponents."""
+    if not packed:
+        _f32(sa, "sa"); _f32(sb, "sb")
+        return k // 128
+    for t, name in ((sa, "sa"), (sb, "sb")):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32 (packed UE8M0), got {t.dtype}")
+    return (k // 128 + 3) // 4
+
+
 def dg_grouped_fp8_contiguous(a, sa, b, sb, c, m_indices):
-    _fp8(a, "a"); _fp8(b, "b"); _f32(sa, "sa"); _f32(sb, "sb")
+    return _grouped_contiguous(_lib.dg_grouped_fp8_contiguous, "dg_grouped_fp8_contiguous", False,
+                               a, sa, b, sb, c, m_indices)
+
+
+def dg_grouped_fp8_contiguous_ue8m0_packed(a, sa, b, sb, c, m_indices):
+    """dg_grouped_fp8_contiguous with packed UE8M0 scales (int32 words of four
+    exponent bytes: sa [M_total, ceil(K/512)], sb [G, ceil(N/128), ceil(K/512)])."""
+    return _grouped_contiguous(_lib.dg_grouped_fp8_contiguous_ue8m0_packed,
+                               "dg_grouped_fp8_contiguous_ue8m0_packed", True, a, sa, b, sb, c, m_indices)
+
+
+def _grouped_contiguous(fn, name, packed, a, sa, b, sb, c, m_indices):
+    _fp8(a, "a"); _fp8(b, "b")
     m_total, k = a.shape
     g, n, _ = b.shape
-    _shape(b, (g, n, k), "b"); _shape(sa, (m_total, k // 128), "sa")
-    _shape(sb, (g, (n + 127) // 128, k // 128), "sb"); _shape(c, (m_total, n), "c")
+    kc = _scale_cols(sa, sb, k, packed)
+    _shape(b, (g, n, k), "b"); _shape(sa, (m_total, kc), "sa")
+    _shape(sb, (g, (n + 127) // 128, kc), "sb"); _shape(c, (m_total, n), "c")
     _shape(m_indices, (m_total,), "m_indices")
     if m_indices.dtype != torch.int32:
         raise TypeError("m_indices must be int32")
     if c.dtype != torch.bfloat16:
         raise TypeError("c must be bfloat16")
     _dev(a, sa, b, sb, c, m_indices)
-    _check(_lib.dg_grouped_fp8_contiguous(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(c), _ptr(m_indices),
-                                          m_total, n, k, g, _stream(c)), "dg_grouped_fp8_contiguous")
+    _check(fn(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(c), _ptr(m_indices), m_total, n, k, g, _stream(c)), name)
     return c
 
 
@@ -246,6 +273,13 @@ def dg_grouped_fp8_masked(a, sa, b, sb, c, masked_m):
     return _grouped_masked(_lib.dg_grouped_fp8_masked, "dg_grouped_fp8_masked", a, sa, b, sb, c, masked_m)
 
 
+def dg_grouped_fp8_masked_ue8m0_packed(a, sa, b, sb, c, masked_m):
+    """dg_grouped_fp8_masked with packed UE8M0 scales (int32 words of four
+    exponent bytes: sa [G, M_max, ceil(K/512)], sb [G, ceil(N/128), ceil(K/512)])."""
+    return _grouped_masked(_lib.dg_grouped_fp8_masked_ue8m0_packed, "dg_grouped_fp8_masked_ue8m0_packed",
+                           a, sa, b, sb, c, masked_m, packed=True)
+
+
 def dg_grouped_fp8_masked_noalloc(a, sa, b, sb, c, masked_m):
     """dg_grouped_fp8_masked without any allocation (split-K partials in the
     library's fixed 64 MB scratch; usable under graph capture).  Calls that
@@ -254,12 +288,13 @@ def dg_grouped_fp8_masked_noalloc(a, sa, b, sb, c, masked_m):
                            a, sa, b, sb, c, masked_m)
 
 
-def _grouped_masked(fn, name, a, sa, b, sb, c, masked_m):
-    _fp8(a, "a"); _fp8(b, "b"); _f32(sa, "sa"); _f32(sb, "sb")
+def _grouped_masked(fn, name, a, sa, b, sb, c, masked_m, packed=False):
+    _fp8(a, "a"); _fp8(b, "b")
     g, m_max, k = a.shape
     n = b.shape[1]
-    _shape(b, (g, n, k), "b"); _shape(sa, (g, m_max, k // 128), "sa")
-    _shape(sb, (g, (n + 127) // 128, k // 128), "sb"); _shape(c, (g, m_max, n), "c")
+    kc = _scale_cols(sa, sb, k, packed)
+    _shape(b, (g, n, k), "b"); _shape(sa, (g, m_max, kc), "sa")
+    _shape(sb, (g, (n + 127) // 128, kc), "sb"); _shape(c, (g, m_max, n), "c")
     _shape(masked_m, (g,), "masked_m")
     if masked_m.dtype != torch.int32:
         raise TypeError("masked_m must be int32")
@@ -370,6 +405,9 @@ def gemm_bf16_bf16_bf16_nt(lhs, rhs, out):
 
 
 def m_grouped_gemm_fp8_fp8_bf16_nt_contiguous(lhs, rhs, out, m_indices):
+    """fp32 scales, or packed UE8M0 (int32 words)."""
+    if lhs[1].dtype == torch.int32:
+        return dg_grouped_fp8_contiguous_ue8m0_packed(lhs[0], lhs[1], rhs[0], rhs[1], out, m_indices)
     return dg_grouped_fp8_contiguous(lhs[0], lhs[1], rhs[0], rhs[1], out, m_indices)
 
 
@@ -386,6 +424,9 @@ def m_grouped_gemm_fp8_fp8_fp8_nt_contiguous_swiglu(lhs, rhs, m_indices):
 
 
 def m_grouped_gemm_fp8_fp8_bf16_nt_masked(lhs, rhs, out, masked_m):
+    """fp32 scales, or packed UE8M0 (int32 words)."""
+    if lhs[1].dtype == torch.int32:
+        return dg_grouped_fp8_masked_ue8m0_packed(lhs[0], lhs[1], rhs[0], rhs[1], out, masked_m)
     return dg_grouped_fp8_masked(lhs[0], lhs[1], rhs[0], rhs[1], out, masked_m)
 
 

@@ -82,10 +82,10 @@ constexpr int kMaskedSplitMinBlocks = 6;
 constexpr size_t kMaxWorkspaceBytes = size_t(256) << 20;  // split-K partials per call
 
 int choose_splits(int kind, int rows, long tiles, int num_cus, int kbs) {
-  if (kind != DG_KIND_DENSE && kind != DG_KIND_MASKED && !dense_like(kind)) return 1;
+  const bool masked = dg::layout_of(kind) == DG_KIND_MASKED;
+  if (!masked && !dense_like(kind)) return 1;
   if (rows > 256) return 1;  // large M: the extra pass costs more than the idle CUs (measured)
   if (tiles * 10 >= num_cus * 7L) return 1;  // enough tiles already
-  const bool masked = kind == DG_KIND_MASKED;
   if (masked && kbs < 3 * kSplitMinBlocks) return 1;  // short K: the reduction pass costs more (measured)
   const long target = masked ? kMaskedSplitTarget : kSplitTarget;
   const long most = kbs / (masked ? kMaskedSplitMinBlocks : kSplitMinBlocks);
@@ -121,7 +121,8 @@ dg::TileShape heuristic(int kind, int rows, int n, int k, int groups, int num_cu
   if (kind == DG_KIND_CONTIGUOUS_SWIGLU) return dg::TileShape{256, 256, 1, 8};
   const int kbs = k / 128;
   const bool long_k = allow_split && kbs >= 3 * kSplitMinBlocks;
-  if (kind == DG_KIND_MASKED && rows <= 256) {
+  const int layout = dg::layout_of(kind);  // the power-of-two kinds plan as their fp32-scale kind
+  if (layout == DG_KIND_MASKED && rows <= 256) {
     // 256 columns on 2x4 waves: 3-4% faster than 1x8 for 16 groups (cold)
     const dg::TileShape tall256{256, 256, 2, 4}, tall128{256, 128, 1, 4}, tall64{256, 64, 1, 4};
     const dg::TileShape tall32{256, 32, 4, 1};
@@ -136,7 +137,7 @@ dg::TileShape heuristic(int kind, int rows, int n, int k, int groups, int num_cu
     if ((long)groups * ceil_div(n, 32) <= num_cus) return tall32;
     return cols128 * 4 >= 3L * num_cus ? tall128 : tall64;
   }
-  if (rows <= 128 || kind == DG_KIND_MASKED) {
+  if (rows <= 128 || layout == DG_KIND_MASKED) {
     const int bm = rows <= 64 ? 64 : 128;
     const dg::TileShape wide = bm == 64 ? dg::TileShape{64, 128, 1, 4} : dg::TileShape{128, 128, 2, 2};
     const dg::TileShape mid = bm == 64 ? dg::TileShape{64, 64, 1, 4} : dg::TileShape{128, 64, 2, 2};
@@ -203,7 +204,7 @@ dg_status plan(int kind, int rows, int n, int k, int groups, int num_cus, bool a
   const int kbs = k / 128;
   int splits = allow_split ? choose_splits(kind, rows, tiles, num_cus, kbs) : 1;
   if (const char* e = std::getenv("DG_FORCE_SPLITS"))
-    if (allow_split && (dense_like(kind) || kind == DG_KIND_MASKED))
+    if (allow_split && (dense_like(kind) || dg::layout_of(kind) == DG_KIND_MASKED))
       splits = std::atoi(e);
   if (splits < 1) splits = 1;
   if (splits > kMaxSplits) splits = kMaxSplits;
@@ -344,7 +345,7 @@ dg_status run(int kind, dg::Params& p, int rows, int n, int k, int groups, hipSt
   if (device_cus(&cus) != 0) return DG_ERROR_LAUNCH;
   (void)hipGetLastError();  // clear a stale error from unrelated work
   if (p.sks == 0) p.sks = p.kbs;  // one fp32 scale per K block unless packed
-  const bool splittable = dense_like(kind) || kind == DG_KIND_MASKED;
+  const bool splittable = dense_like(kind) || dg::layout_of(kind) == DG_KIND_MASKED;
   const bool may_split = splittable && (scratch != nullptr || !stream_capturing(stream));
   Launch l;
   dg_status st = plan(kind, rows, n, k, groups, cus, may_split, p, l);
@@ -539,6 +540,60 @@ dg_status dg_grouped_fp8_contiguous(const void* a, const float* sa, const void* 
   return run(dg::KIND_CONTIGUOUS, p, m_total, n, k, 1, stream);
 }
 
+dg_status dg_grouped_fp8_contiguous_ue8m0_packed(const void* a, const int32_t* sa, const void* b, const int32_t* sb,
+                                                 void* c, const int32_t* m_indices, int m_total, int n, int k,
+                                                 int num_groups, hipStream_t stream) {
+  if (!a || !sa || !b || !sb || !c || !m_indices) return DG_ERROR_INVALID_VALUE;
+  if (m_total <= 0 || n <= 0 || k <= 0 || num_groups <= 0) return DG_ERROR_INVALID_VALUE;
+  if (k % 128 != 0 || m_total % 128 != 0) return DG_ERROR_UNSUPPORTED;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(sa, 4) || !aligned(sb, 4) || !aligned(c, 2) ||
+      !aligned(m_indices, 4))
+    return DG_ERROR_UNSUPPORTED;
+  dg::Params p = base_params();
+  p.a = static_cast<const uint8_t*>(a);
+  p.sa = reinterpret_cast<const float*>(sa);  // the kernel copies the words and reads their bytes
+  p.b = static_cast<const uint8_t*>(b);
+  p.sb = reinterpret_cast<const float*>(sb);
+  p.out = c;
+  p.ctrl = m_indices;
+  p.m = m_total;
+  p.n = n;
+  p.lda = k;
+  p.kbs = k / 128;
+  p.sks = (p.kbs + 3) / 4;
+  p.spk = 2;
+  p.groups = num_groups;
+  p.vec_out = (n % 4 == 0) && aligned(c, 8);
+  return run(dg::KIND_CONTIG_POW2, p, m_total, n, k, 1, stream);
+}
+
+dg_status dg_grouped_fp8_masked_ue8m0_packed(const void* a, const int32_t* sa, const void* b, const int32_t* sb,
+                                             void* c, const int32_t* masked_m, int num_groups, int m_max, int n,
+                                             int k, hipStream_t stream) {
+  if (!a || !sa || !b || !sb || !c || !masked_m) return DG_ERROR_INVALID_VALUE;
+  if (num_groups <= 0 || m_max <= 0 || n <= 0 || k <= 0) return DG_ERROR_INVALID_VALUE;
+  if (k % 128 != 0) return DG_ERROR_UNSUPPORTED;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(sa, 4) || !aligned(sb, 4) || !aligned(c, 2) ||
+      !aligned(masked_m, 4))
+    return DG_ERROR_UNSUPPORTED;
+  dg::Params p = base_params();
+  p.a = static_cast<const uint8_t*>(a);
+  p.sa = reinterpret_cast<const float*>(sa);
+  p.b = static_cast<const uint8_t*>(b);
+  p.sb = reinterpret_cast<const float*>(sb);
+  p.out = c;
+  p.ctrl = masked_m;
+  p.m = m_max;
+  p.n = n;
+  p.lda = k;
+  p.kbs = k / 128;
+  p.sks = (p.kbs + 3) / 4;
+  p.spk = 2;
+  p.groups = num_groups;
+  p.vec_out = (n % 4 == 0) && aligned(c, 8);
+  return run(dg::KIND_MASKED_POW2, p, m_max, n, k, num_groups, stream);
+}
+
 dg_status dg_grouped_fp8_contiguous_swiglu(const void* a, const float* sa, const void* b, const float* sb,
                                            void* q, float* s, const int32_t* m_indices, int m_total, int n, int k,
                                            int num_groups, hipStream_t stream) {
@@ -645,13 +700,14 @@ const char* dg_status_string(dg_status s) {
 dg_status dg_select_config(int kind, int m, int n, int k, int num_groups, int num_cus,
                            dg_tile_config* out) {
   if (!out) return DG_ERROR_INVALID_VALUE;
-  if (kind < DG_KIND_DENSE || kind > DG_KIND_CONTIGUOUS_SWIGLU) return DG_ERROR_INVALID_VALUE;
+  if (kind < DG_KIND_DENSE || kind > DG_KIND_MASKED_POW2) return DG_ERROR_INVALID_VALUE;
   if (kind == DG_KIND_CONTIGUOUS_SWIGLU && (n % 256 != 0 || m % 128 != 0)) return DG_ERROR_UNSUPPORTED;
   if (m <= 0 || n <= 0 || k <= 0 || num_groups <= 0 || num_cus <= 0) return DG_ERROR_INVALID_VALUE;
   if (kind == DG_KIND_BF16 && k > (1 << 22)) return DG_ERROR_UNSUPPORTED;
   dg::Params p = base_params();
   Launch l;
-  const int groups = (kind == DG_KIND_MASKED || kind == DG_KIND_K_GROUPED_WGRAD) ? num_groups : 1;
+  const int groups =
+      (dg::layout_of(kind) == DG_KIND_MASKED || kind == DG_KIND_K_GROUPED_WGRAD) ? num_groups : 1;
   // the planner counts K in 128-byte blocks: BF16 rows are 2K bytes long
   dg_status st = plan(kind, m, n, kind == DG_KIND_BF16 ? 2 * k : k, groups, num_cus, true, p, l);
   if (st != DG_SUCCESS) return st;

@@ -22,7 +22,21 @@ enum Kind : int {
   KIND_CONTIG_SWIGLU = 7,  // contiguous layout with B [G,2I,K] (gate rows, then up rows); the
                            // epilogue applies SwiGLU to the bf16-rounded pair and writes
                            // fp8 q [M_tot,I] with 1x128 scales [M_tot,I/128] (out, out_scale)
+  KIND_CONTIG_POW2 = 8,    // KIND_CONTIGUOUS with power-of-two scales applied by the block-scaled MFMA
+  KIND_MASKED_POW2 = 9,    // KIND_MASKED with power-of-two scales applied by the block-scaled MFMA
 };
+
+// The operand layout and scheduling of a kind (the power-of-two kinds share
+// their fp32-scale kind's).
+constexpr int layout_of(int kind) {
+  return kind == KIND_DENSE_POW2    ? KIND_DENSE
+         : kind == KIND_CONTIG_POW2 ? KIND_CONTIGUOUS
+         : kind == KIND_MASKED_POW2 ? KIND_MASKED
+                                    : kind;
+}
+constexpr bool pow2_kind(int kind) {
+  return kind == KIND_DENSE_POW2 || kind == KIND_CONTIG_POW2 || kind == KIND_MASKED_POW2;
+}
 
 constexpr int kMaxKGroups = 256;
 

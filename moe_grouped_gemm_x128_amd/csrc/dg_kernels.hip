@@ -211,14 +211,15 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   constexpr int FM = WTM / 16;   // 16-row fragments per wave
   constexpr int FN = WTN / 16;   // 16-column fragments per wave
   constexpr bool kRowScaleB = (KIND == KIND_WGRAD || KIND == KIND_KGROUPED);
-  constexpr bool kPow2 = (KIND == KIND_DENSE_POW2);  // scales applied by the MFMA
+  constexpr int LAYOUT = layout_of(KIND);            // dense, contiguous or masked scheduling
+  constexpr bool kPow2 = pow2_kind(KIND);             // scales applied by the MFMA
   constexpr bool kBf16 = (KIND == KIND_BF16);         // no scales at all
   // contiguous layout with the SwiGLU + re-quantise epilogue: the tile's B
   // rows are 128 gate rows and the 128 matching up rows, in LDS order
   // [wave][gate 16 | up 16], so fragment 0 of a wave holds the gate and
   // fragment 1 the up value of the same output element in the same lane
   constexpr bool kSwiGLU = (KIND == KIND_CONTIG_SWIGLU);
-  constexpr bool kContig = (KIND == KIND_CONTIGUOUS) || kSwiGLU;
+  constexpr bool kContig = (LAYOUT == KIND_CONTIGUOUS) || kSwiGLU;
   static_assert(!kSwiGLU || (BM == 256 && BN == 256 && WM == 1 && WN == 8), "fused SwiGLU tile");
   // B loaded with the streaming (nontemporal) cache policy by the instances
   // whose launches read each B tile with one row of tiles: the dense tiles of
@@ -229,7 +230,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   // contiguous -4%).  Decided per instance at compile time: a runtime choice
   // in the DMA loop cost the 256x256 instances registers (spills in the loop).
   constexpr bool kStreamB =
-      ((KIND == KIND_DENSE || KIND == KIND_DENSE_POW2 || kBf16) && BM <= 128) || KIND == KIND_MASKED;
+      ((LAYOUT == KIND_DENSE || kBf16) && BM <= 128) || LAYOUT == KIND_MASKED;
   constexpr bool kDirectAcc = kPow2 || kBf16;         // MFMAs accumulate into acc: no promotion
   constexpr bool kFp32Out = kRowScaleB;
   // the columns of one wave tile sit inside one 128-block: one sb per wave
@@ -239,7 +240,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   // valid rows skips those row fragments (no LDS read, no MFMA; their zero
   // partials keep the promotion rotation unchanged), so one tile can cover
   // every row of a group and B is streamed once per group.
-  constexpr bool kSkipRows = (KIND == KIND_MASKED) && kStreamM && (FM > 4) && (FM % 4 == 0) && (FM <= 16);
+  constexpr bool kSkipRows = (LAYOUT == KIND_MASKED) && kStreamM && (FM > 4) && (FM % 4 == 0) && (FM <= 16);
   static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile is a multiple of 16");
   static_assert(S >= 2, "at least double buffering");
 
@@ -288,7 +289,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
 
   // ---- tile count (masked: from masked_m on the device, no host sync) ----
   int T = p.tiles;
-  if constexpr (KIND == KIND_MASKED) {
+  if constexpr (LAYOUT == KIND_MASKED) {
     T = 0;
     for (int g = 0; g < p.groups; ++g) {
       const int v = min(max(p.ctrl[g], 0), p.m);
@@ -296,7 +297,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     }
   }
   // split-K: `splits` consecutive work items share one output tile
-  constexpr bool kCanSplit = (KIND == KIND_DENSE || KIND == KIND_MASKED || KIND == KIND_DENSE_POW2 || kBf16);
+  constexpr bool kCanSplit = (LAYOUT == KIND_DENSE || LAYOUT == KIND_MASKED || kBf16);
   const int splits = kCanSplit ? p.splits : 1;
   const int TS = T * splits;
   const int per_xcd = (TS + 7) >> 3;
@@ -323,7 +324,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     const int L = splits > 1 ? LS / splits : LS;
     x.split = LS - L * splits;
     int kb1 = p.kbs;
-    if constexpr (KIND == KIND_MASKED) {
+    if constexpr (LAYOUT == KIND_MASKED) {
       int rem = L, mt = 0, v = 0, g = 0;
       for (; g < p.groups; ++g) {
         v = min(max(p.ctrl[g], 0), p.m);
@@ -1110,6 +1111,12 @@ hipError_t launch_shape(int kind, const Params& p, int grid, hipStream_t stream)
     case KIND_CONTIG_SWIGLU:
       launch_kind<BM, BN, WM, WN, S, KIND_CONTIG_SWIGLU>(g, b, stream, p);
       break;
+    case KIND_CONTIG_POW2:
+      launch_kind<BM, BN, WM, WN, S, KIND_CONTIG_POW2>(g, b, stream, p);
+      break;
+    case KIND_MASKED_POW2:
+      launch_kind<BM, BN, WM, WN, S, KIND_MASKED_POW2>(g, b, stream, p);
+      break;
     default:
       return hipErrorInvalidValue;
   }
@@ -1157,12 +1164,12 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const Params p, int 
 }  // namespace
 
 hipError_t launch_splitk_reduce(int kind, const Params& p, hipStream_t stream) {
-  if (kind != KIND_DENSE && kind != KIND_MASKED && kind != KIND_DENSE_POW2 && kind != KIND_BF16)
-    return hipErrorInvalidValue;
+  const int layout = layout_of(kind);
+  if (layout != KIND_DENSE && layout != KIND_MASKED && kind != KIND_BF16) return hipErrorInvalidValue;
   const int64_t items = (int64_t)p.groups * p.m * ((p.n + 3) / 4);
   const int64_t blocks = (items + 255) / 256;
   const int grid = (int)(blocks < 4096 ? (blocks > 0 ? blocks : 1) : 4096);
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid), dim3(256), 0, stream, p, kind == KIND_MASKED ? 1 : 0);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid), dim3(256), 0, stream, p, layout == KIND_MASKED ? 1 : 0);
   return hipGetLastError();
 }
 

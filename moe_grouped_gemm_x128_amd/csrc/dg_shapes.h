@@ -35,11 +35,13 @@ constexpr int kBlockK = 128;  // K block = scale granularity
 // the tile's 128 output columns are exactly one 1x128 scale group.
 constexpr bool excluded(int bm, int bn, int wm, int kind) {
   if (kind == KIND_CONTIG_SWIGLU) return !(bm == 256 && bn == 256 && wm == 1);
+  // the power-of-two kinds have their fp32-scale kind's instances
+  kind = layout_of(kind);
   // 192-row tiles: dense layouts only (a grouped layout's 128-row blocks would
   // straddle them); 224-row tiles: the weight gradient only (7168 = 32 x 224
   // rows of D, so 7168 x 2048 is 256 tiles of 224 x 256 on 256 CUs: 5% faster
   // warm, equal cold; the K-grouped kind's four D were 9% slower cold with it)
-  if (bm == 192) return !(kind == KIND_DENSE || kind == KIND_DENSE_POW2 || kind == KIND_BF16);
+  if (bm == 192) return !(kind == KIND_DENSE || kind == KIND_BF16);
   if (bm == 224) return kind != KIND_WGRAD;
   return bm == 256 && bn == 256 && wm == 2 && (kind == KIND_WGRAD || kind == KIND_KGROUPED);
 }

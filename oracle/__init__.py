@@ -161,14 +161,16 @@ def unpack_ue8m0(words, kblocks: int) -> np.ndarray:
     NaN.  Bytes past `kblocks` are padding and ignored.  Every 2^(E - 127) for
     E <= 254 is an fp32 value (2^-127 a subnormal), so the result is exact.
     """
-    w = np.ascontiguousarray(words).astype(np.int64) & 0xFFFFFFFF
+    words = np.asarray(words)
+    lead = words.shape[:-1]
+    w = np.ascontiguousarray(words).reshape(-1, words.shape[-1]).astype(np.int64) & 0xFFFFFFFF
     r, kw = w.shape
     assert 4 * kw >= kblocks, "too few words for the K blocks"
     out = np.empty((r, kblocks), np.float64)
     for kb in range(kblocks):
         e = (w[:, kb // 4] >> (8 * (kb % 4))) & 0xFF
         out[:, kb] = np.where(e == 255, np.nan, np.ldexp(1.0, (e - 127).astype(np.int32)))
-    return out.astype(np.float32)
+    return out.astype(np.float32).reshape(*lead, kblocks)
 
 
 def gemm_fp8_nt_ue8m0_packed(a, sa_words, b, sb_words):
@@ -176,6 +178,18 @@ def gemm_fp8_nt_ue8m0_packed(a, sa_words, b, sb_words):
     dense oracle (the packed format only encodes power-of-two fp32 scales)."""
     kb = np.asarray(a).shape[1] // 128
     return gemm_fp8_nt(a, unpack_ue8m0(sa_words, kb), b, unpack_ue8m0(sb_words, kb))
+
+
+def grouped_contiguous_ue8m0_packed(a, sa_words, b, sb_words, m_indices, c_init):
+    """Contiguous MoE with packed UE8M0 scales: unpacked, then grouped_contiguous."""
+    kb = np.asarray(a).shape[1] // 128
+    return grouped_contiguous(a, unpack_ue8m0(sa_words, kb), b, unpack_ue8m0(sb_words, kb), m_indices, c_init)
+
+
+def grouped_masked_ue8m0_packed(a, sa_words, b, sb_words, masked_m, c_init):
+    """Masked MoE with packed UE8M0 scales: unpacked, then grouped_masked."""
+    kb = np.asarray(a).shape[2] // 128
+    return grouped_masked(a, unpack_ue8m0(sa_words, kb), b, unpack_ue8m0(sb_words, kb), masked_m, c_init)
 
 
 def grouped_contiguous(a, sa, b, sb, m_indices, c_init):

@@ -23,7 +23,7 @@ int main(void) {
   const int ks[] = {128, 512, 2048, 4608, 7168, 16384, 1 << 20};
   const int gs[] = {1, 2, 4, 16, 256};
   long plans = 0;
-  for (int kind = 0; kind <= 7; ++kind)
+  for (int kind = 0; kind <= 9; ++kind)
     for (unsigned a = 0; a < sizeof(ms) / sizeof(ms[0]); ++a)
       for (unsigned b = 0; b < sizeof(ns) / sizeof(ns[0]); ++b)
         for (unsigned c = 0; c < sizeof(ks) / sizeof(ks[0]); ++c)
@@ -44,7 +44,7 @@ int main(void) {
   CHECK(plans > 1000);
   /* rejected queries */
   dg_tile_config cfg;
-  CHECK(dg_select_config(8, 128, 128, 128, 1, 256, &cfg) == DG_ERROR_INVALID_VALUE);
+  CHECK(dg_select_config(10, 128, 128, 128, 1, 256, &cfg) == DG_ERROR_INVALID_VALUE);
   CHECK(dg_select_config(7, 128, 384, 128, 1, 256, &cfg) == DG_ERROR_UNSUPPORTED);
   CHECK(dg_select_config(0, 0, 128, 128, 1, 256, &cfg) == DG_ERROR_INVALID_VALUE);
   CHECK(dg_select_config(0, 128, 128, 128, 1, 256, NULL) == DG_ERROR_INVALID_VALUE);
@@ -64,6 +64,10 @@ int main(void) {
   CHECK(dg_grouped_fp8_contiguous_swiglu(p, f, p, f, p, NULL, (const int32_t*)p, 128, 512, 128, 2, NULL) ==
         DG_ERROR_INVALID_VALUE);
   CHECK(dg_grouped_fp8_masked(p, f, p, f, p, (const int32_t*)p, 0, 256, 8, 128, NULL) == DG_ERROR_INVALID_VALUE);
+  const int32_t* w = (const int32_t*)p;
+  CHECK(dg_gemm_fp8_nt_ue8m0_packed(p, w, p, w, p, 1, 1, 100, NULL) == DG_ERROR_UNSUPPORTED);
+  CHECK(dg_grouped_fp8_contiguous_ue8m0_packed(p, w, p, w, p, NULL, 128, 8, 128, 2, NULL) == DG_ERROR_INVALID_VALUE);
+  CHECK(dg_grouped_fp8_masked_ue8m0_packed(p, w, p, w, p, w, 2, 256, 8, 200, NULL) == DG_ERROR_UNSUPPORTED);
   CHECK(dg_grouped_fp8_masked_noalloc(p, f, p, f, p, NULL, 2, 256, 8, 128, NULL) == DG_ERROR_INVALID_VALUE);
   CHECK(dg_grouped_fp8_masked_noalloc(p, f, p, f, p, (const int32_t*)p, 2, 256, 8, 200, NULL) == DG_ERROR_UNSUPPORTED);
   CHECK(dg_wgrad_fp8_nt(p, f, p, f, (float*)p, 8, 8, 0, NULL) == DG_ERROR_INVALID_VALUE);

@@ -164,6 +164,22 @@ def test_ue8m0_packed_argument_errors(lib):
     assert f(A16, A16, A16 + 8, A16, A16, 1, 1, 128, None) == UNSUPPORTED    # b alignment
 
 
+def test_grouped_ue8m0_packed_argument_errors(lib):
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    fc = lib.dg_grouped_fp8_contiguous_ue8m0_packed
+    fc.argtypes = [vp] * 6 + [i] * 4 + [vp]
+    assert fc(A16, A16, A16, A16, A16, None, 256, 512, 128, 2, None) == INVALID   # m_indices
+    assert fc(A16, A16, A16, A16, A16, A16, 256, 512, 128, 0, None) == INVALID    # G
+    assert fc(A16, A16, A16, A16, A16, A16, 200, 512, 128, 2, None) == UNSUPPORTED  # M_total % 128
+    assert fc(A16, A16 + 2, A16, A16, A16, A16, 256, 512, 128, 2, None) == UNSUPPORTED
+    fm = lib.dg_grouped_fp8_masked_ue8m0_packed
+    fm.argtypes = [vp] * 6 + [i] * 4 + [vp]
+    assert fm(A16, A16, A16, A16, A16, None, 2, 256, 512, 128, None) == INVALID    # masked_m
+    assert fm(A16, A16, A16, A16, A16, A16, 2, 0, 512, 128, None) == INVALID       # M_max
+    assert fm(A16, A16, A16, A16, A16, A16, 2, 256, 512, 200, None) == UNSUPPORTED  # K % 128
+    assert fm(A16, A16, A16, A16 + 1, A16, A16, 2, 256, 512, 128, None) == UNSUPPORTED
+
+
 def test_quantizer_argument_errors(lib):
     vp, i = ctypes.c_void_p, ctypes.c_int
     for name in ("dg_quantize_fp8_1x128", "dg_quantize_fp8_128x128", "dg_quantize_fp8_1x128_transposed"):
@@ -239,6 +255,7 @@ SHAPES = [(0, m, n, k, 1) for m in (1, 64, 128, 4096)
 SHAPES += [(1, 32768, 4096, 7168, 4), (1, 65536, 7168, 2048, 8), (2, 256, 4096, 7168, 1),
            (2, 256, 7168, 2048, 16), (3, 7168, 2048, 4096, 1), (4, 7168, 2048, 10240, 4)]
 SHAPES += [(5, m, 7168, 16384, 1) for m in (64, 4096)] + [(6, m, 7168, 8192, 1) for m in (64, 4096)]
+SHAPES += [(8, 32768, 4096, 7168, 4), (9, 256, 4096, 7168, 1), (9, 256, 7168, 2048, 16)]
 
 
 @pytest.mark.parametrize("kind,m,n,k,g", SHAPES)
@@ -246,12 +263,12 @@ def test_heuristic_invariants(lib, kind, m, n, k, g):
     c = _cfg(lib, kind, m, n, k, g)
     assert c["waves_m"] * c["waves_n"] in (4, 8)
     assert c["block_m"] % (16 * c["waves_m"]) == 0 and c["block_n"] % (16 * c["waves_n"]) == 0
-    groups = g if kind in (2, 4) else 1
+    groups = g if kind in (2, 4, 9) else 1
     tiles = groups * -(-m // c["block_m"]) * -(-n // c["block_n"])
     assert c["tiles"] == tiles
     s = c["k_splits"]
     assert 1 <= s <= 16
-    if kind not in (0, 2, 5, 6):
+    if kind not in (0, 2, 5, 6, 9):
         assert s == 1  # split K only for the bf16-output dense and masked layouts
     kbs = k // 64 if kind == 6 else k // 128  # BF16: K blocks of 64 values (128 bytes)
     if s > 1:
@@ -288,6 +305,14 @@ def test_masked_plan(lib):
     assert (c["block_m"], c["block_n"], c["k_splits"]) == (256, 32, 1)
 
 
+def test_power_of_two_kinds_plan_as_their_layout(lib):
+    """The packed-UE8M0 grouped kinds take their fp32-scale kind's plan."""
+    for (kind, base, m, n, k, g) in [(8, 1, 65536, 4096, 7168, 8), (8, 1, 32768, 7168, 2048, 4),
+                                     (9, 2, 256, 4096, 7168, 1), (9, 2, 256, 4096, 7168, 16),
+                                     (9, 2, 256, 7168, 2048, 4), (5, 0, 64, 2112, 7168, 1)]:
+        assert _cfg(lib, kind, m, n, k, g) == _cfg(lib, base, m, n, k, g), (kind, m, n, k, g)
+
+
 def test_split_k_planning(lib):
     """Few output tiles and a long K: split K to give every CU work; many
     tiles: no split."""
@@ -304,8 +329,7 @@ def test_heuristic_rejects_bad_queries(lib):
     c = ctypes.c_int * 8
     out = c()
     lib.dg_select_config.argtypes = [ctypes.c_int] * 6 + [ctypes.c_void_p]
-    assert lib.dg_select_config(9, 1, 1, 128, 1, 256, ctypes.addressof(out)) == INVALID
-    assert lib.dg_select_config(8, 1, 1, 128, 1, 256, ctypes.addressof(out)) == INVALID
+    assert lib.dg_select_config(10, 1, 1, 128, 1, 256, ctypes.addressof(out)) == INVALID
     assert lib.dg_select_config(-1, 1, 1, 128, 1, 256, ctypes.addressof(out)) == INVALID
     # the fused SwiGLU kind needs N % 256 == 0 and M % 128 == 0
     assert lib.dg_select_config(7, 128, 384, 128, 1, 256, ctypes.addressof(out)) == UNSUPPORTED

@@ -116,3 +116,23 @@ def test_planted_mistakes_fail_a_pin(mutant):
     bad = _mutant(**mutant)
     assert not all(pin(bad) for pin in PINS), f"no pin catches {mutant}"
     assert all(pin(_mutant()) for pin in PINS), "the unmutated rewrite must pass every pin"
+
+
+def test_grouped_packed_oracles_are_the_grouped_oracles():
+    """Scales of any rank unpack along their last axis; the grouped packed
+    oracles are the grouped oracles on the unpacked scales."""
+    from tests.parity import SENTINEL_BF16
+    x = inputs.make_contiguous(3, 256, 140, 640, seed=inputs.SEED_BASE + 66, pow2=True)
+    assert inputs.pack_ue8m0(x.sb).shape == (3, 2, 2)
+    assert np.array_equal(oracle.unpack_ue8m0(inputs.pack_ue8m0(x.sb), 5), x.sb)
+    init = np.full((x.m_total, x.n), SENTINEL_BF16, np.uint16)
+    got = oracle.grouped_contiguous_ue8m0_packed(x.a, inputs.pack_ue8m0(x.sa), x.b, inputs.pack_ue8m0(x.sb),
+                                                 x.m_indices, init)
+    want = oracle.grouped_contiguous(x.a, x.sa, x.b, x.sb, x.m_indices, init)
+    assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1], equal_nan=True)
+    mm = np.array([0, 5, 70], np.int32)
+    y = inputs.make_masked(3, 70, 140, 640, seed=inputs.SEED_BASE + 67, masked_m=mm, pow2=True)
+    init = np.full((3, 70, 140), SENTINEL_BF16, np.uint16)
+    got = oracle.grouped_masked_ue8m0_packed(y.a, inputs.pack_ue8m0(y.sa), y.b, inputs.pack_ue8m0(y.sb), mm, init)
+    want = oracle.grouped_masked(y.a, y.sa, y.b, y.sb, mm, init)
+    assert np.array_equal(got[0], want[0])
