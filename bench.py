@@ -468,7 +468,8 @@ def build_quantize():
     gen.manual_seed(inputs.SEED_BASE + 5)
     specs = [("quant_1x128_m65536_k7168", 0, 65536, 7168), ("quant_1x128_m4096_k7168", 0, 4096, 7168),
              ("quant_128x128_n7168_k16384", 1, 7168, 16384), ("quant_1x128T_t4096_f7168", 2, 4096, 7168),
-             ("quant_1x128T_t4096_f2048", 2, 4096, 2048)]
+             ("quant_1x128T_t4096_f2048", 2, 4096, 2048), ("quant_1x128_ue8m0_m65536_k7168", 3, 65536, 7168),
+             ("quant_128x128_ue8m0_n7168_k16384", 4, 7168, 16384)]
     calls = []
     for name, mode, r, c in specs:
         x = torch.randn((r, c), generator=gen, device="cuda", dtype=torch.float32)
@@ -480,10 +481,18 @@ def build_quantize():
             q = torch.empty((r, c), dtype=torch.uint8, device="cuda")
             sc = torch.empty(((r + 127) // 128, c // 128), dtype=torch.float32, device="cuda")
             fn = lambda x=x, q=q, sc=sc: dg.dg_quantize_fp8_128x128(x, q, sc)
-        else:
+        elif mode == 2:
             q = torch.empty((c, r), dtype=torch.uint8, device="cuda")
             sc = torch.empty((c, r // 128), dtype=torch.float32, device="cuda")
             fn = lambda x=x, q=q, sc=sc: dg.dg_quantize_fp8_1x128_transposed(x, q, sc)
+        elif mode == 3:  # power-of-two scales, packed UE8M0 words
+            q = torch.empty((r, c), dtype=torch.uint8, device="cuda")
+            sc = torch.empty((r, (c // 128 + 3) // 4), dtype=torch.int32, device="cuda")
+            fn = lambda x=x, q=q, sc=sc: dg.dg_quantize_fp8_1x128_ue8m0(x, q, sc)
+        else:
+            q = torch.empty((r, c), dtype=torch.uint8, device="cuda")
+            sc = torch.empty(((r + 127) // 128, (c // 128 + 3) // 4), dtype=torch.int32, device="cuda")
+            fn = lambda x=x, q=q, sc=sc: dg.dg_quantize_fp8_128x128_ue8m0(x, q, sc)
         nbytes = r * c * 5 + sc.numel() * 4
 
         def sample(rng, rows, x=x, mode=mode, c=c):
@@ -492,15 +501,17 @@ def build_quantize():
             import oracle
             rows = min(rows, x.shape[0])
             h = x[:rows].cpu().numpy()
-            f = (oracle.quantize_1x128, oracle.quantize_128x128, oracle.quantize_1x128_transposed)[mode]
+            f = (oracle.quantize_1x128, oracle.quantize_128x128, oracle.quantize_1x128_transposed,
+                 oracle.quantize_1x128_ue8m0, oracle.quantize_128x128_ue8m0)[mode]
             f(h)
             return rows * c * 5
 
         calls.append(Call(name, 0.0, nbytes, fn, (sample, c), group="quantize"))
     return calls, {"workload": "quantize", "description":
                    "FP8 quantiser: 1x128 activations [65536,7168] and [4096,7168], 128x128 weights "
-                   "[7168,16384], token-contiguous 1x128 transposed [4096,7168] and [4096,2048]",
-                   "scales": "absmax/448 fp32", "in": "fp32", "out": "e4m3"}
+                   "[7168,16384], token-contiguous 1x128 transposed [4096,7168] and [4096,2048]; "
+                   "the first and third with power-of-two scales in packed UE8M0 words",
+                   "scales": "absmax/448 fp32 (packed UE8M0: the next power of two)", "in": "fp32", "out": "e4m3"}
 
 
 SWIGLU_METRIC = "SwiGLU + FP8 1x128 re-quantise GB/s (bf16 in, e4m3 + fp32 scales out) and % of MI355X HBM peak"

@@ -240,6 +240,22 @@ dg_status dg_quantize_fp8_1x128(const float* x, void* q, float* s, int m, int k,
 dg_status dg_quantize_fp8_128x128(const float* x, void* q, float* s, int n, int k,
                                   hipStream_t stream);
 
+/* Both rules with power-of-two scales in the packed UE8M0 format that the
+ * *_ue8m0_packed GEMMs take (DeepGEMM pages, aikraft.ru support table: packed
+ * UE8M0, four values in one torch.int).  The pages give no rule for choosing
+ * such a scale; taken: the smallest 2^(E - 127), E in [0, 254], not below the
+ * fp32 rule's s = amax / 448 (1 for an all-zero group), so
+ *     q = e4m3 round-to-nearest-even( clamp(x / 2^(E - 127), -448, 448) )
+ * with an exact quotient.  The codes E are packed four per int32 word along
+ * K, group 4w + i in byte i of word w; the bytes past the last group are 0:
+ *   1x128:   x [M,K] fp32 -> q [M,K] fp8, s [M, ceil(K/512)] int32
+ *   128x128: x [N,K] fp32 -> q [N,K] fp8, s [ceil(N/128), ceil(K/512)] int32
+ * Sizes, alignment and error rules as the fp32-scale calls above. */
+dg_status dg_quantize_fp8_1x128_ue8m0(const float* x, void* q, int32_t* s, int m, int k,
+                                      hipStream_t stream);
+dg_status dg_quantize_fp8_128x128_ue8m0(const float* x, void* q, int32_t* s, int n, int k,
+                                        hipStream_t stream);
+
 /* Token-contiguous operands of the weight-gradient GEMMs (DeepGEMM pages,
  * "反向传播中的梯度计算"): the 1x128 rule applied to the transpose of x, i.e.
  * groups of 128 consecutive tokens of one feature.

@@ -44,11 +44,14 @@ _lib.dg_gemm_bf16_nt.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _vp]
 _lib.dg_quantize_fp8_1x128.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
 _lib.dg_quantize_fp8_128x128.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
 _lib.dg_quantize_fp8_1x128_transposed.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
+_lib.dg_quantize_fp8_1x128_ue8m0.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
+_lib.dg_quantize_fp8_128x128_ue8m0.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
 _lib.dg_swiglu_quantize_fp8_1x128.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
 for _f in ("dg_gemm_fp8_nt", "dg_grouped_fp8_contiguous", "dg_grouped_fp8_contiguous_swiglu", "dg_grouped_fp8_masked", "dg_grouped_fp8_masked_noalloc",
            "dg_wgrad_fp8_nt", "dg_k_grouped_wgrad_fp8_nt", "dg_gemm_fp8_nt_ue8m0", "dg_gemm_fp8_nt_ue8m0_packed", "dg_grouped_fp8_contiguous_ue8m0_packed",
            "dg_grouped_fp8_masked_ue8m0_packed", "dg_gemm_bf16_nt", "dg_quantize_fp8_1x128",
-           "dg_quantize_fp8_128x128", "dg_quantize_fp8_1x128_transposed", "dg_swiglu_quantize_fp8_1x128"):
+           "dg_quantize_fp8_128x128", "dg_quantize_fp8_1x128_transposed", "dg_swiglu_quantize_fp8_1x128",
+           "dg_quantize_fp8_1x128_ue8m0", "dg_quantize_fp8_128x128_ue8m0"):
     getattr(_lib, _f).restype = ctypes.c_int
 _lib.dg_status_string.argtypes = [ctypes.c_int]
 _lib.dg_status_string.restype = ctypes.c_char_p
@@ -355,6 +358,35 @@ def dg_quantize_fp8_128x128(x, q, s):
     return q, s
 
 
+def _i32w(t, name):
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32 (packed UE8M0), got {t.dtype}")
+
+
+def dg_quantize_fp8_1x128_ue8m0(x, q, s):
+    """x fp32 [M,K] -> q fp8 [M,K], s int32 [M,ceil(K/512)]: power-of-two
+    scales, packed UE8M0 (see include/dg.h)."""
+    _f32(x, "x"); _fp8(q, "q"); _i32w(s, "s")
+    _dev(x, q, s)
+    m, k = x.shape
+    _shape(q, (m, k), "q"); _shape(s, (m, (k // 128 + 3) // 4), "s")
+    _check(_lib.dg_quantize_fp8_1x128_ue8m0(_ptr(x), _ptr(q), _ptr(s), m, k, _stream(x)),
+           "dg_quantize_fp8_1x128_ue8m0")
+    return q, s
+
+
+def dg_quantize_fp8_128x128_ue8m0(x, q, s):
+    """x fp32 [N,K] -> q fp8 [N,K], s int32 [ceil(N/128),ceil(K/512)]: power-of-two
+    scales, packed UE8M0 (see include/dg.h)."""
+    _f32(x, "x"); _fp8(q, "q"); _i32w(s, "s")
+    _dev(x, q, s)
+    n, k = x.shape
+    _shape(q, (n, k), "q"); _shape(s, ((n + 127) // 128, (k // 128 + 3) // 4), "s")
+    _check(_lib.dg_quantize_fp8_128x128_ue8m0(_ptr(x), _ptr(q), _ptr(s), n, k, _stream(x)),
+           "dg_quantize_fp8_128x128_ue8m0")
+    return q, s
+
+
 def dg_quantize_fp8_1x128_transposed(x, q, s):
     """x fp32 [T,F] -> q fp8 [F,T], s fp32 [F,T/128] (see include/dg.h)."""
     _f32(x, "x"); _fp8(q, "q"); _f32(s, "s")
@@ -450,6 +482,21 @@ def quantize_fp8_128x128(x):
     n, k = x.shape
     return dg_quantize_fp8_128x128(x, torch.empty((n, k), dtype=FP8, device=x.device),
                                    torch.empty(((n + 127) // 128, k // 128), dtype=torch.float32, device=x.device))
+
+
+def quantize_fp8_1x128_ue8m0(x):
+    """Activations with power-of-two scales: (fp8 [M,K], packed UE8M0 int32 [M,ceil(K/512)])."""
+    m, k = x.shape
+    return dg_quantize_fp8_1x128_ue8m0(x, torch.empty((m, k), dtype=FP8, device=x.device),
+                                       torch.empty((m, (k // 128 + 3) // 4), dtype=torch.int32, device=x.device))
+
+
+def quantize_fp8_128x128_ue8m0(x):
+    """Weights with power-of-two scales: (fp8 [N,K], packed UE8M0 int32 [ceil(N/128),ceil(K/512)])."""
+    n, k = x.shape
+    return dg_quantize_fp8_128x128_ue8m0(x, torch.empty((n, k), dtype=FP8, device=x.device),
+                                         torch.empty(((n + 127) // 128, (k // 128 + 3) // 4), dtype=torch.int32,
+                                                     device=x.device))
 
 
 def quantize_fp8_1x128_transposed(x):

@@ -738,6 +738,22 @@ dg_status dg_quantize_fp8_128x128(const float* x, void* q, float* s, int n, int 
   return quantize(1, x, q, s, n, k, stream);
 }
 
+dg_status dg_quantize_fp8_1x128_ue8m0(const float* x, void* q, int32_t* s, int m, int k, hipStream_t stream) {
+  if (!x || !q || !s) return DG_ERROR_INVALID_VALUE;
+  if (m <= 0 || k <= 0) return DG_ERROR_INVALID_VALUE;
+  if (k % 128 != 0) return DG_ERROR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(q, 4) || !aligned(s, 4)) return DG_ERROR_UNSUPPORTED;
+  return quantize(3, x, q, reinterpret_cast<float*>(s), m, k, stream);
+}
+
+dg_status dg_quantize_fp8_128x128_ue8m0(const float* x, void* q, int32_t* s, int n, int k, hipStream_t stream) {
+  if (!x || !q || !s) return DG_ERROR_INVALID_VALUE;
+  if (n <= 0 || k <= 0) return DG_ERROR_INVALID_VALUE;
+  if (k % 128 != 0) return DG_ERROR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(q, 4) || !aligned(s, 4)) return DG_ERROR_UNSUPPORTED;
+  return quantize(4, x, q, reinterpret_cast<float*>(s), n, k, stream);
+}
+
 dg_status dg_quantize_fp8_1x128_transposed(const float* x, void* q, float* s, int t, int f,
                                            hipStream_t stream) {
   if (!x || !q || !s) return DG_ERROR_INVALID_VALUE;

@@ -87,7 +87,8 @@ hipError_t launch_splitk_reduce(int kind, const Params& p, hipStream_t stream);
 
 // FP8 quantiser (dg_quant.hip).  mode 0: x [rows,cols] -> 1x128 groups
 // along cols; 1: 128x128 blocks; 2: x [rows=T, cols=F] -> q [F,T] with 1x128
-// groups along T.  num_cus sizes the grid.
+// groups along T; 3, 4: modes 0, 1 with power-of-two scales written as packed
+// UE8M0 bytes (s then points to int32 words).  num_cus sizes the grid.
 hipError_t launch_swiglu_quantize(const uint16_t* c, uint8_t* q, float* s, int rows, int half_cols, int num_cus,
                                   hipStream_t stream);
 hipError_t launch_quantize(int mode, const float* x, uint8_t* q, float* s, int rows, int cols, int num_cus,

@@ -43,7 +43,33 @@ using codec::scale_of;
 using codec::encode4;
 using codec::silu;
 
-enum QuantMode : int { Q_ROWS = 0, Q_BLOCKS = 1, Q_TRANSPOSED = 2 };
+enum QuantMode : int { Q_ROWS = 0, Q_BLOCKS = 1, Q_TRANSPOSED = 2, Q_ROWS_UE8M0 = 3, Q_BLOCKS_UE8M0 = 4 };
+
+// Power-of-two (UE8M0) scales (DeepGEMM pages, aikraft.ru support table:
+// packed UE8M0, four values in one torch.int): a group's scale is the
+// smallest 2^(E - 127), E in [0, 254], not below s0 = scale_of(amax), read off
+// s0's fp32 fields -- an exact power keeps its exponent field, anything above
+// it takes the next; a subnormal s0 is at most 2^-127 (E = 0, the field 0
+// with mantissa 2^22) or below 2^-126 (E = 1).  The quotient by 2^(E - 127)
+// is exact, so the codes are those of an exact division.  E goes to byte
+// (group mod 4) of word group/4 of the row's packed words; a row's last group
+// also zeroes the bytes past it.
+__device__ __forceinline__ uint32_t ue8m0_code(float amax) {
+  const uint32_t b = __float_as_uint(scale_of(amax));
+  const uint32_t ex = b >> 23, man = b & 0x7fffffu;
+  if (ex == 0) return man > 0x400000u ? 1u : 0u;
+  return min(ex + (man != 0u ? 1u : 0u), 254u);
+}
+__device__ __forceinline__ float ue8m0_value(uint32_t e) {
+  return __uint_as_float(e == 0 ? 0x400000u : e << 23);
+}
+// byte `g` of a row of `kw` packed words, plus the row's padding bytes when g
+// is its last group
+__device__ __forceinline__ void put_code(uint8_t* row_bytes, int g, int groups, int kw, uint32_t e) {
+  row_bytes[g] = (uint8_t)e;
+  if (g == groups - 1)
+    for (int p = groups; p < 4 * kw; ++p) row_bytes[p] = 0;
+}
 
 
 // x / s, equal to the IEEE fp32 quotient: y0 = x * RN(1/s), then two
@@ -77,11 +103,12 @@ __device__ __forceinline__ float4 load_nt(const float* p) {
   return float4{t[0], t[1], t[2], t[3]};
 }
 
-// 128 x 128 tiles: MODE is Q_BLOCKS or Q_TRANSPOSED
+// 128 x 128 tiles: MODE is Q_BLOCKS, Q_BLOCKS_UE8M0 or Q_TRANSPOSED
 template <int MODE>
 __global__ __launch_bounds__(kQThreads) void quant_kernel(const float* __restrict__ x, uint8_t* __restrict__ q,
                                                           float* __restrict__ s, int rows, int cols, int64_t tiles,
                                                           int col_tiles) {
+  constexpr bool kUe8m0 = MODE == Q_BLOCKS_UE8M0;
   // Q_BLOCKS / Q_TRANSPOSED: per-wave partial maxima; Q_TRANSPOSED: byte tile
   __shared__ float sMax[8][kQ];
   __shared__ __attribute__((aligned(16))) uint8_t sT[MODE == Q_TRANSPOSED ? kQ : 1][kQ + 16];
@@ -106,7 +133,7 @@ __global__ __launch_bounds__(kQThreads) void quant_kernel(const float* __restric
     }
     auto amax4 = [](const float4& a) { return fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))); };
 
-    if constexpr (MODE == Q_BLOCKS) {
+    if constexpr (MODE == Q_BLOCKS || MODE == Q_BLOCKS_UE8M0) {
       float m = 0.f;
 #pragma unroll
       for (int i = 0; i < kQStrips; ++i) m = fmaxf(m, amax4(v[i]));
@@ -122,8 +149,16 @@ __global__ __launch_bounds__(kQThreads) void quant_kernel(const float* __restric
       float mm = sMax[0][0];
 #pragma unroll
       for (int w = 1; w < 8; ++w) mm = fmaxf(mm, sMax[w][0]);
-      const float sc = scale_of(mm);
-      if (t == 0) s[tr * col_tiles + tc] = sc;
+      float sc;
+      if constexpr (kUe8m0) {
+        const uint32_t e = ue8m0_code(mm);
+        sc = ue8m0_value(e);
+        const int kw = (col_tiles + 3) / 4;
+        if (t == 0) put_code(reinterpret_cast<uint8_t*>(s) + tr * (4 * kw), tc, col_tiles, kw, e);
+      } else {
+        sc = scale_of(mm);
+        if (t == 0) s[tr * col_tiles + tc] = sc;
+      }
 #pragma unroll
       for (int i = 0; i < kQStrips; ++i) {
         const int64_t r = r0 + 16 * i + rsub;
@@ -194,8 +229,10 @@ __global__ __launch_bounds__(kQThreads) void quant_kernel(const float* __restric
 // 1x128 groups of a row-major [M, K] array (K % 128 == 0) are consecutive
 // 512-byte runs of the flat array: each wave streams 16 consecutive groups
 // (8 KB) per step, lane l holding float4 number l + 64j (group 2j + l/32).
+// kUe8m0: power-of-two scales, packed (`gpr` groups per row).
+template <bool kUe8m0>
 __global__ __launch_bounds__(kQThreads) void quant_rows_kernel(const float* __restrict__ x, uint8_t* __restrict__ q,
-                                                               float* __restrict__ s, int64_t groups) {
+                                                               float* __restrict__ s, int64_t groups, int gpr) {
   const int lane = threadIdx.x & 63;
   const int64_t waves = (int64_t)gridDim.x * (kQThreads / 64);
   const int64_t chunks = (groups + 15) / 16;
@@ -215,10 +252,25 @@ __global__ __launch_bounds__(kQThreads) void quant_rows_kernel(const float* __re
       m = max_xor(m, 4);
       m = max_xor(m, 2);
       m = max_xor(m, 1);
-      const float sc = scale_of(m);
       const int64_t g = g0 + 2 * j + (lane >> 5);
+      float sc;
+      uint32_t e = 0;
+      if constexpr (kUe8m0) {
+        e = ue8m0_code(m);
+        sc = ue8m0_value(e);
+      } else {
+        sc = scale_of(m);
+      }
       if (g < groups) {
-        if ((lane & 31) == 0) s[g] = sc;
+        if ((lane & 31) == 0) {
+          if constexpr (kUe8m0) {
+            const int64_t row = g / gpr;
+            const int kw = (gpr + 3) / 4;
+            put_code(reinterpret_cast<uint8_t*>(s) + row * (4 * kw), (int)(g - row * gpr), gpr, kw, e);
+          } else {
+            s[g] = sc;
+          }
+        }
         __builtin_nontemporal_store(
             encode4(quotient(v[j].x, sc), quotient(v[j].y, sc), quotient(v[j].z, sc), quotient(v[j].w, sc)),
             reinterpret_cast<uint32_t*>(q + g0 * kQ + 256 * j + 4 * lane));
@@ -320,16 +372,24 @@ hipError_t launch_quantize(int mode, const float* x, uint8_t* q, float* s, int r
   const int grid = (int)(tiles < cap ? tiles : cap);
   if (grid <= 0) return hipSuccess;
   switch (mode) {
-    case Q_ROWS: {
+    case Q_ROWS:
+    case Q_ROWS_UE8M0: {
       const int64_t groups = (int64_t)rows * (cols / kQ);
       const int64_t wgs = (groups + 16 * (kQThreads / 64) - 1) / (16 * (kQThreads / 64));
       const int g2 = (int)(wgs < cap ? wgs : cap);
-      hipLaunchKernelGGL(quant_rows_kernel, dim3(g2), dim3(kQThreads), 0, stream, x, q, s, groups);
+      if (mode == Q_ROWS)
+        hipLaunchKernelGGL(quant_rows_kernel<false>, dim3(g2), dim3(kQThreads), 0, stream, x, q, s, groups, cols / kQ);
+      else
+        hipLaunchKernelGGL(quant_rows_kernel<true>, dim3(g2), dim3(kQThreads), 0, stream, x, q, s, groups, cols / kQ);
       break;
     }
     case Q_BLOCKS:
       hipLaunchKernelGGL(quant_kernel<Q_BLOCKS>, dim3(grid), dim3(kQThreads), 0, stream, x, q, s, rows, cols, tiles,
                          col_tiles);
+      break;
+    case Q_BLOCKS_UE8M0:
+      hipLaunchKernelGGL(quant_kernel<Q_BLOCKS_UE8M0>, dim3(grid), dim3(kQThreads), 0, stream, x, q, s, rows, cols,
+                         tiles, col_tiles);
       break;
     case Q_TRANSPOSED:
       hipLaunchKernelGGL(quant_kernel<Q_TRANSPOSED>, dim3(grid), dim3(kQThreads), 0, stream, x, q, s, rows, cols,

@@ -337,6 +337,27 @@ def quantize_128x128(x: np.ndarray):
     return q, s
 
 
+def quantize_1x128_ue8m0(x: np.ndarray):
+    """x fp32 [M,K] -> (q uint8 [M,K], packed UE8M0 codes int32 [M,ceil(K/512)]):
+    the smallest power-of-two scale not below amax/448 per 1x128 group."""
+    x = _c(x, np.float32)
+    m, k = x.shape
+    q = np.empty((m, k), np.uint8)
+    s = np.empty((m, (k // 128 + 3) // 4), np.int32)
+    _check(lib().dgo_quantize_1x128_ue8m0(_p(x), _I(m), _I(k), _p(q), _p(s)), "quantize_1x128_ue8m0")
+    return q, s
+
+
+def quantize_128x128_ue8m0(x: np.ndarray):
+    """x fp32 [N,K] -> (q uint8 [N,K], packed UE8M0 codes int32 [ceil(N/128),ceil(K/512)])."""
+    x = _c(x, np.float32)
+    n, k = x.shape
+    q = np.empty((n, k), np.uint8)
+    s = np.empty(((n + 127) // 128, (k // 128 + 3) // 4), np.int32)
+    _check(lib().dgo_quantize_128x128_ue8m0(_p(x), _I(n), _I(k), _p(q), _p(s)), "quantize_128x128_ue8m0")
+    return q, s
+
+
 def quantize_1x128_transposed(x: np.ndarray):
     """x fp32 [T,F] -> (q uint8 [F,T], s fp32 [F,T/128]): 1x128 groups along T."""
     x = _c(x, np.float32)

@@ -127,6 +127,89 @@ int dgo_quantize_1x128_transposed(const float* x, int64_t t, int64_t f, uint8_t*
   return rc;
 }
 
+/* ---- power-of-two (UE8M0) scales, packed four to an int32 --------------
+ *
+ * DeepGEMM pages (aikraft.ru, support table: the scale format of the newer
+ * architecture is packed UE8M0, four values in one torch.int).  The pages
+ * give no rule for choosing such a scale.  Reading taken: the scale of a
+ * group is the smallest E8M0 value 2^(E - 127), E in [0, 254], that is not
+ * below the fp32 scale above (so no element is clipped harder than with it):
+ *
+ *   s0   = fp32(amax / 448)                  (1 for an all-zero group)
+ *   E    = least E in [0, 254] with 2^(E - 127) >= s0
+ *   q(x) = e4m3_RNE( clamp(x / 2^(E - 127), -448, 448) )
+ *
+ * The quotient by a power of two is exact in fp64; handed to the encoder as
+ * fp32 it stays exact down to 2^-126, and anything smaller encodes to zero
+ * either way (the smallest e4m3 magnitude is 2^-9).  The codes E go to packed
+ * words [rows, ceil(groups/4)] int32: group g of a row is byte g mod 4 (bits
+ * 8(g mod 4) .. +7) of word g/4; the bytes past the last group are 0. */
+static unsigned ue8m0_of(float amax) {
+  const double s0 = (double)scale_of(amax);
+  for (unsigned e = 0; e < 254; ++e)
+    if (ldexp(1.0, (int)e - 127) >= s0) return e;
+  return 254;
+}
+
+static uint8_t quantize_pow2(float x, unsigned e) {
+  double y = (double)x / ldexp(1.0, (int)e - 127);
+  if (y > E4M3_LARGEST) y = E4M3_LARGEST;
+  if (y < -E4M3_LARGEST) y = -E4M3_LARGEST;
+  return e4m3_encode((float)y);
+}
+
+static void put_code(int32_t* words, int64_t kw, int64_t row, int64_t g, unsigned e) {
+  uint32_t w = (uint32_t)words[row * kw + g / 4];
+  w |= (uint32_t)e << (8 * (g % 4));
+  words[row * kw + g / 4] = (int32_t)w;
+}
+
+/* x [m, k] -> q [m, k], s [m, ceil(k/512)] packed codes of the 1x128 groups */
+int dgo_quantize_1x128_ue8m0(const float* x, int64_t m, int64_t k, uint8_t* q, int32_t* s) {
+  if (m < 0 || k < 0 || k % QG) return -1;
+  const int64_t kg = k / QG, kw = (kg + 3) / 4;
+  memset(s, 0, sizeof(int32_t) * (size_t)(m * kw));
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < m; ++r) {
+    for (int64_t g = 0; g < kg; ++g) {
+      const float* xg = x + r * k + g * QG;
+      float amax = 0.0f;
+      for (int i = 0; i < QG; ++i) {
+        const float v = fabsf(xg[i]);
+        if (v > amax) amax = v;
+      }
+      const unsigned e = ue8m0_of(amax);
+      put_code(s, kw, r, g, e);
+      for (int i = 0; i < QG; ++i) q[r * k + g * QG + i] = quantize_pow2(xg[i], e);
+    }
+  }
+  return 0;
+}
+
+/* x [n, k] -> q [n, k], s [ceil(n/128), ceil(k/512)] packed codes of the 128x128 blocks */
+int dgo_quantize_128x128_ue8m0(const float* x, int64_t n, int64_t k, uint8_t* q, int32_t* s) {
+  if (n < 0 || k < 0 || k % QG) return -1;
+  const int64_t kg = k / QG, nb = (n + QG - 1) / QG, kw = (kg + 3) / 4;
+  memset(s, 0, sizeof(int32_t) * (size_t)(nb * kw));
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < nb; ++b) {
+    for (int64_t g = 0; g < kg; ++g) {
+      const int64_t r0 = b * QG, r1 = (r0 + QG < n) ? r0 + QG : n;
+      float amax = 0.0f;
+      for (int64_t rr = r0; rr < r1; ++rr)
+        for (int i = 0; i < QG; ++i) {
+          const float v = fabsf(x[rr * k + g * QG + i]);
+          if (v > amax) amax = v;
+        }
+      const unsigned e = ue8m0_of(amax);
+      put_code(s, kw, b, g, e);
+      for (int64_t rr = r0; rr < r1; ++rr)
+        for (int i = 0; i < QG; ++i) q[rr * k + g * QG + i] = quantize_pow2(x[rr * k + g * QG + i], e);
+    }
+  }
+  return 0;
+}
+
 /* ---- SwiGLU on the first linear's output, then the 1x128 rule ----------
  *
  * DeepGEMM pages (the Russian overview "DeepSeek выложила в открытый доступ

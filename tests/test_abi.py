@@ -182,7 +182,8 @@ def test_grouped_ue8m0_packed_argument_errors(lib):
 
 def test_quantizer_argument_errors(lib):
     vp, i = ctypes.c_void_p, ctypes.c_int
-    for name in ("dg_quantize_fp8_1x128", "dg_quantize_fp8_128x128", "dg_quantize_fp8_1x128_transposed"):
+    for name in ("dg_quantize_fp8_1x128", "dg_quantize_fp8_128x128", "dg_quantize_fp8_1x128_transposed",
+                 "dg_quantize_fp8_1x128_ue8m0", "dg_quantize_fp8_128x128_ue8m0"):
         f = getattr(lib, name)
         f.argtypes = [vp, vp, vp, i, i, vp]
         assert f(None, A16, A16, 128, 128, None) == INVALID, name

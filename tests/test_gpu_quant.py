@@ -166,3 +166,77 @@ def test_quantised_operands_feed_the_gemm(dg):
     ref, _ = oracle.gemm_fp8_nt(oa, osa, ob, osb)
     check_close(bits_to_f64(bf16_bits(c)), bits_to_f64(ref),
                 "quantise + dense GEMM 256x384x1024")
+
+
+# ---- power-of-two (UE8M0) scales, packed four to an int32 -------------------
+
+def run_ue8m0(fn, x, qshape, sshape):
+    """Codes prefilled with 0x7F (NaN) and words with 0x7F7F7F7F, which no
+    group writes (its E is at most 254 and padding bytes are 0)."""
+    xd = torch.from_numpy(x).cuda()
+    q = torch.full(qshape, 0x7F, dtype=torch.uint8, device="cuda")
+    s = torch.full(sshape, 0x7F7F7F7F, dtype=torch.int32, device="cuda")
+    fn(xd, q, s)
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), s.cpu().numpy()
+
+
+def check_ue8m0(got, ref, what):
+    (q, s), (qr, sr) = got, ref
+    assert q.shape == qr.shape and s.shape == sr.shape, what
+    bad = np.flatnonzero(q != qr)
+    assert bad.size == 0, f"{what}: {bad.size} codes differ, first at {np.unravel_index(bad[0], q.shape)}: " \
+                          f"gpu {q.flat[bad[0]]:#04x} oracle {qr.flat[bad[0]]:#04x}"
+    assert np.array_equal(s, sr), f"{what}: {int(np.count_nonzero(s != sr))} packed scale words differ"
+
+
+def wide_data(seed, rows, cols):
+    """data() with group magnitudes over 2^-130 .. 2^100, so the codes E run
+    from 0 (scales below the E8M0 range) to 227 and subnormal scales occur."""
+    x = data(seed, rows, cols)
+    rng = np.random.default_rng(seed + 1)
+    mag = np.ldexp(np.float32(1.0), rng.integers(-130, 100, size=(rows, cols // 128))).astype(np.float32)
+    return np.ascontiguousarray((x.reshape(rows, -1, 128) * mag[:, :, None]).reshape(rows, cols).astype(np.float32))
+
+
+@pytest.mark.parametrize("m,k", [(1, 128), (37, 384), (128, 512), (130, 640), (300, 1152), (257, 7168)])
+def test_1x128_ue8m0(dg, m, k):
+    """K/128 = 1, 3, 4, 5, 9, 56 groups per row: whole and padded words."""
+    say(f"quantize 1x128 ue8m0 {m}x{k}")
+    for x in (data(m * 11 + k, m, k), wide_data(m * 13 + k, m, k)):
+        got = run_ue8m0(dg.dg_quantize_fp8_1x128_ue8m0, x, (m, k), (m, (k // 128 + 3) // 4))
+        check_ue8m0(got, oracle.quantize_1x128_ue8m0(x), f"1x128 ue8m0 {m}x{k}")
+
+
+@pytest.mark.parametrize("n,k", [(1, 128), (100, 384), (128, 512), (300, 640), (2112, 1152)])
+def test_128x128_ue8m0(dg, n, k):
+    say(f"quantize 128x128 ue8m0 {n}x{k}")
+    x = data(n * 17 + k, n, k)
+    if k >= 256:
+        x[: min(n, 128), 128:256] = 0.0  # an all-zero block: code 127, codes 0
+    nb = (n + 127) // 128
+    got = run_ue8m0(dg.dg_quantize_fp8_128x128_ue8m0, x, (n, k), (nb, (k // 128 + 3) // 4))
+    check_ue8m0(got, oracle.quantize_128x128_ue8m0(x), f"128x128 ue8m0 {n}x{k}")
+
+
+def test_ue8m0_quantise_then_packed_gemm(dg):
+    """The power-of-two path end to end on the GPU: both operands quantised
+    with packed UE8M0 scales, then the packed GEMM, against the oracle's
+    quantiser and GEMM on the same fp32 inputs."""
+    from tests.parity import bf16_bits, bits_to_f64, check_close, sentinel_bf16
+    m, n, k = 300, 520, 1664
+    rng = np.random.default_rng(91)
+    xa = rng.standard_normal((m, k)).astype(np.float32)
+    xb = rng.standard_normal((n, k)).astype(np.float32)
+    say("ue8m0 quantise -> packed GEMM")
+    qa, sa = dg.quantize_fp8_1x128_ue8m0(torch.from_numpy(xa).cuda())
+    qb, sb = dg.quantize_fp8_128x128_ue8m0(torch.from_numpy(xb).cuda())
+    c = sentinel_bf16((m, n))
+    dg.dg_gemm_fp8_nt_ue8m0_packed(qa, sa, qb, sb, c)
+    torch.cuda.synchronize()
+    ra, wa = oracle.quantize_1x128_ue8m0(xa)
+    rb, wb = oracle.quantize_128x128_ue8m0(xb)
+    assert np.array_equal(qa.view(torch.uint8).cpu().numpy(), ra) and np.array_equal(sa.cpu().numpy(), wa)
+    assert np.array_equal(qb.view(torch.uint8).cpu().numpy(), rb) and np.array_equal(sb.cpu().numpy(), wb)
+    ref, _ = oracle.gemm_fp8_nt_ue8m0_packed(ra, wa, rb, wb)
+    check_close(bits_to_f64(bf16_bits(c)), bits_to_f64(ref), "ue8m0 quantise -> GEMM")
