@@ -244,6 +244,11 @@ __global__ __launch_bounds__(kQThreads) void quant_rows_kernel(const float* __re
       const int64_t g = g0 + 2 * j + (lane >> 5);
       v[j] = g < groups ? load_nt(x + g0 * kQ + 256 * j + 4 * lane) : float4{0.f, 0.f, 0.f, 0.f};
     }
+    // power-of-two scales whose rows have a multiple of 4 groups: the packed
+    // codes have no padding, so the step's 16 groups are 16 consecutive bytes
+    // -- written as 4 words by lanes 0-3 after the loop instead of 16 byte stores
+    const bool whole = kUe8m0 && (gpr % 4 == 0) && g0 + 16 <= groups;
+    uint32_t ecode[8];  // code of this lane's group in pass j
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       float m = fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w)));
@@ -261,12 +266,15 @@ __global__ __launch_bounds__(kQThreads) void quant_rows_kernel(const float* __re
       } else {
         sc = scale_of(m);
       }
+      ecode[j] = e;
       if (g < groups) {
         if ((lane & 31) == 0) {
           if constexpr (kUe8m0) {
-            const int64_t row = g / gpr;
-            const int kw = (gpr + 3) / 4;
-            put_code(reinterpret_cast<uint8_t*>(s) + row * (4 * kw), (int)(g - row * gpr), gpr, kw, e);
+            if (!whole) {
+              const int64_t row = g / gpr;
+              const int kw = (gpr + 3) / 4;
+              put_code(reinterpret_cast<uint8_t*>(s) + row * (4 * kw), (int)(g - row * gpr), gpr, kw, e);
+            }
           } else {
             s[g] = sc;
           }
@@ -275,6 +283,24 @@ __global__ __launch_bounds__(kQThreads) void quant_rows_kernel(const float* __re
             encode4(quotient(v[j].x, sc), quotient(v[j].y, sc), quotient(v[j].z, sc), quotient(v[j].w, sc)),
             reinterpret_cast<uint32_t*>(q + g0 * kQ + 256 * j + 4 * lane));
       }
+    }
+    if constexpr (kUe8m0) {
+      // group 2j + h (h = lane / 32) of the step has code ecode[j] in lane
+      // half h; word w holds groups 4w .. 4w + 3 = passes 2w, 2w + 1, both halves
+      uint32_t other[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) other[j] = (uint32_t)__shfl_xor((int)ecode[j], 32, 64);
+      uint32_t word = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t lo = lane < 32 ? ecode[2 * w] : other[2 * w];          // group 4w
+        const uint32_t hi = lane < 32 ? other[2 * w] : ecode[2 * w];          // group 4w + 1
+        const uint32_t lo2 = lane < 32 ? ecode[2 * w + 1] : other[2 * w + 1];  // group 4w + 2
+        const uint32_t hi2 = lane < 32 ? other[2 * w + 1] : ecode[2 * w + 1];  // group 4w + 3
+        const uint32_t vw = lo | (hi << 8) | (lo2 << 16) | (hi2 << 24);
+        word = (lane == w) ? vw : word;
+      }
+      if (whole && lane < 4) reinterpret_cast<uint32_t*>(s)[(g0 >> 2) + lane] = word;
     }
   }
 }
