@@ -315,10 +315,13 @@ def test_power_of_two_kinds_plan_as_their_layout(lib):
 
 
 def test_split_k_planning(lib):
-    """Few output tiles and a long K: split K to give every CU work; many
-    tiles: no split."""
+    """Few output tiles and a long K: split K four ways (with 64-column tiles
+    when the 128-column ones are too few: fewer, larger items than CUs
+    measured faster for M=64, N=2112, K=7168); many tiles: no split."""
     c = _cfg(lib, 0, 64, 2112, 7168)
-    assert c["k_splits"] > 1 and c["tiles"] * c["k_splits"] >= 256
+    assert c["k_splits"] == 4 and (c["block_m"], c["block_n"]) == (64, 64) and c["tiles"] * c["k_splits"] >= 128
+    c = _cfg(lib, 0, 64, 4096, 7168)
+    assert c["k_splits"] == 4 and c["tiles"] * c["k_splits"] >= 256
     c = _cfg(lib, 2, 256, 4096, 7168, 1)
     assert c["k_splits"] > 1
     assert _cfg(lib, 0, 4096, 7168, 16384)["k_splits"] == 1
