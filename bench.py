@@ -29,7 +29,8 @@ the FP8 re-quantise fused into the epilogue (`fused_swiglu`).
 Other workloads (dense, contiguous, masked, wgrad, k_grouped_wgrad, small,
 dense_ue8m0, contiguous_ue8m0, masked_ue8m0 -- those sweeps with packed UE8M0
 scales --, bf16 -- the
-sweep's shapes in BF16 against the bf16 peak --, quantize, the FP8 quantiser
+sweep's shapes in BF16 against the bf16 peak --, grouped_bf16 -- contiguous and masked
+problems in BF16 --, quantize, the FP8 quantiser
 in GB/s, and swiglu_quantize, the SwiGLU + FP8 re-quantise step between an
 expert's two GEMMs in GB/s, and contiguous_swiglu, the contiguous sweep with
 SwiGLU + re-quantise fused into the GEMM) print a line of the same form.  Exactly one JSON
@@ -451,6 +452,70 @@ def build_bf16():
                    "shapes": len(calls), "scales": "none", "out": "bf16"}
 
 
+def build_grouped_bf16():
+    """The grouped layouts in BF16 (dg_grouped_bf16_contiguous and
+    dg_grouped_bf16_masked): the contiguous sweep's G=4 problems and the masked
+    decode's G=4 and G=16 problems at N=4096, K=7168, with N(0,1) operands
+    rounded to bf16 and no scales; rooflines against the bf16 dense peak and HBM."""
+    import torch
+    import moe_grouped_gemm_x128_amd as dg
+    from harness import inputs, workloads
+
+    to_dev = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+    calls = []
+    for s in workloads.contiguous_sweep():
+        if s["g"] != 4:
+            continue
+        g, rpe, n, k = s["g"], s["rows_per_expert"], s["n"], s["k"]
+        x = inputs.make_contiguous_bf16(g, rpe, n, k, s["seed"])
+        da, db, ids = to_dev(x.a), to_dev(x.b), _dev(x.ctrl)
+        out = torch.empty((g * rpe, n), dtype=torch.bfloat16, device="cuda")
+        fn = lambda da=da, db=db, out=out, ids=ids: dg.dg_grouped_bf16_contiguous(da, db, out, ids)
+        rows = np.flatnonzero(x.ctrl >= 0)
+        mv = rows.size
+        nbytes = 2 * (mv * k + g * n * k + mv * n) + g * rpe * 4
+
+        def sample(rng, count, x=x, rows=rows, n=n, k=k, g=g):
+            import oracle
+            r = rows[rng.integers(0, rows.size, count)]
+            c = rng.integers(0, n, count)
+            for e in range(g):
+                sel = np.flatnonzero(x.ctrl[r] == e)
+                oracle.gemm_bf16_nt_at(x.a, x.b[e], r[sel], c[sel])
+            return 2.0 * k * count
+
+        calls.append(Call(s["name"] + "_bf16", 2.0 * mv * n * k, nbytes, fn, sample, peak=PEAK_BF16_TFLOPS,
+                          group="grouped_bf16"))
+    for s in workloads.masked_sweep():
+        if s["g"] not in (4, 16) or s["n"] != 4096:
+            continue
+        g, m_max, n, k = s["g"], s["m_max"], s["n"], s["k"]
+        mm = inputs._rng(s["seed"], 4).integers(64, 193, size=g).astype(np.int32)
+        x = inputs.make_masked_bf16(g, m_max, n, k, s["seed"], masked_m=mm)
+        da, db, dmm = to_dev(x.a), to_dev(x.b), _dev(mm)
+        out = torch.empty((g, m_max, n), dtype=torch.bfloat16, device="cuda")
+        fn = lambda da=da, db=db, out=out, dmm=dmm: dg.dg_grouped_bf16_masked(da, db, out, dmm)
+        mv = int(mm.sum())
+        nbytes = 2 * (mv * k + g * n * k + mv * n) + g * 4
+
+        def sample(rng, count, x=x, mm=mm, n=n, k=k, g=g):
+            import oracle
+            gs = rng.integers(0, g, count)
+            r = (rng.random(count) * mm[gs]).astype(np.int64)
+            c = rng.integers(0, n, count)
+            for e in range(g):
+                sel = np.flatnonzero(gs == e)
+                oracle.gemm_bf16_nt_at(x.a[e], x.b[e], r[sel], c[sel])
+            return 2.0 * k * count
+
+        calls.append(Call(s["name"] + "_bf16", 2.0 * mv * n * k, nbytes, fn, sample, peak=PEAK_BF16_TFLOPS,
+                          group="grouped_bf16"))
+    return calls, {"workload": "grouped_bf16", "description":
+                   "MoE contiguous G=4 x 8192 rows (ragged padding), (N,K) in {(4096,7168),(7168,2048)}, and masked "
+                   "decode G in {4,16}, M_max=256, masked_m ~ U{64..192}, N=4096, K=7168, in BF16",
+                   "scales": "none", "out": "bf16"}
+
+
 QUANT_METRIC = "FP8 quantiser GB/s (absmax/448 fp32 scales) and % of MI355X HBM peak"
 
 
@@ -780,7 +845,7 @@ def main():
     ap.add_argument("--workload", default="all",
                     choices=["all", "dense", "small", "contiguous", "masked", "wgrad", "k_grouped_wgrad", "quantize",
                              "dense_ue8m0", "bf16", "swiglu_quantize", "contiguous_swiglu", "contiguous_ue8m0",
-                             "masked_ue8m0"])
+                             "masked_ue8m0", "grouped_bf16"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold-median", action="store_true", help="skip the cold-cache median of the dominant GEMM")
@@ -806,7 +871,7 @@ def main():
                 "quantize": build_quantize, "dense_ue8m0": lambda: build_dense(pow2=True), "bf16": build_bf16,
                 "swiglu_quantize": build_swiglu, "contiguous_swiglu": build_contiguous_swiglu,
                 "contiguous_ue8m0": lambda: build_contiguous(pow2=True),
-                "masked_ue8m0": lambda: build_masked(pow2=True)}
+                "masked_ue8m0": lambda: build_masked(pow2=True), "grouped_bf16": build_grouped_bf16}
     if args.copy_calibration:
         copy_calibration()
         return
@@ -867,7 +932,7 @@ def main():
             SWIGLU_METRIC if swiglu else QUANT_METRIC, "f32"
         data = "synthetic (seeded N(0,1) bf16)" if swiglu else "synthetic (seeded N(0,1) fp32)"
     else:
-        bf16 = args.workload == "bf16"
+        bf16 = args.workload in ("bf16", "grouped_bf16")
         value, unit, metric, dtype = step_flops / (ms_per_step * 1e-3) / 1e12, "TFLOP/s", METRIC, \
             "bf16" if bf16 else "fp8"
         data = "synthetic (seeded N(0,1), bf16)" if bf16 else "synthetic (seeded N(0,1), e4m3-quantised)"

@@ -154,6 +154,39 @@ def make_dense_bf16(m: int, n: int, k: int, seed: int) -> DenseBf16:
                      _to_bf16_bits(_normal(_rng(seed, 1), (n, k))))
 
 
+def _expert_ids(g: int, rows_per_expert: int, seed: int, max_pad: int) -> np.ndarray:
+    """Each expert's segment: its valid rows, then U{0..max_pad} padding rows (-1)."""
+    pads = np.minimum(_rng(seed, 3).integers(0, max_pad + 1, size=g), rows_per_expert)
+    ids = np.full(g * rows_per_expert, -1, dtype=np.int32)
+    for e in range(g):
+        ids[e * rows_per_expert:e * rows_per_expert + rows_per_expert - int(pads[e])] = e
+    return ids
+
+
+@dataclass
+class GroupedBf16:
+    """Grouped BF16 operands (bf16 bit patterns): contiguous a [M_total, K] with
+    m_indices, or masked a [G, M_max, K] with masked_m; b [G, N, K]."""
+    a: np.ndarray
+    b: np.ndarray
+    ctrl: np.ndarray
+
+
+def make_contiguous_bf16(g: int, rows_per_expert: int, n: int, k: int, seed: int,
+                         max_pad: int = 127) -> GroupedBf16:
+    """N(0,1) values rounded to bf16; the contiguous layout of make_contiguous."""
+    assert rows_per_expert % BLOCK_K == 0
+    a = _to_bf16_bits(_normal(_rng(seed, 0), (g * rows_per_expert, k)))
+    b = _to_bf16_bits(_normal(_rng(seed, 1), (g * n, k))).reshape(g, n, k)
+    return GroupedBf16(a, b, _expert_ids(g, rows_per_expert, seed, max_pad))
+
+
+def make_masked_bf16(g: int, m_max: int, n: int, k: int, seed: int, masked_m) -> GroupedBf16:
+    a = _to_bf16_bits(_normal(_rng(seed, 0), (g * m_max, k))).reshape(g, m_max, k)
+    b = _to_bf16_bits(_normal(_rng(seed, 1), (g * n, k))).reshape(g, n, k)
+    return GroupedBf16(a, b, np.asarray(masked_m, dtype=np.int32))
+
+
 def _grouped_rhs(g: int, n: int, k: int, seed: int, pow2: bool = False) -> tuple[np.ndarray, np.ndarray]:
     nb = (n + BLOCK_K - 1) // BLOCK_K
     b = np.empty((g, n, k), dtype=np.uint8)

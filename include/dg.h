@@ -110,6 +110,18 @@ dg_status dg_gemm_fp8_nt_ue8m0_packed(const void* a, const int32_t* sa, const vo
 dg_status dg_gemm_bf16_nt(const void* a, const void* b, void* c, int m, int n, int k,
                           hipStream_t stream);
 
+/* The two grouped layouts in BF16 (the BF16 GEMM of dg_gemm_bf16_nt on the
+ * grouped calls' scheduling): bf16 operands, fp32 accumulation, no scales,
+ * round-to-nearest-even bf16 output.  Row rules, layout limits and results as
+ * dg_grouped_fp8_contiguous / dg_grouped_fp8_masked:
+ *   contiguous: a [M_total,K], b [G,N,K], c [M_total,N], m_indices [M_total]
+ *   masked:     a [G,M_max,K], b [G,N,K], c [G,M_max,N], masked_m [G]
+ * K >= 64, K % 64 == 0 and K <= 2^22; a, b 16-byte aligned. */
+dg_status dg_grouped_bf16_contiguous(const void* a, const void* b, void* c, const int32_t* m_indices,
+                                     int m_total, int n, int k, int num_groups, hipStream_t stream);
+dg_status dg_grouped_bf16_masked(const void* a, const void* b, void* c, const int32_t* masked_m,
+                                 int num_groups, int m_max, int n, int k, hipStream_t stream);
+
 /* MoE grouped GEMM, contiguous layout (DeepGEMM pages, "分组 GEMM": training
  * forward and inference prefill; "使用示例": m_indices gives each LHS row its
  * group).  The rows of all experts are stacked into one LHS:
@@ -300,7 +312,9 @@ typedef enum {
   DG_KIND_BF16 = 6,           /* dg_gemm_bf16_nt (k counts bf16 values) */
   DG_KIND_CONTIGUOUS_SWIGLU = 7, /* dg_grouped_fp8_contiguous_swiglu (n = 2I) */
   DG_KIND_CONTIGUOUS_POW2 = 8,   /* dg_grouped_fp8_contiguous_ue8m0_packed */
-  DG_KIND_MASKED_POW2 = 9        /* dg_grouped_fp8_masked_ue8m0_packed */
+  DG_KIND_MASKED_POW2 = 9,       /* dg_grouped_fp8_masked_ue8m0_packed */
+  DG_KIND_CONTIGUOUS_BF16 = 10,  /* dg_grouped_bf16_contiguous (k counts bf16 values) */
+  DG_KIND_MASKED_BF16 = 11       /* dg_grouped_bf16_masked (k counts bf16 values) */
 } dg_kind;
 
 /* Tile configuration the per-shape heuristic picks (DeepGEMM pages: block

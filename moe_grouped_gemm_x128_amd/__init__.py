@@ -41,6 +41,8 @@ _lib.dg_gemm_fp8_nt_ue8m0_packed.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32
 _lib.dg_grouped_fp8_contiguous_ue8m0_packed.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]
 _lib.dg_grouped_fp8_masked_ue8m0_packed.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]
 _lib.dg_gemm_bf16_nt.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _vp]
+_lib.dg_grouped_bf16_contiguous.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]
+_lib.dg_grouped_bf16_masked.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]
 _lib.dg_quantize_fp8_1x128.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
 _lib.dg_quantize_fp8_128x128.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
 _lib.dg_quantize_fp8_1x128_transposed.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
@@ -49,7 +51,7 @@ _lib.dg_quantize_fp8_128x128_ue8m0.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
 _lib.dg_swiglu_quantize_fp8_1x128.argtypes = [_vp, _vp, _vp, _i32, _i32, _vp]
 for _f in ("dg_gemm_fp8_nt", "dg_grouped_fp8_contiguous", "dg_grouped_fp8_contiguous_swiglu", "dg_grouped_fp8_masked", "dg_grouped_fp8_masked_noalloc",
            "dg_wgrad_fp8_nt", "dg_k_grouped_wgrad_fp8_nt", "dg_gemm_fp8_nt_ue8m0", "dg_gemm_fp8_nt_ue8m0_packed", "dg_grouped_fp8_contiguous_ue8m0_packed",
-           "dg_grouped_fp8_masked_ue8m0_packed", "dg_gemm_bf16_nt", "dg_quantize_fp8_1x128",
+           "dg_grouped_fp8_masked_ue8m0_packed", "dg_gemm_bf16_nt", "dg_grouped_bf16_contiguous", "dg_grouped_bf16_masked", "dg_quantize_fp8_1x128",
            "dg_quantize_fp8_128x128", "dg_quantize_fp8_1x128_transposed", "dg_swiglu_quantize_fp8_1x128",
            "dg_quantize_fp8_1x128_ue8m0", "dg_quantize_fp8_128x128_ue8m0"):
     getattr(_lib, _f).restype = ctypes.c_int
@@ -68,7 +70,7 @@ _lib.dg_select_config.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, ctypes.POI
 _lib.dg_select_config.restype = ctypes.c_int
 
 (KIND_DENSE, KIND_CONTIGUOUS, KIND_MASKED, KIND_WGRAD, KIND_K_GROUPED_WGRAD, KIND_DENSE_POW2, KIND_BF16,
- KIND_CONTIGUOUS_SWIGLU, KIND_CONTIGUOUS_POW2, KIND_MASKED_POW2) = range(10)
+ KIND_CONTIGUOUS_SWIGLU, KIND_CONTIGUOUS_POW2, KIND_MASKED_POW2, KIND_CONTIGUOUS_BF16, KIND_MASKED_BF16) = range(12)
 FP8 = torch.float8_e4m3fn
 
 
@@ -219,6 +221,38 @@ def _scale_cols(sa, sb, k, packed):
         if t.dtype != torch.int32:
             raise TypeError(f"{name} must be int32 (packed UE8M0), got {t.dtype}")
     return (k // 128 + 3) // 4
+
+
+def dg_grouped_bf16_contiguous(a, b, c, m_indices):
+    """Contiguous MoE layout in BF16: a [M_total,K], b [G,N,K], c [M_total,N]
+    bf16, m_indices [M_total] int32 (see include/dg.h)."""
+    for t, name in ((a, "a"), (b, "b"), (c, "c")):
+        _bf16(t, name)
+    m_total, k = a.shape
+    g, n, _ = b.shape
+    _shape(b, (g, n, k), "b"); _shape(c, (m_total, n), "c"); _shape(m_indices, (m_total,), "m_indices")
+    if m_indices.dtype != torch.int32:
+        raise TypeError("m_indices must be int32")
+    _dev(a, b, c, m_indices)
+    _check(_lib.dg_grouped_bf16_contiguous(_ptr(a), _ptr(b), _ptr(c), _ptr(m_indices), m_total, n, k, g, _stream(c)),
+           "dg_grouped_bf16_contiguous")
+    return c
+
+
+def dg_grouped_bf16_masked(a, b, c, masked_m):
+    """Masked MoE layout in BF16: a [G,M_max,K], b [G,N,K], c [G,M_max,N] bf16,
+    masked_m [G] int32 (see include/dg.h)."""
+    for t, name in ((a, "a"), (b, "b"), (c, "c")):
+        _bf16(t, name)
+    g, m_max, k = a.shape
+    n = b.shape[1]
+    _shape(b, (g, n, k), "b"); _shape(c, (g, m_max, n), "c"); _shape(masked_m, (g,), "masked_m")
+    if masked_m.dtype != torch.int32:
+        raise TypeError("masked_m must be int32")
+    _dev(a, b, c, masked_m)
+    _check(_lib.dg_grouped_bf16_masked(_ptr(a), _ptr(b), _ptr(c), _ptr(masked_m), g, m_max, n, k, _stream(c)),
+           "dg_grouped_bf16_masked")
+    return c
 
 
 def dg_grouped_fp8_contiguous(a, sa, b, sb, c, m_indices):
@@ -453,6 +487,14 @@ def m_grouped_gemm_fp8_fp8_fp8_nt_contiguous_swiglu(lhs, rhs, m_indices):
     return dg_grouped_fp8_contiguous_swiglu(
         lhs[0], lhs[1], rhs[0], rhs[1], torch.empty((m_total, i), dtype=FP8, device=dev),
         torch.empty((m_total, i // 128), dtype=torch.float32, device=dev), m_indices)
+
+
+def m_grouped_gemm_bf16_bf16_bf16_nt_contiguous(lhs, rhs, out, m_indices):
+    return dg_grouped_bf16_contiguous(lhs, rhs, out, m_indices)
+
+
+def m_grouped_gemm_bf16_bf16_bf16_nt_masked(lhs, rhs, out, masked_m):
+    return dg_grouped_bf16_masked(lhs, rhs, out, masked_m)
 
 
 def m_grouped_gemm_fp8_fp8_bf16_nt_masked(lhs, rhs, out, masked_m):

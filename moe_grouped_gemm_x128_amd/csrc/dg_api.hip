@@ -523,6 +523,46 @@ dg_status dg_gemm_bf16_nt(const void* a, const void* b, void* c, int m, int n, i
   return run(dg::KIND_BF16, p, m, n, 2 * k, 1, stream);
 }
 
+dg_status dg_grouped_bf16_contiguous(const void* a, const void* b, void* c, const int32_t* m_indices, int m_total,
+                                     int n, int k, int num_groups, hipStream_t stream) {
+  if (!a || !b || !c || !m_indices) return DG_ERROR_INVALID_VALUE;
+  if (m_total <= 0 || n <= 0 || k <= 0 || num_groups <= 0) return DG_ERROR_INVALID_VALUE;
+  if (k % 64 != 0 || k > (1 << 22) || m_total % 128 != 0) return DG_ERROR_UNSUPPORTED;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, 2) || !aligned(m_indices, 4)) return DG_ERROR_UNSUPPORTED;
+  dg::Params p = base_params();
+  p.a = static_cast<const uint8_t*>(a);
+  p.b = static_cast<const uint8_t*>(b);
+  p.out = c;
+  p.ctrl = m_indices;
+  p.m = m_total;
+  p.n = n;
+  p.lda = 2 * k;    // bytes per row
+  p.kbs = k / 64;   // 128-byte K blocks
+  p.groups = num_groups;
+  p.vec_out = (n % 4 == 0) && aligned(c, 8);
+  return run(dg::KIND_CONTIG_BF16, p, m_total, n, 2 * k, 1, stream);
+}
+
+dg_status dg_grouped_bf16_masked(const void* a, const void* b, void* c, const int32_t* masked_m, int num_groups,
+                                 int m_max, int n, int k, hipStream_t stream) {
+  if (!a || !b || !c || !masked_m) return DG_ERROR_INVALID_VALUE;
+  if (num_groups <= 0 || m_max <= 0 || n <= 0 || k <= 0) return DG_ERROR_INVALID_VALUE;
+  if (k % 64 != 0 || k > (1 << 22)) return DG_ERROR_UNSUPPORTED;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, 2) || !aligned(masked_m, 4)) return DG_ERROR_UNSUPPORTED;
+  dg::Params p = base_params();
+  p.a = static_cast<const uint8_t*>(a);
+  p.b = static_cast<const uint8_t*>(b);
+  p.out = c;
+  p.ctrl = masked_m;
+  p.m = m_max;
+  p.n = n;
+  p.lda = 2 * k;
+  p.kbs = k / 64;
+  p.groups = num_groups;
+  p.vec_out = (n % 4 == 0) && aligned(c, 8);
+  return run(dg::KIND_MASKED_BF16, p, m_max, n, 2 * k, num_groups, stream);
+}
+
 dg_status dg_grouped_fp8_contiguous(const void* a, const float* sa, const void* b, const float* sb,
                                     void* c, const int32_t* m_indices, int m_total, int n, int k,
                                     int num_groups, hipStream_t stream) {
@@ -708,16 +748,16 @@ const char* dg_status_string(dg_status s) {
 dg_status dg_select_config(int kind, int m, int n, int k, int num_groups, int num_cus,
                            dg_tile_config* out) {
   if (!out) return DG_ERROR_INVALID_VALUE;
-  if (kind < DG_KIND_DENSE || kind > DG_KIND_MASKED_POW2) return DG_ERROR_INVALID_VALUE;
+  if (kind < DG_KIND_DENSE || kind > DG_KIND_MASKED_BF16) return DG_ERROR_INVALID_VALUE;
   if (kind == DG_KIND_CONTIGUOUS_SWIGLU && (n % 256 != 0 || m % 128 != 0)) return DG_ERROR_UNSUPPORTED;
   if (m <= 0 || n <= 0 || k <= 0 || num_groups <= 0 || num_cus <= 0) return DG_ERROR_INVALID_VALUE;
-  if (kind == DG_KIND_BF16 && k > (1 << 22)) return DG_ERROR_UNSUPPORTED;
+  if (dg::bf16_kind(kind) && k > (1 << 22)) return DG_ERROR_UNSUPPORTED;
   dg::Params p = base_params();
   Launch l;
   const int groups =
       (dg::layout_of(kind) == DG_KIND_MASKED || kind == DG_KIND_K_GROUPED_WGRAD) ? num_groups : 1;
   // the planner counts K in 128-byte blocks: BF16 rows are 2K bytes long
-  dg_status st = plan(kind, m, n, kind == DG_KIND_BF16 ? 2 * k : k, groups, num_cus, true, p, l);
+  dg_status st = plan(kind, m, n, dg::bf16_kind(kind) ? 2 * k : k, groups, num_cus, true, p, l);
   if (st != DG_SUCCESS) return st;
   out->block_m = l.shape.bm;
   out->block_n = l.shape.bn;

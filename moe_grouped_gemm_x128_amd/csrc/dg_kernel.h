@@ -24,15 +24,21 @@ enum Kind : int {
                            // fp8 q [M_tot,I] with 1x128 scales [M_tot,I/128] (out, out_scale)
   KIND_CONTIG_POW2 = 8,    // KIND_CONTIGUOUS with power-of-two scales applied by the block-scaled MFMA
   KIND_MASKED_POW2 = 9,    // KIND_MASKED with power-of-two scales applied by the block-scaled MFMA
+  KIND_CONTIG_BF16 = 10,   // KIND_CONTIGUOUS with bf16 operands and no scales (as KIND_BF16)
+  KIND_MASKED_BF16 = 11,   // KIND_MASKED with bf16 operands and no scales (as KIND_BF16)
 };
 
-// The operand layout and scheduling of a kind (the power-of-two kinds share
-// their fp32-scale kind's).
+// The operand layout and scheduling of a kind (the power-of-two and the
+// grouped bf16 kinds share their fp32-scale kind's; the dense bf16 kind
+// keeps its own).
 constexpr int layout_of(int kind) {
-  return kind == KIND_DENSE_POW2    ? KIND_DENSE
-         : kind == KIND_CONTIG_POW2 ? KIND_CONTIGUOUS
-         : kind == KIND_MASKED_POW2 ? KIND_MASKED
-                                    : kind;
+  return kind == KIND_DENSE_POW2                                 ? KIND_DENSE
+         : kind == KIND_CONTIG_POW2 || kind == KIND_CONTIG_BF16 ? KIND_CONTIGUOUS
+         : kind == KIND_MASKED_POW2 || kind == KIND_MASKED_BF16 ? KIND_MASKED
+                                                                 : kind;
+}
+constexpr bool bf16_kind(int kind) {
+  return kind == KIND_BF16 || kind == KIND_CONTIG_BF16 || kind == KIND_MASKED_BF16;
 }
 constexpr bool pow2_kind(int kind) {
   return kind == KIND_DENSE_POW2 || kind == KIND_CONTIG_POW2 || kind == KIND_MASKED_POW2;

@@ -213,7 +213,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   constexpr bool kRowScaleB = (KIND == KIND_WGRAD || KIND == KIND_KGROUPED);
   constexpr int LAYOUT = layout_of(KIND);            // dense, contiguous or masked scheduling
   constexpr bool kPow2 = pow2_kind(KIND);             // scales applied by the MFMA
-  constexpr bool kBf16 = (KIND == KIND_BF16);         // no scales at all
+  constexpr bool kBf16 = bf16_kind(KIND);              // bf16 operands, no scales at all
   // contiguous layout with the SwiGLU + re-quantise epilogue: the tile's B
   // rows are 128 gate rows and the 128 matching up rows, in LDS order
   // [wave][gate 16 | up 16], so fragment 0 of a wave holds the gate and
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   // contiguous -4%).  Decided per instance at compile time: a runtime choice
   // in the DMA loop cost the 256x256 instances registers (spills in the loop).
   constexpr bool kStreamB =
-      ((LAYOUT == KIND_DENSE || kBf16) && BM <= 128) || LAYOUT == KIND_MASKED;
+      ((LAYOUT == KIND_DENSE || KIND == KIND_BF16) && BM <= 128) || LAYOUT == KIND_MASKED;
   constexpr bool kDirectAcc = kPow2 || kBf16;         // MFMAs accumulate into acc: no promotion
   constexpr bool kFp32Out = kRowScaleB;
   // the columns of one wave tile sit inside one 128-block: one sb per wave
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     }
   }
   // split-K: `splits` consecutive work items share one output tile
-  constexpr bool kCanSplit = (LAYOUT == KIND_DENSE || LAYOUT == KIND_MASKED || kBf16);
+  constexpr bool kCanSplit = (LAYOUT == KIND_DENSE || LAYOUT == KIND_MASKED || KIND == KIND_BF16);
   const int splits = kCanSplit ? p.splits : 1;
   const int TS = T * splits;
   const int per_xcd = (TS + 7) >> 3;
@@ -1116,6 +1116,12 @@ hipError_t launch_shape(int kind, const Params& p, int grid, hipStream_t stream)
       break;
     case KIND_MASKED_POW2:
       launch_kind<BM, BN, WM, WN, S, KIND_MASKED_POW2>(g, b, stream, p);
+      break;
+    case KIND_CONTIG_BF16:
+      launch_kind<BM, BN, WM, WN, S, KIND_CONTIG_BF16>(g, b, stream, p);
+      break;
+    case KIND_MASKED_BF16:
+      launch_kind<BM, BN, WM, WN, S, KIND_MASKED_BF16>(g, b, stream, p);
       break;
     default:
       return hipErrorInvalidValue;

@@ -6,7 +6,7 @@
 namespace dg {
 
 bool has_instance(int kind, const TileShape& s) {
-  if (kind < KIND_DENSE || kind > KIND_MASKED_POW2) return false;
+  if (kind < KIND_DENSE || kind > KIND_MASKED_BF16) return false;
 #define X(BM, BN, WM, WN, S) \
   if (s.bm == BM && s.bn == BN && s.wm == WM && s.wn == WN) return !excluded(BM, BN, WM, kind);
   DG_SHAPES(X)

@@ -394,6 +394,34 @@ def gemm_bf16_nt_at(a, b, rows, cols):
     return out
 
 
+def grouped_contiguous_bf16(a, b, m_indices, c_init):
+    """Contiguous MoE in BF16: the rows whose expert id is e in [0, G) are the
+    BF16 oracle's product of those rows of A with B[e]; every other row keeps
+    c_init.  Returns (C bf16 bits, exact fp64 with NaN on untouched rows)."""
+    a, b = np.asarray(a, np.uint16), np.asarray(b, np.uint16)
+    ids = np.asarray(m_indices)
+    c = np.array(c_init, np.uint16, copy=True)
+    x = np.full(c.shape, np.nan)
+    for e in range(b.shape[0]):
+        rows = np.flatnonzero(ids == e)
+        if rows.size:
+            c[rows], x[rows] = gemm_bf16_nt(a[rows], b[e])
+    return c, x
+
+
+def grouped_masked_bf16(a, b, masked_m, c_init):
+    """Masked MoE in BF16: rows r < clamp(masked_m[g], 0, M_max) of group g are
+    the BF16 oracle's product of A[g, :r] with B[g]; other rows keep c_init."""
+    a, b = np.asarray(a, np.uint16), np.asarray(b, np.uint16)
+    c = np.array(c_init, np.uint16, copy=True)
+    x = np.full(c.shape, np.nan)
+    for g in range(a.shape[0]):
+        v = int(min(max(int(masked_m[g]), 0), a.shape[1]))
+        if v:
+            c[g, :v], x[g, :v] = gemm_bf16_nt(a[g, :v], b[g])
+    return c, x
+
+
 # ---- SwiGLU then 1x128 quantise (dg_quant_oracle.c) ----
 
 def swiglu_quantize_1x128(c: np.ndarray):

@@ -23,7 +23,7 @@ int main(void) {
   const int ks[] = {128, 512, 2048, 4608, 7168, 16384, 1 << 20};
   const int gs[] = {1, 2, 4, 16, 256};
   long plans = 0;
-  for (int kind = 0; kind <= 9; ++kind)
+  for (int kind = 0; kind <= 11; ++kind)
     for (unsigned a = 0; a < sizeof(ms) / sizeof(ms[0]); ++a)
       for (unsigned b = 0; b < sizeof(ns) / sizeof(ns[0]); ++b)
         for (unsigned c = 0; c < sizeof(ks) / sizeof(ks[0]); ++c)
@@ -33,7 +33,8 @@ int main(void) {
               const dg_status s = dg_select_config(kind, ms[a], ns[b], ks[c], gs[d], cus, &cfg);
               if (s != DG_SUCCESS) continue;
               ++plans;
-              const int kblocks = (kind == DG_KIND_BF16 ? 2 * ks[c] : ks[c]) / 128;
+              const int bf16 = kind == DG_KIND_BF16 || kind == DG_KIND_CONTIGUOUS_BF16 || kind == DG_KIND_MASKED_BF16;
+              const int kblocks = (bf16 ? 2 * ks[c] : ks[c]) / 128;
               CHECK(cfg.block_m > 0 && cfg.block_n > 0 && cfg.block_n % 16 == 0);
               CHECK(cfg.waves_m > 0 && cfg.waves_n > 0);
               CHECK(cfg.tiles >= 1 && cfg.grid >= 1);
@@ -44,7 +45,7 @@ int main(void) {
   CHECK(plans > 1000);
   /* rejected queries */
   dg_tile_config cfg;
-  CHECK(dg_select_config(10, 128, 128, 128, 1, 256, &cfg) == DG_ERROR_INVALID_VALUE);
+  CHECK(dg_select_config(12, 128, 128, 128, 1, 256, &cfg) == DG_ERROR_INVALID_VALUE);
   CHECK(dg_select_config(7, 128, 384, 128, 1, 256, &cfg) == DG_ERROR_UNSUPPORTED);
   CHECK(dg_select_config(0, 0, 128, 128, 1, 256, &cfg) == DG_ERROR_INVALID_VALUE);
   CHECK(dg_select_config(0, 128, 128, 128, 1, 256, NULL) == DG_ERROR_INVALID_VALUE);
@@ -57,6 +58,8 @@ int main(void) {
   CHECK(dg_gemm_fp8_nt(mis, f, p, f, p, 1, 1, 128, NULL) == DG_ERROR_UNSUPPORTED);
   CHECK(dg_gemm_fp8_nt_ue8m0(p, f, p, f, p, -1, 1, 128, NULL) == DG_ERROR_INVALID_VALUE);
   CHECK(dg_gemm_bf16_nt(p, p, p, 1, 1, 100, NULL) == DG_ERROR_UNSUPPORTED);
+  CHECK(dg_grouped_bf16_contiguous(p, p, p, NULL, 128, 8, 128, 2, NULL) == DG_ERROR_INVALID_VALUE);
+  CHECK(dg_grouped_bf16_masked(p, p, p, (const int32_t*)p, 2, 256, 8, 100, NULL) == DG_ERROR_UNSUPPORTED);
   CHECK(dg_grouped_fp8_contiguous(p, f, p, f, p, (const int32_t*)p, 100, 8, 128, 2, NULL) == DG_ERROR_UNSUPPORTED);
   CHECK(dg_grouped_fp8_contiguous(p, f, p, f, p, NULL, 128, 8, 128, 2, NULL) == DG_ERROR_INVALID_VALUE);
   CHECK(dg_grouped_fp8_contiguous_swiglu(p, f, p, f, p, (float*)p, (const int32_t*)p, 128, 384, 128, 2, NULL) ==

@@ -164,6 +164,22 @@ def test_ue8m0_packed_argument_errors(lib):
     assert f(A16, A16, A16 + 8, A16, A16, 1, 1, 128, None) == UNSUPPORTED    # b alignment
 
 
+def test_grouped_bf16_argument_errors(lib):
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    fc = lib.dg_grouped_bf16_contiguous
+    fc.argtypes = [vp] * 4 + [i] * 4 + [vp]
+    assert fc(A16, A16, A16, None, 256, 512, 128, 2, None) == INVALID     # m_indices
+    assert fc(A16, A16, A16, A16, 256, 512, 96, 2, None) == UNSUPPORTED   # K % 64
+    assert fc(A16, A16, A16, A16, 200, 512, 128, 2, None) == UNSUPPORTED  # M_total % 128
+    assert fc(A16, A16 + 8, A16, A16, 256, 512, 128, 2, None) == UNSUPPORTED
+    fm = lib.dg_grouped_bf16_masked
+    fm.argtypes = [vp] * 4 + [i] * 4 + [vp]
+    assert fm(A16, A16, A16, None, 2, 256, 512, 128, None) == INVALID      # masked_m
+    assert fm(A16, A16, A16, A16, 0, 256, 512, 128, None) == INVALID       # G
+    assert fm(A16, A16, A16, A16, 2, 256, 512, 1 << 23, None) == UNSUPPORTED
+    assert fm(A16, A16, MIS, A16, 2, 256, 512, 128, None) == UNSUPPORTED   # c alignment
+
+
 def test_grouped_ue8m0_packed_argument_errors(lib):
     vp, i = ctypes.c_void_p, ctypes.c_int
     fc = lib.dg_grouped_fp8_contiguous_ue8m0_packed
@@ -257,6 +273,7 @@ SHAPES += [(1, 32768, 4096, 7168, 4), (1, 65536, 7168, 2048, 8), (2, 256, 4096, 
            (2, 256, 7168, 2048, 16), (3, 7168, 2048, 4096, 1), (4, 7168, 2048, 10240, 4)]
 SHAPES += [(5, m, 7168, 16384, 1) for m in (64, 4096)] + [(6, m, 7168, 8192, 1) for m in (64, 4096)]
 SHAPES += [(8, 32768, 4096, 7168, 4), (9, 256, 4096, 7168, 1), (9, 256, 7168, 2048, 16)]
+SHAPES += [(10, 32768, 4096, 7168, 4), (11, 256, 4096, 7168, 1), (11, 256, 7168, 2048, 16)]
 
 
 @pytest.mark.parametrize("kind,m,n,k,g", SHAPES)
@@ -264,14 +281,14 @@ def test_heuristic_invariants(lib, kind, m, n, k, g):
     c = _cfg(lib, kind, m, n, k, g)
     assert c["waves_m"] * c["waves_n"] in (4, 8)
     assert c["block_m"] % (16 * c["waves_m"]) == 0 and c["block_n"] % (16 * c["waves_n"]) == 0
-    groups = g if kind in (2, 4, 9) else 1
+    groups = g if kind in (2, 4, 9, 11) else 1
     tiles = groups * -(-m // c["block_m"]) * -(-n // c["block_n"])
     assert c["tiles"] == tiles
     s = c["k_splits"]
     assert 1 <= s <= 16
-    if kind not in (0, 2, 5, 6, 9):
+    if kind not in (0, 2, 5, 6, 9, 11):
         assert s == 1  # split K only for the bf16-output dense and masked layouts
-    kbs = k // 64 if kind == 6 else k // 128  # BF16: K blocks of 64 values (128 bytes)
+    kbs = k // 64 if kind in (6, 10, 11) else k // 128  # BF16: K blocks of 64 values (128 bytes)
     if s > 1:
         chunk = -(-kbs // s)
         assert -(-kbs // chunk) == s, "a split would be empty"
@@ -333,7 +350,7 @@ def test_heuristic_rejects_bad_queries(lib):
     c = ctypes.c_int * 8
     out = c()
     lib.dg_select_config.argtypes = [ctypes.c_int] * 6 + [ctypes.c_void_p]
-    assert lib.dg_select_config(10, 1, 1, 128, 1, 256, ctypes.addressof(out)) == INVALID
+    assert lib.dg_select_config(12, 1, 1, 128, 1, 256, ctypes.addressof(out)) == INVALID
     assert lib.dg_select_config(-1, 1, 1, 128, 1, 256, ctypes.addressof(out)) == INVALID
     # the fused SwiGLU kind needs N % 256 == 0 and M % 128 == 0
     assert lib.dg_select_config(7, 128, 384, 128, 1, 256, ctypes.addressof(out)) == UNSUPPORTED

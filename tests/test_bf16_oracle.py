@@ -134,3 +134,36 @@ def test_planted_bf16_mistake_is_caught(name, tmp_path):
             if not ok:
                 failed.append(n)
     assert failed, f"planted mistake {name} was not caught by any pin"
+
+
+# ---- the grouped BF16 compositions (oracle.grouped_contiguous_bf16 / _masked_bf16) ----
+
+def test_grouped_bf16_compositions_against_the_dense_oracle():
+    """One expert owning every row is the dense oracle; padding rows, ids past
+    G and rows past masked_m keep their initial bits; renumbering the experts
+    (ids and B slices alike) leaves the result unchanged; masked_m beyond M_max
+    is M_max."""
+    from harness import inputs
+    x = inputs.make_contiguous_bf16(3, 128, 70, 192, seed=inputs.SEED_BASE + 40, max_pad=60)
+    init = np.full((x.a.shape[0], 70), 0xFFFF, np.uint16)
+    ones = np.zeros(x.a.shape[0], np.int32)
+    c1, _ = oracle.grouped_contiguous_bf16(x.a, x.b[:1], ones, init)
+    d1, _ = oracle.gemm_bf16_nt(x.a, x.b[0])
+    assert np.array_equal(c1, d1)
+    ids = x.ctrl.copy()
+    ids[:7] = 9                                     # past G: skipped
+    c, _ = oracle.grouped_contiguous_bf16(x.a, x.b, ids, init)
+    keep = (ids < 0) | (ids >= 3)
+    assert np.all(c[keep] == 0xFFFF) and not np.any(c[~keep] == 0xFFFF)
+    perm = np.array([2, 0, 1])                     # expert e becomes perm[e]
+    ids2 = np.where((ids >= 0) & (ids < 3), perm[np.clip(ids, 0, 2)], ids).astype(np.int32)
+    b2 = np.empty_like(x.b)
+    b2[perm] = x.b
+    c2, _ = oracle.grouped_contiguous_bf16(x.a, b2, ids2, init)
+    assert np.array_equal(c, c2)
+    y = inputs.make_masked_bf16(3, 40, 50, 128, seed=inputs.SEED_BASE + 41, masked_m=[0, 17, 99])
+    init = np.full((3, 40, 50), 0xFFFF, np.uint16)
+    cm, _ = oracle.grouped_masked_bf16(y.a, y.b, y.ctrl, init)
+    assert np.all(cm[0] == 0xFFFF) and np.all(cm[1, 17:] == 0xFFFF)
+    assert np.array_equal(cm[1, :17], oracle.gemm_bf16_nt(y.a[1, :17], y.b[1])[0])
+    assert np.array_equal(cm[2], oracle.gemm_bf16_nt(y.a[2], y.b[2])[0])
