@@ -245,7 +245,27 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   static_assert(S >= 2, "at least double buffering");
 
   // ---- LDS stage layout and DMA pieces ----
-  constexpr int SA_N = ((BM + 63) / 64) * 64;                   // floats
+  // Row scales of A in groups of kGrp K blocks (contiguous layout, two-stage
+  // rings): a tile's sa for its K blocks 4g .. 4g+3 is fetched once, at the
+  // start of the block before 4g, into one of two group buffers after the
+  // ring.  Each lane of a group piece reads one scale word of row l/4 (16
+  // rows x 4 words per piece), so a piece touches 16 rows' cache lines
+  // instead of 64 and each row once per four K blocks instead of every
+  // block.  A per-block sa piece touches one line per row (rows K/128 words
+  // apart), which costs the texture path more than the operand pieces' whole
+  // lines where sa misses the L2: the contiguous layout's sa (all tokens'
+  // rows) is 4-8x the dense shapes'.  Measured: contiguous G=8, N=4096,
+  // K=7168 4-5% faster; the dense shapes, whose sa stays in the L2 when
+  // warm, 4-5% slower warm (3-5% faster cold), so they keep per-block
+  // pieces, and so do deeper rings (a group buffer would still be read when
+  // the next tile's first group lands in it).
+  constexpr bool kSaGrp = (S == 2) && !kBf16 && kContig;
+  constexpr int kGrp = 4;
+  constexpr int SAG_ROWS = ((BM + 15) / 16) * 16;
+  constexpr int SAG_BYTES = SAG_ROWS * 16;                       // [row][4 words]
+  constexpr int PSAG = kSaGrp ? SAG_ROWS / 16 : 0;               // group pieces
+  constexpr int QSAG = (PSAG + NW - 1) / NW;
+  constexpr int SA_N = kSaGrp ? 0 : ((BM + 63) / 64) * 64;      // floats per stage
   constexpr int SB_N = kRowScaleB ? ((BN + 63) / 64) * 64 : 64;  // floats
   constexpr int OFF_A = 0;
   constexpr int OFF_B = BM * kBK;
@@ -266,7 +286,9 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   constexpr int DMIN = QA + QB + QS;
   static_assert(BN % 16 == 0, "whole 16-column fragments");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE + 1024];  // + padding-DMA sink
+  // + padding-DMA sink (1 KB) + the two sa group buffers
+  constexpr int OFF_G = S * STAGE + 1024;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[OFF_G + (kSaGrp ? 2 * SAG_BYTES : 0)];
   // bf16 epilogue staging: a wave's 16-row fragment row goes through LDS so
   // that each store covers whole (64 columns) or half (32 columns) 128-byte
   // lines; rows padded by 16 bytes against bank conflicts
@@ -446,7 +468,9 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   struct Res {
     Rsrc a, b;
     Rsrc s[QS];
+    Rsrc sa;   // sa rows of the tile (grouped sa)
     int kb0, nkb;
+    int gpar;  // group buffer of the tile's first sa group
   };
   // r advanced by `bytes` with its range cut where it ended (empty if that is
   // past the end or !on); wave-uniform
@@ -487,8 +511,10 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
       const Rsrc src{is_a ? sa.lo : sb.lo, is_a ? sa.hi : sb.hi, is_a ? sa.num : sb.num, sa.flags};
       r.s[q] = moved(src, rowoff, sp < PS);
     }
+    r.sa = sa;
     r.kb0 = x.kb0;
     r.nkb = x.live ? x.nkb : 0;
+    r.gpar = 0;
     return r;
   };
   // Cross-tile prefetch: the DMAs of the next tile's first S-1 K blocks are
@@ -519,13 +545,15 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   int t_next = blockIdx.x;
   Tile cur = next_live(t_next);
   int qbase = 0;        // ring stage of the current tile's first K block
+  int gpar = 0;         // sa group buffer of the current tile's first group
   bool first = true;
   while (cur.live) {
     // the next tile: looked up (with cross-tile prefetch) only before the
     // current tile's last S-1 K blocks, so its state is not live in the main
     // part of the K loop (registers)
     Tile nxt = decode(t_end);
-    const Res rc = make_res(cur);
+    Res rc = make_res(cur);
+    rc.gpar = gpar;
     const int n0 = cur.n0, rows = cur.rows, nkb = cur.nkb, split = cur.split;
     const int64_t out_row0 = cur.out_row0;
 
@@ -548,6 +576,10 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     // fused SwiGLU: the B scale piece's lane 1 reads the up block I/128 blocks
     // on, so the stage holds sb(gate) at 0 and sb(up) at 1
     const uint32_t svoff_b = kSwiGLU && lane == 1 ? (uint32_t)(p.n / 2 / kBK) * p.sks * 4 : svoff;
+    // sa group pieces: lane l reads word l%4 of the group in row l/4 of the
+    // piece (rows 16*pg .. 16*pg+15 of the tile)
+    const uint32_t gvoff = (uint32_t)((lane >> 2) + 16 * wave) * p.sks * 4 + (uint32_t)(lane & 3) * 4;
+    const uint32_t gstep = (uint32_t)(16 * NW) * p.sks * 4;  // rows between a wave's pieces
 
     // The DMAs of one K block: each source moved to the block (empty past
     // the tile's K range or for a dead tile: such a block reads zeros and
@@ -558,7 +590,9 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     // block instead of stalling every wave at the same point.
     struct Blk {
       v4i a, b, s[QS];
-      uint32_t base;
+      v4i g;  // sa rows of the tile at the group's first word (a group's first block only)
+      uint32_t base, gbase;
+      bool grp;
     };
     // A source moved to K byte offset `koff` of its rows (scalar arithmetic):
     // a non-empty range holds at least one row, which is longer than any K
@@ -579,6 +613,16 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
 #pragma unroll
       for (int q = 0; q < QS; ++q) d.s[q] = at_k(r.s[q], (kb >> p.spk) * 4, live);
       d.base = __builtin_amdgcn_readfirstlane(smem_lds + st * STAGE);
+      d.grp = false;
+      d.gbase = 0;
+      if constexpr (kSaGrp) {
+        // the group's words: fp32 scales of blocks kb .. kb+3, or the packed
+        // words from the one holding block kb on (a group of four blocks
+        // spans at most two of them)
+        d.grp = live && (rel % kGrp) == 0;
+        d.g = at_k(r.sa, (p.spk ? (kb >> 2) : kb) * 4, d.grp);
+        d.gbase = __builtin_amdgcn_readfirstlane(smem_lds + OFF_G + ((r.gpar + rel / kGrp) & 1) * SAG_BYTES);
+      }
       return d;
     };
     constexpr int ND = QA + QB + QS;
@@ -618,6 +662,19 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
         if (QA + QB + q < lo || QA + QB + q >= hi) continue;
         const int sp = wave + NW * q;
         dma4(sp < PS ? d.base + OFF_SA + sp * 256 : smem_lds + S * STAGE, d.s[q], sp < PSA ? svoff : svoff_b);
+      }
+      if (lo < 0 && kSaGrp) {
+        // the block's sa group (issue(d, -1, -1) at a block start, not
+        // spread over the fragment groups: a branch among the MFMAs costs
+        // registers); pieces past the tile's rows read nothing into the sink
+#pragma unroll
+        for (int q = 0; q < QSAG; ++q) {
+          const int pg = wave + NW * q;
+          const bool real = PSAG % NW == 0 || pg < PSAG;
+          v4i rq = d.g;
+          rq[2] = real ? d.g[2] : 0;
+          dma4(real ? d.gbase + pg * 256 : smem_lds + S * STAGE, rq, gvoff + q * gstep);
+        }
       }
     };
     const int qs = qbase % S;
@@ -702,7 +759,11 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
       if (first || !xfer) {
   #pragma unroll
         for (int s = 0; s < S - 1; ++s)
-          if (s < nkb) issue(blk_of(rc, s, (qs + s) % S), 0, ND);
+          if (s < nkb) {
+            const Blk d0 = blk_of(rc, s, (qs + s) % S);
+            issue(d0, 0, ND);
+            if constexpr (kSaGrp) issue(d0, -1, -1);  // (s == 0 starts a group)
+          }
       }
 
       // one K block; `dma` is the block issued during it (S-1 ahead)
@@ -729,6 +790,11 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
         const uint8_t* sA = smem + st * STAGE + OFF_A;
         const uint8_t* sB = smem + st * STAGE + OFF_B;
         const float* sSA = reinterpret_cast<const float*>(smem + st * STAGE + OFF_SA);
+        // grouped sa: this block's word of each row in its group's buffer
+        const float* sSG = reinterpret_cast<const float*>(smem + OFF_G + ((rc.gpar + rel / kGrp) & 1) * SAG_BYTES);
+        const int kbr = rc.kb0 + rel;
+        const int gw = p.spk ? (kbr >> 2) - ((kbr - rel % kGrp) >> 2) : rel % kGrp;
+        auto sa_row = [&](int r) -> float { return kSaGrp ? sSG[4 * r + gw] : sSA[r]; };
         const float* sSB = reinterpret_cast<const float*>(smem + st * STAGE + OFF_SB);
         const uint8_t* wA = sA + wm * WTM * kBK;  // this wave's first A row
         const uint8_t* wB = sB + wn * WTN * kBK;  // this wave's first B row
@@ -751,10 +817,10 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
         // LDS read it has just issued; only three scales are live);
         // otherwise all FM (resident, few) are read up front
         float sav[kStreamM ? 1 : FM];
-        float sa_next = (kStreamM && NOV > 0) ? sSA[wm * WTM + l16] : 0.f;
+        float sa_next = (kStreamM && NOV > 0) ? sa_row(wm * WTM + l16) : 0.f;
         if constexpr (!kStreamM) {
   #pragma unroll
-          for (int j = 0; j < FM; ++j) sav[j] = sSA[wm * WTM + 16 * j + l16];
+          for (int j = 0; j < FM; ++j) sav[j] = sa_row(wm * WTM + 16 * j + l16);
         }
         float sa_prev = 0.f, sa_cur = 0.f;
         // B scale per n-fragment (block scales) or per column quad (row scales)
@@ -791,6 +857,8 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
           else
             fma4(acc_at(NOV - 1, r), pend[r], part[r]);
         };
+        if constexpr (kSaGrp)
+          if (dma.grp) issue(dma, -1, -1);
         if constexpr (NOV == 0) issue(dma, 0, ND);  // no groups to spread over
 
   #pragma unroll
@@ -799,7 +867,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
           if (o + 1 < NOV) nxt = load_s(o + 1);
           if constexpr (kStreamM) {
             sa_cur = sa_next;
-            if (o + 1 < NOV) sa_next = sSA[wm * WTM + 16 * (o + 1) + l16];
+            if (o + 1 < NOV) sa_next = sa_row(wm * WTM + 16 * (o + 1) + l16);
           }
   #pragma unroll
           for (int r = 0; r < NR; ++r) {
@@ -856,7 +924,8 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
       // last S-1 blocks: the DMAs are the next tile's first blocks (cross-tile
       // prefetch), else dead blocks
       if (xfer) nxt = next_live(t_next);
-      const Res rn = make_res(nxt);
+      Res rn = make_res(nxt);
+      rn.gpar = (gpar + (nkb + kGrp - 1) / kGrp) & 1;
   #pragma unroll 1
       for (int rel = tail; rel < nkb; ++rel) block(rel, blk_of(rn, rel + S - 1 - nkb, (qs + rel + S - 1) % S));
   #pragma unroll
@@ -1070,6 +1139,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
     // ---- next tile ----
     if (!xfer) nxt = next_live(t_next);
     qbase += nkb;
+    gpar = (gpar + (nkb + kGrp - 1) / kGrp) & 1;
     cur = nxt;
     first = false;
   }
