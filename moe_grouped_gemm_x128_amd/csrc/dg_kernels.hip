@@ -626,10 +626,29 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
       return d;
     };
     constexpr int ND = QA + QB + QS;
+    // Piece order within a block: A, B, then the scale pieces -- except for
+    // the masked layout, whose scale pieces go first.  The wave's DMAs
+    // complete in issue order as far as its waits can tell, and a scale
+    // piece (one row per lane, a cache line each) takes longer than an
+    // operand piece (whole lines): issued last it holds up the wait for the
+    // whole block.  Measured: the masked decode G=16 7-10% faster; the dense
+    // small-M tiles mixed (-4% to +9%), the large tiles equal, so only the
+    // masked layout reorders.
+    constexpr bool kScalesFirst = (LAYOUT == KIND_MASKED);
+    constexpr int iA = kScalesFirst ? QS : 0, iB = iA + QA, iS = kScalesFirst ? 0 : QA + QB;
     auto issue = [&](const Blk& d, int lo, int hi) {
+      auto scales = [&]() {
+#pragma unroll
+        for (int q = 0; q < QS; ++q) {
+          if (iS + q < lo || iS + q >= hi) continue;
+          const int sp = wave + NW * q;
+          dma4(sp < PS ? d.base + OFF_SA + sp * 256 : smem_lds + S * STAGE, d.s[q], sp < PSA ? svoff : svoff_b);
+        }
+      };
+      if constexpr (kScalesFirst) scales();
 #pragma unroll
       for (int q = 0; q < QA; ++q)
-        if (q >= lo && q < hi) {
+        if (iA + q >= lo && iA + q < hi) {
           if constexpr (PA % NW == 0) {
             dma16(d.base + OFF_A + (wave + NW * q) * 1024, d.a, voff0 + q * step);
           } else {
@@ -642,7 +661,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
         }
 #pragma unroll
       for (int q = 0; q < QB; ++q) {
-        if (QA + q < lo || QA + q >= hi) continue;
+        if (iB + q < lo || iB + q >= hi) continue;
         const int pi = wave + NW * q;
         if constexpr (PB % NW == 0) {
           if constexpr (kStreamB)
@@ -657,12 +676,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
           dma16(real ? d.base + OFF_B + pi * 1024 : smem_lds + S * STAGE, rq, voff0 + q * step);
         }
       }
-#pragma unroll
-      for (int q = 0; q < QS; ++q) {
-        if (QA + QB + q < lo || QA + QB + q >= hi) continue;
-        const int sp = wave + NW * q;
-        dma4(sp < PS ? d.base + OFF_SA + sp * 256 : smem_lds + S * STAGE, d.s[q], sp < PSA ? svoff : svoff_b);
-      }
+      if constexpr (!kScalesFirst) scales();
       if (lo < 0 && kSaGrp) {
         // the block's sa group (issue(d, -1, -1) at a block start, not
         // spread over the fragment groups: a branch among the MFMAs costs
