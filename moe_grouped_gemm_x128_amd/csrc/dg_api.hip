@@ -117,8 +117,9 @@ struct Candidate {
 //     per CU) x (tile area / tile efficiency), so a large tile wins unless
 //     it leaves CUs idle.
 dg::TileShape heuristic(int kind, int rows, int n, int k, int groups, int num_cus, bool allow_split) {
-  // the fused SwiGLU epilogue has one tile: 128 gate + 128 up columns, 1x8 waves
-  if (kind == DG_KIND_CONTIGUOUS_SWIGLU) return dg::TileShape{256, 256, 1, 8};
+  // the fused SwiGLU epilogue's tile: 128 gate + 128 up columns on 2x4 waves
+  // (3-4% faster than 1x8, like the plain contiguous GEMM)
+  if (kind == DG_KIND_CONTIGUOUS_SWIGLU) return dg::TileShape{256, 256, 2, 4};
   const int kbs = k / 128;
   const bool long_k = allow_split && kbs >= 3 * kSplitMinBlocks;
   const int layout = dg::layout_of(kind);  // the power-of-two kinds plan as their fp32-scale kind

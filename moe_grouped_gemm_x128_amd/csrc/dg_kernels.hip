@@ -220,7 +220,8 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   // fragment 1 the up value of the same output element in the same lane
   constexpr bool kSwiGLU = (KIND == KIND_CONTIG_SWIGLU);
   constexpr bool kContig = (LAYOUT == KIND_CONTIGUOUS) || kSwiGLU;
-  static_assert(!kSwiGLU || (BM == 256 && BN == 256 && WM == 1 && WN == 8), "fused SwiGLU tile");
+  static_assert(!kSwiGLU || (BM == 256 && BN == 256 && ((WM == 1 && WN == 8) || (WM == 2 && WN == 4))),
+                "fused SwiGLU tile");
   // B loaded with the streaming (nontemporal) cache policy by the instances
   // whose launches read each B tile with one row of tiles: the dense tiles of
   // at most 128 rows (the heuristic's choice for M <= 128) and the masked
@@ -296,7 +297,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   constexpr int kStageRow = WTN * 2 + 16;
   __shared__ __attribute__((aligned(16))) uint8_t sOut[kStage ? NW : 1][kStage ? 16 * kStageRow : 16];
   // fused SwiGLU: each wave's |h| maximum over its 16 columns, per tile row
-  __shared__ __attribute__((aligned(16))) float sRowMax[kSwiGLU ? BM : 1][kSwiGLU ? NW : 4];
+  __shared__ __attribute__((aligned(16))) float sRowMax[kSwiGLU ? BM : 1][kSwiGLU ? WN : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -849,8 +850,8 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   #pragma unroll
           for (int i = 0; i < FN; ++i) sbv[i] = sb;
         } else if constexpr (kSwiGLU) {
-          sbv[0] = sSB[0];  // gate block
-          sbv[1] = sSB[1];  // up block
+  #pragma unroll
+          for (int i = 0; i < FN; ++i) sbv[i] = sSB[i & 1];  // gate block, up block, ...
         } else {
   #pragma unroll
           for (int i = 0; i < FN; ++i) sbv[i] = sSB[(n0 + wn * WTN + 16 * i) / kBK - n0 / kBK];
@@ -983,38 +984,52 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
       // h = silu(gate) * up on the bf16-rounded GEMM outputs (what the unfused
       // path stores and its SwiGLU kernel reads), then the 1x128 rule over the
       // tile's 128 output columns [n0, n0 + 128) of each row: the waves' |h|
-      // maxima over their 16 columns meet in LDS.  Lane (l16, lq) of fragment
-      // row j holds columns 16 wn + 4 lq .. + 3 of row 16 j + l16.
+      // maxima over their columns meet in LDS.  A wave's fragments 2q and
+      // 2q+1 are the gate and up values of its column pair q: lane (l16, lq)
+      // of fragment row j holds output columns n0 + (WTN/2) wn + 16 q + 4 lq
+      // .. + 3 of tile row wm WTM + 16 j + l16.
+      constexpr int NP = FN / 2;  // gate/up fragment pairs per wave
+      static_assert(FN % 2 == 0 && WN % 4 == 0, "SwiGLU pairs and row-maximum vectors");
       const int half = p.n / 2;
       auto bf16r = [](float x) { return __uint_as_float((uint32_t)f32_to_bf16(x) << 16); };
 #pragma unroll
       for (int j = 0; j < FM; ++j) {
         float m = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float h = codec::silu(bf16r(acc[0][j][e])) * bf16r(acc[1][j][e]);
-          acc[0][j][e] = h;
-          m = fmaxf(m, fabsf(h));
+        for (int q = 0; q < NP; ++q) {
+          float h[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            h[e] = codec::silu(bf16r(acc[2 * q][j][e])) * bf16r(acc[2 * q + 1][j][e]);
+            m = fmaxf(m, fabsf(h[e]));
+          }
+          acc[2 * q][j] = v4f{h[0], h[1], h[2], h[3]};
         }
         m = fmaxf(m, __shfl_xor(m, 16));
         m = fmaxf(m, __shfl_xor(m, 32));
-        if (lq == 0) sRowMax[16 * j + l16][wave] = m;
+        if (lq == 0) sRowMax[wm * WTM + 16 * j + l16][wn] = m;
       }
       barrier();  // every wave's maxima are in LDS
       uint8_t* qo = static_cast<uint8_t*>(p.out);
 #pragma unroll
       for (int j = 0; j < FM; ++j) {
-        const int r = 16 * j + l16;
-        const float4 a = *reinterpret_cast<const float4*>(&sRowMax[r][0]);
-        const float4 b = *reinterpret_cast<const float4*>(&sRowMax[r][4]);
-        const float amax = fmaxf(fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w)), fmaxf(fmaxf(b.x, b.y), fmaxf(b.z, b.w)));
+        const int r = wm * WTM + 16 * j + l16;
+        float amax = 0.f;
+#pragma unroll
+        for (int c = 0; c < WN; c += 4) {
+          const float4 a = *reinterpret_cast<const float4*>(&sRowMax[r][c]);
+          amax = fmaxf(amax, fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w)));
+        }
         const float sc = codec::scale_of(amax);
         const codec::GroupRecip gr = codec::group_recip(sc);
-        const uint32_t w = codec::encode4(codec::scaled(acc[0][j][0], gr), codec::scaled(acc[0][j][1], gr),
-                                          codec::scaled(acc[0][j][2], gr), codec::scaled(acc[0][j][3], gr));
         if (rbit(j, l16)) {
           const int64_t orow = out_row0 + r;
-          *reinterpret_cast<uint32_t*>(qo + orow * half + n0 + 16 * wn + 4 * lq) = w;
+#pragma unroll
+          for (int q = 0; q < NP; ++q) {
+            const uint32_t w = codec::encode4(codec::scaled(acc[2 * q][j][0], gr), codec::scaled(acc[2 * q][j][1], gr),
+                                              codec::scaled(acc[2 * q][j][2], gr), codec::scaled(acc[2 * q][j][3], gr));
+            *reinterpret_cast<uint32_t*>(qo + orow * half + n0 + (WTN / 2) * wn + 16 * q + 4 * lq) = w;
+          }
           if (wn == 0 && lq == 0) p.out_scale[orow * (half / kBK) + n0 / kBK] = sc;
         }
       }

@@ -30,11 +30,12 @@ constexpr int kBlockK = 128;  // K block = scale granularity
 // Instances left out: the 256x256 tile with 2x4 waves needs more than the
 // register file for the fp32 read-modify-write epilogue of the weight-gradient
 // kinds (it would spill); those kinds use the 1x8 layout of that tile.  The
-// fused SwiGLU epilogue exists for the 256x256 tile on 1x8 waves only: each
-// wave then holds 16 gate and the matching 16 up columns of all 256 rows, and
-// the tile's 128 output columns are exactly one 1x128 scale group.
+// fused SwiGLU epilogue exists for the 256x256 tile only (on 2x4 or 1x8
+// waves): its 128 gate and 128 up columns give 128 output columns, exactly
+// one 1x128 scale group, and each wave holds the gate and the matching up
+// columns of its rows.
 constexpr bool excluded(int bm, int bn, int wm, int kind) {
-  if (kind == KIND_CONTIG_SWIGLU) return !(bm == 256 && bn == 256 && wm == 1);
+  if (kind == KIND_CONTIG_SWIGLU) return !(bm == 256 && bn == 256 && (wm == 1 || wm == 2));
   // the power-of-two kinds have their fp32-scale kind's instances
   kind = layout_of(kind);
   // 192-row tiles: dense layouts only (a grouped layout's 128-row blocks would

@@ -122,9 +122,9 @@ def test_fused_swiglu_argument_errors(lib):
 
 
 def test_fused_swiglu_plan(lib):
-    """One tile: 256 rows x (128 gate + 128 up columns) on 1x8 waves, never split."""
+    """One tile: 256 rows x (128 gate + 128 up columns) on 2x4 waves, never split."""
     c = _cfg(lib, 7, 65536, 4096, 7168)
-    assert (c["block_m"], c["block_n"], c["waves_m"], c["waves_n"]) == (256, 256, 1, 8)
+    assert (c["block_m"], c["block_n"], c["waves_m"], c["waves_n"]) == (256, 256, 2, 4)
     assert c["tiles"] == (65536 // 256) * (4096 // 256) and c["k_splits"] == 1
 
 

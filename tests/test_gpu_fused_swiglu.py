@@ -13,8 +13,12 @@ Two bars:
     dg_swiglu_quantize_fp8_1x128): identical bits, on random N(0,1)-quantised
     operands too, since the fused epilogue rounds to bf16 and then runs the same
     arithmetic as the stand-alone kernel.
-Rows whose expert id is -1 (or not in [0, G)) keep their sentinel bytes."""
+Rows whose expert id is -1 (or not in [0, G)) keep their sentinel bytes.  The
+small cases run on both instances of the fused epilogue: the default 2x4-wave
+tile and the 1x8-wave one (DG_FORCE_TILE)."""
 from __future__ import annotations
+
+import os
 
 import numpy as np
 import pytest
@@ -35,6 +39,19 @@ S_SENTINEL = float("nan")
 def dg():
     import moe_grouped_gemm_x128_amd as m
     return m
+
+
+TILES = [None, "256x256x1x8"]
+
+
+@pytest.fixture
+def force_tile():
+    def _set(tile):
+        os.environ.pop("DG_FORCE_TILE", None)
+        if tile is not None:
+            os.environ["DG_FORCE_TILE"] = tile
+    yield _set
+    os.environ.pop("DG_FORCE_TILE", None)
 
 
 def run_fused(dg, a, sa, b, sb, ids):
@@ -106,10 +123,12 @@ def layout_ids(c, kind):
     (2, 512, 256, 128, "out_of_range"),    # one K block
     (1, 128, 128, 7168, "ragged"),         # long K, a single 128-row block
 ])
-def test_fused_swiglu_against_oracle(dg, g, rows, i, k, kind):
+@pytest.mark.parametrize("tile", TILES)
+def test_fused_swiglu_against_oracle(dg, force_tile, tile, g, rows, i, k, kind):
     c = inputs.make_contiguous_exact(g, rows, 2 * i, k, seed=inputs.SEED_BASE + 70 + g + k)
     ids = layout_ids(c, kind)
-    say(f"fused swiglu vs oracle G={g} rows={rows} I={i} K={k} {kind}")
+    force_tile(tile)
+    say(f"fused swiglu vs oracle G={g} rows={rows} I={i} K={k} {kind} tile={tile}")
     args = (dev(c.a), dev(c.sa), dev(c.b), dev(c.sb), dev(ids))
     q, s = run_fused(dg, *args)
     valid, q_ref, s_ref, h = oracle_composition(c, ids)
@@ -119,13 +138,15 @@ def test_fused_swiglu_against_oracle(dg, g, rows, i, k, kind):
     assert np.array_equal(q, q2) and np.array_equal(s, s2, equal_nan=True), "second call differs"
 
 
+@pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("g,rows,i,k", [(4, 384, 256, 384), (8, 256, 512, 1024)])
-def test_fused_swiglu_equals_unfused_path(dg, g, rows, i, k):
+def test_fused_swiglu_equals_unfused_path(dg, force_tile, tile, g, rows, i, k):
     """Random N(0,1)-quantised operands: the fused call gives the unfused GPU
     path's bits (GEMM into bf16, then the stand-alone SwiGLU quantiser)."""
     c = inputs.make_contiguous(g, rows, 2 * i, k, seed=inputs.SEED_BASE + 90 + g)
     ids = c.m_indices
-    say(f"fused swiglu vs unfused G={g} rows={rows} I={i} K={k}")
+    force_tile(tile)
+    say(f"fused swiglu vs unfused G={g} rows={rows} I={i} K={k} tile={tile}")
     args = (dev(c.a), dev(c.sa), dev(c.b), dev(c.sb), dev(ids))
     q, s = run_fused(dg, *args)
     qu, su = run_unfused(dg, *args)

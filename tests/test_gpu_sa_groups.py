@@ -89,10 +89,12 @@ def test_contiguous_ue8m0_packed_tiles_per_workgroup(dg, k):
     _check(x, bf16_bits(c), x.sa, x.sb, f"contiguous packed K={k}", seed=k + 1)
 
 
+@pytest.mark.parametrize("tile", [None, "256x256x1x8"])
 @pytest.mark.parametrize("k", [640, 1152])
-def test_fused_swiglu_tiles_per_workgroup(dg, k):
+def test_fused_swiglu_tiles_per_workgroup(dg, force_tile, tile, k):
     x = inputs.make_contiguous(G, ROWS, N, k, seed=inputs.SEED_BASE + 160 + k // 128)
-    say(f"fused swiglu sa groups K={k}")
+    force_tile(tile)
+    say(f"fused swiglu sa groups K={k} tile={tile}")
     ids = dev(x.m_indices)
     a, sa, b, sb = dev(x.a), dev(x.sa), dev(x.b), dev(x.sb)
     i = N // 2
