@@ -216,8 +216,8 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   constexpr bool kBf16 = bf16_kind(KIND);              // bf16 operands, no scales at all
   // contiguous layout with the SwiGLU + re-quantise epilogue: the tile's B
   // rows are 128 gate rows and the 128 matching up rows, in LDS order
-  // [wave][gate 16 | up 16], so fragment 0 of a wave holds the gate and
-  // fragment 1 the up value of the same output element in the same lane
+  // [pair][gate 16 | up 16], so a wave's fragments 2q and 2q+1 hold the gate
+  // and the up value of the same output element in the same lane
   constexpr bool kSwiGLU = (KIND == KIND_CONTIG_SWIGLU);
   constexpr bool kContig = (LAYOUT == KIND_CONTIGUOUS) || kSwiGLU;
   static_assert(!kSwiGLU || (BM == 256 && BN == 256 && ((WM == 1 && WN == 8) || (WM == 2 && WN == 4))),
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fp8_gemm_kernel(const Params p) 
   constexpr bool kStage = !kFp32Out && !kSwiGLU && (WTN == 64 || WTN == 32);
   constexpr int kStageRow = WTN * 2 + 16;
   __shared__ __attribute__((aligned(16))) uint8_t sOut[kStage ? NW : 1][kStage ? 16 * kStageRow : 16];
-  // fused SwiGLU: each wave's |h| maximum over its 16 columns, per tile row
+  // fused SwiGLU: each wave's |h| maximum over its columns, per tile row
   __shared__ __attribute__((aligned(16))) float sRowMax[kSwiGLU ? BM : 1][kSwiGLU ? WN : 4];
 
   const int tid = threadIdx.x;
